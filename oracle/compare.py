@@ -1,0 +1,130 @@
+"""ORACLE -- TEST INFRASTRUCTURE ONLY.  Comparison of a library result with the oracle.
+
+The rule (per element of x[K, M, N]):
+  * every code must equal the oracle's, except where the oracle reports that more than
+    one code is reachable -- the value lies within 1e-6 relative of a rounding tie, or
+    within the fp32-accumulation error bound of a rounding boundary (of the code itself
+    or of the dtype-rounded intermediate).  There the code may differ by one step (one
+    int4 value, or one E2M1 magnitude of the same sign, or the sign of an E2M1 zero when
+    the value is within error of 0), and it must lie in the reachable range;
+  * such differences may make up at most ceil(1e-4 * elements) of a result;
+  * per-token fp32 scales agree within 1e-5 relative;
+  * an e8m0 code equals the oracle's, or is the oracle's alternative code when the group's
+    max is within error (or 1e-6 relative) of a power-of-two boundary; that group's
+    codes are then checked against the oracle's encoding under the alternative code;
+    the pad byte of an odd group count is 0.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+MISMATCH_CAP_REL = 1e-4
+SCALE_REL_TOL = 1e-5
+
+
+def unpack_nibbles(packed: np.ndarray, count: int) -> np.ndarray:
+    """[S, count/2] bytes -> [S, count] codes (low nibble = lower index)."""
+    p = np.asarray(packed, dtype=np.uint8).reshape(packed.shape[0], -1)
+    out = np.empty((p.shape[0], p.shape[1] * 2), dtype=np.uint8)
+    out[:, 0::2] = p & 0xF
+    out[:, 1::2] = p >> 4
+    return out[:, :count]
+
+
+def _int4_level(c: np.ndarray) -> np.ndarray:
+    c = c.astype(np.int16)
+    return np.where(c >= 8, c - 16, c)
+
+
+def _e2m1_level(c: np.ndarray) -> np.ndarray:
+    c = c.astype(np.int16)
+    return np.where(c & 8, -(c & 7), c & 7)
+
+
+def compare(orc: dict, gpu_packed: np.ndarray, gpu_scale: np.ndarray, max_report: int = 8) -> dict:
+    """Compare library outputs for the slices the oracle ran.
+
+    gpu_packed: [S, M*N/2] uint8 (the library's codes, any of the packed layouts, which
+    are byte-identical); gpu_scale: float32 [S] (per token) or uint8 [S, GS] (e8m0).
+    """
+    mode, M, N, S = orc["mode"], orc["M"], orc["N"], orc["S"]
+    MN = M * N
+    per_token = mode in ("int32", "int4")
+    g = unpack_nibbles(np.asarray(gpu_packed).reshape(S, -1), MN)
+    o = unpack_nibbles(orc["packed"], MN)
+    rep = {"elements": S * MN, "mismatch": 0, "mismatch_in_stated_window": 0, "flagged": 0,
+           "alt_groups": 0, "max_scale_rel": 0.0, "errors": []}
+    errs = rep["errors"]
+
+    if per_token:
+        gl, ol = _int4_level(g), _int4_level(o)
+        lo, hi = orc["lo"].astype(np.int16), orc["hi"].astype(np.int16)
+        zs_ok = np.zeros_like(gl, dtype=bool)
+        sign_diff = np.zeros_like(gl, dtype=bool)
+        gs = np.asarray(gpu_scale, dtype=np.float32).reshape(S)
+        os_ = orc["scale"]
+        with np.errstate(divide="ignore", invalid="ignore"):
+            rel = np.where(os_ == 0, np.where(gs == 0, 0.0, np.inf),
+                           np.abs(gs.astype(np.float64) - os_) / np.abs(os_.astype(np.float64)))
+        rep["max_scale_rel"] = float(rel.max()) if rel.size else 0.0
+        bad = np.nonzero(rel > SCALE_REL_TOL)[0]
+        for s in bad[:max_report]:
+            errs.append(f"slice {s}: scale {gs[s]!r} vs oracle {os_[s]!r}")
+        if bad.size:
+            rep["scale_fail"] = int(bad.size)
+    else:
+        G = -(-MN // 32)
+        GS = 2 * (-(-MN // 64))
+        ge = np.asarray(gpu_scale, dtype=np.uint8).reshape(S, GS)
+        oe = orc["e8m0"]
+        if GS > G:  # pad slot of an odd group count
+            badpad = np.nonzero(ge[:, G] != 0)[0]
+            for s in badpad[:max_report]:
+                errs.append(f"slice {s}: pad e8m0 byte {ge[s, G]} != 0")
+            if badpad.size:
+                rep["pad_fail"] = int(badpad.size)
+        gcode, ocode = ge[:, :G].astype(np.int16), oe[:, :G].astype(np.int16)
+        use_alt = (gcode != ocode) & (gcode == orc["g_alt"]) & (gcode >= orc["g_lo"]) & \
+                  (gcode <= orc["g_hi"])
+        bad_g = (gcode != ocode) & ~use_alt
+        if bad_g.any():
+            ss, gg = np.nonzero(bad_g)
+            for s, gi in list(zip(ss, gg))[:max_report]:
+                errs.append(f"slice {s} group {gi}: e8m0 {gcode[s, gi]} vs oracle {ocode[s, gi]} "
+                            f"(reachable {orc['g_lo'][s, gi]}..{orc['g_hi'][s, gi]})")
+            rep["e8m0_fail"] = int(bad_g.sum())
+        rep["alt_groups"] = int(use_alt.sum())
+        alt_el = np.repeat(use_alt, 32, axis=1)[:, :MN]
+        gl = _e2m1_level(g)
+        ol = np.where(alt_el, orc["alt_lvl"], orc["lvl"]).astype(np.int16)
+        lo = np.where(alt_el, orc["alt_lo"], orc["lo"]).astype(np.int16)
+        hi = np.where(alt_el, orc["alt_hi"], orc["hi"]).astype(np.int16)
+        zs_ok = np.where(alt_el, orc["alt_zsign"], orc["zsign"]).astype(bool)
+        # sign of an E2M1 zero: the oracle's sign is that of its y, which is the
+        # sign bit of its main code
+        sign_diff = (gl == 0) & (ol == 0) & ((g & 8) != (o & 8))
+
+    diff = (gl != ol) | sign_diff
+    flagged = (lo != hi) | zs_ok
+    rep["flagged"] = int(flagged.sum())
+    ok_level = (gl >= lo) & (gl <= hi) & (np.abs(gl - ol) <= 1)
+    ok_sign = ~sign_diff | zs_ok
+    allowed = ok_level & ok_sign
+    bad = diff & ~allowed
+    rep["mismatch"] = int(diff.sum())
+    rep["mismatch_in_stated_window"] = int((diff & (orc["ns_tie"] != 0)).sum())
+    if bad.any():
+        ss, ff = np.nonzero(bad)
+        for s, f in list(zip(ss, ff))[:max_report]:
+            errs.append(f"slice {s} elem {f} (m={f // N}, n={f % N}): code {g[s, f]:#x} "
+                        f"level {gl[s, f]} vs oracle level {ol[s, f]} reachable "
+                        f"[{lo[s, f]}, {hi[s, f]}]")
+        rep["code_fail"] = int(bad.sum())
+    cap = math.ceil(MISMATCH_CAP_REL * rep["elements"])
+    rep["mismatch_cap"] = cap
+    if rep["mismatch"] > cap:
+        errs.append(f"{rep['mismatch']} tie mismatches exceed the cap {cap}")
+    rep["ok"] = not errs
+    return rep

@@ -1,0 +1,569 @@
+/*
+ * ORACLE -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, scalar CPU implementation of the fused transform + dynamic
+ * quantization operator, written from the page "aclnnFlatQuantV2 算子拆解：
+ * 两步矩阵乘 + 动态量化，CANN 上怎么写一次讲清" (cited below as [FQV2], by
+ * section).  Only the tests, the smoke check and the benchmark's CPU-baseline
+ * leg may load it.  It shares no code with the GPU library.
+ *
+ * Other pages cited, for conventions the operator page leaves open:
+ *   [MOCONV] the ModelOpt Conv3D implicit-GEMM page, section 6.1 (the eight
+ *            E2M1 magnitudes and the seven decision points between them);
+ *   [DSQ]    the dequant_swiglu_quant Triton-Ascend page, section 6.1
+ *            (round-half-to-even, 2.5 -> 2 and 3.5 -> 4);
+ *   [APT]    the APT-LLM page, section 2.1 (symmetric b-bit integer
+ *            quantization clamped to [-2^(b-1), 2^(b-1)-1]).
+ *
+ * What is computed for one slice x_k [M, N] (readings of silent or garbled
+ * points are marked "reading"):
+ *   T = RNE_dt(fl32(x_k . P2))       [FQV2] 第1步; reading: the intermediate is
+ *                                    rounded to the activation dtype, the
+ *                                    matrices' own dtype (they may not be mixed)
+ *   y = fl32(P1 . T)                 [FQV2] 第2步; y stays fp32.  With an empty
+ *                                    [0,0] P2 the first step is skipped.
+ *   per token:  scale = fl32(max|y| / fl32(7/clipRatio)),
+ *               code  = clamp(RNE(fl32(y / scale)), -8, 7)    [FQV2] 第3步 pertoken
+ *   per group of 32 over the flattened index f = m*N + n ([FQV2] 第3步 pergroup):
+ *     V1 (dstTypeMax == 0): e8m0 = clamp(floor(log2 amax) - 2 + 127, 0, 254),
+ *        reading: emax = 2, the exponent of E2M1's largest value 6 = 1.5 * 2^2;
+ *     V2 (dstTypeMax in [6,12]): S = fl32(amax / dstTypeMax), split into the
+ *        biased exponent E and mantissa; E += 1 when S is normal, E < 254 and
+ *        the mantissa is non-zero; e8m0 = E                     [FQV2] 第4步
+ *     element code = E2M1_RNE_saturating(y * 2^(127 - e8m0))
+ *
+ * All sums are accumulated in double (bf16/fp16 products are exact in double)
+ * and rounded once.  Scale arithmetic is IEEE fp32 (C float, no contraction).
+ *
+ * Besides the codes the oracle reports, per element, the range of codes that
+ * any correct fp32 implementation can reach: fp32 sums in any order carry an
+ * error of at most gamma(n) * sum|terms| (gamma(n) = n u / (1 - n u),
+ * u = 2^-24, Higham, "Accuracy and Stability of Numerical Algorithms",
+ * Lemma 3.1 / eq. 3.5), which can flip the dtype rounding of T and, through
+ * it and through the scale, move y/scale across a code boundary.  The range
+ * also covers the stated tolerance window of 1e-6 relative around a tie.
+ */
+#include <float.h>
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define FQO_F16 1
+#define FQO_BF16 2
+#define FQO_PER_TOKEN 0
+#define FQO_PER_GROUP 1
+
+#define TIE_REL 1e-6 /* the stated tie window, relative */
+
+/* ---- exact decoding of the 16-bit inputs --------------------------------- */
+
+static double bf16_value(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+static double f16_value(uint16_t h) {
+  int s = (h >> 15) & 1, e = (h >> 10) & 0x1F, m = h & 0x3FF;
+  double v;
+  if (e == 0)
+    v = ldexp((double)m, -24);
+  else if (e == 31)
+    v = m ? NAN : INFINITY;
+  else
+    v = ldexp((double)(1024 + m), e - 25);
+  return s ? -v : v;
+}
+
+static double dt_value(uint16_t h, int dtype) { return dtype == FQO_BF16 ? bf16_value(h) : f16_value(h); }
+
+/* ---- round to nearest even into a binary format -------------------------
+ * A format with `frac` fraction bits, minimum normal exponent `emin` and
+ * largest finite value `maxv`.  Textbook construction: scale so that the
+ * quantum of v's binade becomes 1, round to an integer (nearbyint, default
+ * round-to-nearest-even mode), scale back.  Subnormals use the quantum of
+ * the smallest binade.  Magnitudes beyond the last finite value round to
+ * infinity when they reach maxv + half a quantum.
+ */
+static double rne_format(double v, int frac, int emin, double maxv) {
+  if (v == 0.0 || isnan(v) || isinf(v)) return v;
+  int ex;
+  frexp(v, &ex);           /* |v| = m * 2^ex, m in [0.5, 1): floor(log2|v|) = ex - 1 */
+  int e = ex - 1;
+  if (e < emin) e = emin;
+  int q = e - frac;        /* exponent of the quantum */
+  double r = ldexp(nearbyint(ldexp(v, -q)), q);
+  if (fabs(r) > maxv) return v > 0 ? INFINITY : -INFINITY;
+  return r;
+}
+
+double fqo_round_f32(double v) { return rne_format(v, 23, -126, FLT_MAX); }
+double fqo_round_bf16(double v) { return rne_format(v, 7, -126, 3.3895313892515355e38); }
+double fqo_round_f16(double v) { return rne_format(v, 10, -14, 65504.0); }
+static double round_dt(double v, int dtype) { return dtype == FQO_BF16 ? fqo_round_bf16(v) : fqo_round_f16(v); }
+
+/* gamma(n) of the error analysis of recursive/any-order summation */
+static double gamma_n(int64_t n) {
+  const double u = 5.9604644775390625e-08; /* 2^-24 */
+  return (double)n * u / (1.0 - (double)n * u);
+}
+
+/* ---- int4 encoder ([FQV2] 第3步 pertoken; [APT] 2.1 clamp; [DSQ] 6.1 RNE) -- */
+
+int fqo_int4_code(float q) {
+  float r = nearbyintf(q); /* round half to even (default rounding mode) */
+  if (r < -8.0f) r = -8.0f;
+  if (r > 7.0f) r = 7.0f;
+  return (int)r;
+}
+
+/* ---- E2M1 encoder ----------------------------------------------------------
+ * The eight magnitudes of [MOCONV] 6.1; the code is sign<<3 | index, the
+ * index being the position in the magnitude list (1 exponent pair + 1
+ * mantissa bit: s e1 e0 m).  Nearest magnitude by exhaustive distance; an
+ * exact tie goes to the even index, which is round-half-to-even on the
+ * format's mantissa bit.  Magnitudes above 6 therefore map to 6
+ * (saturation; E2M1 has no infinity or NaN).
+ */
+static const double E2M1_MAG[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+/* tie: 0 = even index, 1 = lower index, 2 = upper index */
+static int e2m1_index(double a, int tie) {
+  int best = 0;
+  double bd = fabs(a - E2M1_MAG[0]);
+  for (int i = 1; i < 8; ++i) {
+    double d = fabs(a - E2M1_MAG[i]);
+    if (d < bd) {
+      bd = d;
+      best = i;
+    } else if (d == bd) { /* tie between best (lower) and i (upper) */
+      if (tie == 2 || (tie == 0 && (i % 2 == 0))) best = i;
+    }
+  }
+  return best;
+}
+
+int fqo_e2m1_code(double v) {
+  int s = signbit(v) ? 1 : 0;
+  return (s << 3) | e2m1_index(fabs(v), 0);
+}
+
+double fqo_e2m1_value(int code) {
+  double m = E2M1_MAG[code & 7];
+  return (code & 8) ? -m : m;
+}
+
+/* signed level: +index for a positive code, -index for a negative one */
+static int level_of_code(int code) { return (code & 8) ? -(code & 7) : (code & 7); }
+static int e2m1_level_down(double v) { return v >= 0 ? e2m1_index(v, 1) : -e2m1_index(-v, 2); }
+static int e2m1_level_up(double v) { return v >= 0 ? e2m1_index(v, 2) : -e2m1_index(-v, 1); }
+
+/* ---- e8m0 scale codes ------------------------------------------------------ */
+
+/* V1, [FQV2] 第3步 pergroup: sharedExp = floor(log2(amax)) - emax, emax = 2. */
+int fqo_e8m0_v1(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  int ex;
+  frexp((double)amax, &ex);
+  int code = (ex - 1) - 2 + 127;
+  if (code < 0) code = 0;
+  if (code > 254) code = 254;
+  return code;
+}
+
+/* V2, [FQV2] 第4步, from the fp32 bit fields of S. */
+int fqo_e8m0_v2_bits(float amax, float dmax) {
+  float S = amax / dmax;
+  uint32_t b;
+  memcpy(&b, &S, 4);
+  uint32_t E = (b >> 23) & 0xFF, mant = b & 0x7FFFFF;
+  if (E >= 1 && E < 254 && mant != 0) E += 1;
+  return (int)E;
+}
+
+/* V2 again, from frexp, as an independent cross-check of the bit version. */
+int fqo_e8m0_v2_frexp(float amax, float dmax) {
+  float S = amax / dmax;
+  if (S == 0.0f) return 0;
+  if (S < FLT_MIN) return 0; /* subnormal: biased exponent 0, never incremented */
+  int ex;
+  double m = frexp((double)S, &ex); /* S = m 2^ex, m in [0.5, 1) */
+  int E = (ex - 1) + 127;
+  if (m != 0.5 && E < 254) E += 1;
+  return E;
+}
+
+static int e8m0_code(float amax, double dst_max) {
+  if (dst_max == 0.0) return fqo_e8m0_v1(amax); /* [FQV2] V1 还是 V2: 0.0 behaves as V1 */
+  return fqo_e8m0_v2_bits(amax, (float)dst_max);
+}
+
+/* 2^(127 - code) as a double (exact) */
+static double inv_scale_of_code(int code) { return ldexp(1.0, 127 - code); }
+
+/* ---- batch interface ---------------------------------------------------- */
+
+typedef struct {
+  int32_t dtype;        /* FQO_F16 | FQO_BF16 */
+  int32_t mode;         /* FQO_PER_TOKEN | FQO_PER_GROUP */
+  int64_t M, N;
+  int32_t two_sided;    /* 0: the right transform is skipped ([0,0] P2) */
+  int32_t pad_;
+  double clip_ratio;
+  double dst_type_max;
+} fqo_params;
+
+/* Per-slice outputs; every array holds nslices consecutive slices.  Any pointer
+ * may be NULL when that output is not wanted.  Levels: the int4 value for per
+ * token; the signed E2M1 magnitude index for per group. */
+typedef struct {
+  uint8_t* packed;   /* M*N/2 bytes per slice: 4-bit codes, low nibble = lower index */
+  float* scale;      /* per token: 1 per slice */
+  uint8_t* e8m0;     /* per group: 2*ceil(M*N/64) bytes per slice (odd pad byte = 0) */
+  float* y;          /* M*N fp32 per slice */
+  uint16_t* t;       /* M*N dtype bits per slice (the rounded intermediate) */
+  int8_t* lvl;       /* M*N: the oracle's level */
+  int8_t* lo;        /* M*N: lowest reachable level */
+  int8_t* hi;        /* M*N: highest reachable level */
+  uint8_t* zsign;    /* M*N: a zero code may carry either sign */
+  uint8_t* ns_tie;   /* M*N: within 1e-6 relative of a rounding tie */
+  int8_t* alt_lvl;   /* per group: the same four under the alternative e8m0 code */
+  int8_t* alt_lo;
+  int8_t* alt_hi;
+  uint8_t* alt_zsign;
+  uint8_t* g_lo;     /* per group: reachable e8m0 code range */
+  uint8_t* g_hi;
+  uint8_t* g_alt;    /* per group: the alternative e8m0 code (== the code if none) */
+  float* scale_lo;   /* per token: reachable scale range */
+  float* scale_hi;
+} fqo_out;
+
+typedef struct {
+  const fqo_params* p;
+  const uint16_t *x, *p1, *p2;
+  const fqo_out* o;
+  int64_t s_begin, s_end;
+  int want_ranges;
+  int status;
+} job_t;
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+static void put_nibble(uint8_t* packed, int64_t f, int code) {
+  uint8_t c = (uint8_t)(code & 0xF);
+  if (f & 1)
+    packed[f >> 1] = (uint8_t)((packed[f >> 1] & 0x0F) | (c << 4));
+  else
+    packed[f >> 1] = (uint8_t)((packed[f >> 1] & 0xF0) | c);
+}
+
+static int slice(const fqo_params* p, const uint16_t* xs, const double* P1, const double* P2,
+                 const fqo_out* o, int64_t s, int want, double* ws) {
+  const int64_t M = p->M, N = p->N, MN = M * N;
+  double* X = ws;              /* M*N */
+  double* T = X + MN;          /* M*N  rounded intermediate */
+  double* Tlo = T + MN;        /* M*N  reachable range of the GPU's rounded intermediate */
+  double* Thi = Tlo + MN;
+  double* Y = Thi + MN;        /* M*N  fp32 y (as double) */
+  double* Ylo = Y + MN;        /* M*N  bounds on any fp32 implementation's y */
+  double* Yhi = Ylo + MN;
+  for (int64_t f = 0; f < MN; ++f) X[f] = dt_value(xs[f], p->dtype);
+
+  /* [FQV2] 第1步: right-multiply by P2 along the trailing axis */
+  if (p->two_sided) {
+    const double gN = gamma_n(N);
+    for (int64_t m = 0; m < M; ++m)
+      for (int64_t n = 0; n < N; ++n) {
+        double s = 0.0, sa = 0.0;
+        for (int64_t j = 0; j < N; ++j) {
+          double pr = X[m * N + j] * P2[j * N + n];
+          s += pr;
+          sa += fabs(pr);
+        }
+        T[m * N + n] = round_dt(fqo_round_f32(s), p->dtype);
+        if (want) {
+          double r = gN * sa;
+          Tlo[m * N + n] = round_dt(s - r, p->dtype);
+          Thi[m * N + n] = round_dt(s + r, p->dtype);
+        }
+      }
+  } else {
+    for (int64_t f = 0; f < MN; ++f) T[f] = Tlo[f] = Thi[f] = X[f];
+  }
+  if (o->t)
+    for (int64_t f = 0; f < MN; ++f) {
+      /* store the rounded intermediate as dtype bits */
+      double v = T[f];
+      uint16_t bits;
+      if (p->dtype == FQO_BF16) {
+        float fv = (float)v;
+        uint32_t u;
+        memcpy(&u, &fv, 4);
+        bits = (uint16_t)(u >> 16); /* exact: v is a bf16 value */
+      } else {
+        /* exact fp16 encoding of an fp16 value */
+        double a = fabs(v);
+        uint16_t sg = signbit(v) ? 0x8000 : 0;
+        if (a == 0.0)
+          bits = sg;
+        else if (isinf(a))
+          bits = sg | 0x7C00;
+        else if (a < ldexp(1.0, -14))
+          bits = sg | (uint16_t)ldexp(a, 24);
+        else {
+          int ex;
+          double mm = frexp(a, &ex); /* a = mm 2^ex */
+          int e = ex - 1;
+          uint16_t frac = (uint16_t)(ldexp(mm * 2.0, 10) - 1024.0);
+          bits = sg | (uint16_t)((e + 15) << 10) | frac;
+        }
+      }
+      o->t[s * MN + f] = bits;
+    }
+
+  /* [FQV2] 第2步: left-multiply by P1 along axis 1 */
+  const double gM = gamma_n(M);
+  for (int64_t i = 0; i < M; ++i)
+    for (int64_t n = 0; n < N; ++n) {
+      double acc = 0.0;
+      for (int64_t m = 0; m < M; ++m) acc += P1[i * M + m] * T[m * N + n];
+      Y[i * N + n] = fqo_round_f32(acc);
+      if (want) {
+        double lo = 0.0, hi = 0.0, sa = 0.0;
+        for (int64_t m = 0; m < M; ++m) {
+          double a = P1[i * M + m] * Tlo[m * N + n], b = P1[i * M + m] * Thi[m * N + n];
+          lo += a < b ? a : b;
+          hi += a < b ? b : a;
+          sa += fabs(a) > fabs(b) ? fabs(a) : fabs(b);
+        }
+        double r = gM * sa;
+        Ylo[i * N + n] = lo - r;
+        Yhi[i * N + n] = hi + r;
+      }
+    }
+  if (o->y)
+    for (int64_t f = 0; f < MN; ++f) o->y[s * MN + f] = (float)Y[f];
+
+  uint8_t* packed = o->packed ? o->packed + s * (MN / 2) : NULL;
+
+  if (p->mode == FQO_PER_TOKEN) {
+    /* [FQV2] 第3步 pertoken: one fp32 scale per slice k */
+    float amax = 0.0f;
+    for (int64_t f = 0; f < MN; ++f) {
+      float a = fabsf((float)Y[f]);
+      if (a > amax) amax = a;
+    }
+    const float d = (float)(7.0 / p->clip_ratio);
+    const float scale = amax / d;
+    if (o->scale) o->scale[s] = scale;
+    double Alo = 0.0, Ahi = 0.0, slo = 0.0, shi = 0.0;
+    if (want) {
+      for (int64_t f = 0; f < MN; ++f) {
+        double lo = Ylo[f], hi = Yhi[f];
+        double amin = lo > 0 ? lo : (hi < 0 ? -hi : 0.0);
+        double amx = fabs(lo) > fabs(hi) ? fabs(lo) : fabs(hi);
+        if (amin > Alo) Alo = amin;
+        if (amx > Ahi) Ahi = amx;
+      }
+      /* the stated window also applies to the scale's own tie-free rounding */
+      slo = Alo / (double)d * (1.0 - 2.4e-7);
+      shi = Ahi / (double)d * (1.0 + 2.4e-7);
+      if (amax == 0.0f) slo = shi = 0.0;
+      if (o->scale_lo) o->scale_lo[s] = (float)slo;
+      if (o->scale_hi) o->scale_hi[s] = (float)shi;
+    }
+    for (int64_t f = 0; f < MN; ++f) {
+      int code = 0;
+      float q = 0.0f;
+      if (scale > 0.0f) {
+        q = (float)Y[f] / scale;
+        code = fqo_int4_code(q);
+      }
+      if (packed) put_nibble(packed, f, code);
+      if (o->lvl) o->lvl[s * MN + f] = (int8_t)code;
+      if (o->zsign) o->zsign[s * MN + f] = 0; /* int4 zero is unsigned */
+      int tie = 0;
+      if (scale > 0.0f) {
+        double t = floor((double)q) + 0.5;
+        if (t >= -7.5 && t <= 6.5 && fabs((double)q - t) <= TIE_REL * fabs(t)) tie = 1;
+      }
+      if (o->ns_tie) o->ns_tie[s * MN + f] = (uint8_t)tie;
+      if (want && (o->lo || o->hi)) {
+        int lo, hi;
+        if (amax == 0.0f) {
+          lo = hi = 0;
+        } else if (!(slo > 0.0)) {
+          lo = -8;
+          hi = 7;
+        } else {
+          double c[4] = {Ylo[f] / slo, Ylo[f] / shi, Yhi[f] / slo, Yhi[f] / shi};
+          double qlo = c[0], qhi = c[0];
+          for (int i = 1; i < 4; ++i) {
+            if (c[i] < qlo) qlo = c[i];
+            if (c[i] > qhi) qhi = c[i];
+          }
+          /* two fp32 roundings (reciprocal and product) and the stated window */
+          double w = 2.4e-7 + TIE_REL;
+          qlo -= fabs(qlo) * w;
+          qhi += fabs(qhi) * w;
+          double dl = ceil(qlo - 0.5), dh = floor(qhi + 0.5);
+          if (dl < -8) dl = -8;
+          if (dl > 7) dl = 7;
+          if (dh < -8) dh = -8;
+          if (dh > 7) dh = 7;
+          lo = (int)dl;
+          hi = (int)dh;
+          if (lo > code) lo = code;
+          if (hi < code) hi = code;
+        }
+        if (o->lo) o->lo[s * MN + f] = (int8_t)lo;
+        if (o->hi) o->hi[s * MN + f] = (int8_t)hi;
+      }
+    }
+    return 0;
+  }
+
+  /* [FQV2] 第3步 pergroup / 第4步: groups of 32 over the flattened slice */
+  const int64_t G = ceil_div(MN, 32);
+  const int64_t GS = 2 * ceil_div(MN, 64);
+  uint8_t* e8 = o->e8m0 ? o->e8m0 + s * GS : NULL;
+  if (e8)
+    for (int64_t g = 0; g < GS; ++g) e8[g] = 0;
+  for (int64_t g = 0; g < G; ++g) {
+    const int64_t f0 = g * 32, f1 = (f0 + 32 < MN) ? f0 + 32 : MN;
+    float amax = 0.0f;
+    for (int64_t f = f0; f < f1; ++f) {
+      float a = fabsf((float)Y[f]);
+      if (a > amax) amax = a;
+    }
+    const int code = e8m0_code(amax, p->dst_type_max);
+    if (e8) e8[g] = (uint8_t)code;
+    int glo = code, ghi = code, alt = code;
+    if (want) {
+      double Alo = 0.0, Ahi = 0.0;
+      for (int64_t f = f0; f < f1; ++f) {
+        double lo = Ylo[f], hi = Yhi[f];
+        double amin = lo > 0 ? lo : (hi < 0 ? -hi : 0.0);
+        double amx = fabs(lo) > fabs(hi) ? fabs(lo) : fabs(hi);
+        if (amin > Alo) Alo = amin;
+        if (amx > Ahi) Ahi = amx;
+      }
+      /* the stated window around a power-of-two boundary */
+      if ((double)amax * (1.0 - TIE_REL) < Alo) Alo = (double)amax * (1.0 - TIE_REL);
+      if ((double)amax * (1.0 + TIE_REL) > Ahi) Ahi = (double)amax * (1.0 + TIE_REL);
+      /* the code is monotone in amax; a real bound maps through the float
+         values next to it */
+      float flo = (float)Alo, fhi = (float)Ahi;
+      if ((double)flo > Alo) flo = nextafterf(flo, 0.0f);
+      if ((double)fhi < Ahi) fhi = nextafterf(fhi, INFINITY);
+      if (Alo <= 0.0) flo = 0.0f;
+      glo = e8m0_code(flo, p->dst_type_max);
+      ghi = e8m0_code(fhi, p->dst_type_max);
+      if (glo > code) glo = code;
+      if (ghi < code) ghi = code;
+      alt = (glo < code) ? glo : (ghi > code ? ghi : code);
+      if (o->g_lo) o->g_lo[s * G + g] = (uint8_t)glo;
+      if (o->g_hi) o->g_hi[s * G + g] = (uint8_t)ghi;
+      if (o->g_alt) o->g_alt[s * G + g] = (uint8_t)alt;
+    }
+    for (int pass = 0; pass < 2; ++pass) {
+      const int c = pass == 0 ? code : alt;
+      if (pass == 1 && !want) break;
+      const double R = inv_scale_of_code(c);
+      for (int64_t f = f0; f < f1; ++f) {
+        const double v = Y[f] * R; /* exact power-of-two scaling */
+        const int ec = fqo_e2m1_code(v);
+        if (pass == 0) {
+          if (packed) put_nibble(packed, f, ec);
+          int tie = 0;
+          static const double mids[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
+          for (int i = 0; i < 7; ++i)
+            if (fabs(fabs(v) - mids[i]) <= TIE_REL * mids[i]) tie = 1;
+          if (o->ns_tie) o->ns_tie[s * MN + f] = (uint8_t)tie;
+        }
+        int8_t* L = pass == 0 ? o->lvl : o->alt_lvl;
+        int8_t* Lo = pass == 0 ? o->lo : o->alt_lo;
+        int8_t* Hi = pass == 0 ? o->hi : o->alt_hi;
+        uint8_t* Z = pass == 0 ? o->zsign : o->alt_zsign;
+        if (L) L[s * MN + f] = (int8_t)level_of_code(ec);
+        if (want) {
+          double vlo = Ylo[f] * R, vhi = Yhi[f] * R;
+          double w = TIE_REL * fabs(v);
+          if (v - w < vlo) vlo = v - w;
+          if (v + w > vhi) vhi = v + w;
+          int lo = e2m1_level_down(vlo), hi = e2m1_level_up(vhi);
+          int lv = level_of_code(ec);
+          if (lo > lv) lo = lv;
+          if (hi < lv) hi = lv;
+          if (Lo) Lo[s * MN + f] = (int8_t)lo;
+          if (Hi) Hi[s * MN + f] = (int8_t)hi;
+          if (Z) Z[s * MN + f] = (uint8_t)(Ylo[f] <= 0.0 && Yhi[f] >= 0.0);
+        }
+      }
+    }
+  }
+  return 0;
+}
+
+static void* worker(void* arg) {
+  job_t* j = (job_t*)arg;
+  const fqo_params* p = j->p;
+  const int64_t M = p->M, N = p->N, MN = M * N;
+  double* P1 = (double*)malloc((size_t)(M * M) * sizeof(double));
+  double* P2 = p->two_sided ? (double*)malloc((size_t)(N * N) * sizeof(double)) : NULL;
+  double* ws = (double*)malloc((size_t)(7 * MN) * sizeof(double));
+  if (!P1 || !ws || (p->two_sided && !P2)) {
+    j->status = -2;
+    free(P1); free(P2); free(ws);
+    return NULL;
+  }
+  for (int64_t i = 0; i < M * M; ++i) P1[i] = dt_value(j->p1[i], p->dtype);
+  if (P2)
+    for (int64_t i = 0; i < N * N; ++i) P2[i] = dt_value(j->p2[i], p->dtype);
+  for (int64_t s = j->s_begin; s < j->s_end; ++s)
+    if (slice(p, j->x + s * MN, P1, P2, j->o, s, j->want_ranges, ws) != 0) j->status = -3;
+  free(P1); free(P2); free(ws);
+  return NULL;
+}
+
+/*
+ * Run the oracle on nslices consecutive slices x[nslices, M, N] (dtype bits).
+ * p2 is ignored when two_sided == 0.  Returns 0, or a negative value on a bad
+ * argument.  nthreads worker threads split the slices.
+ */
+int fqo_run(const fqo_params* p, const uint16_t* x, const uint16_t* p1, const uint16_t* p2,
+            int64_t nslices, const fqo_out* o, int nthreads) {
+  if (!p || !x || !p1 || !o || nslices < 0) return -1;
+  if (p->dtype != FQO_F16 && p->dtype != FQO_BF16) return -1;
+  if (p->M < 1 || p->N < 1 || p->M > 4096 || p->N > 4096) return -1;
+  if (p->mode == FQO_PER_TOKEN && !(p->clip_ratio > 0.0 && p->clip_ratio <= 1.0)) return -1;
+  if (p->two_sided && !p2) return -1;
+  if ((p->M * p->N) % 2 != 0 && o->packed) return -1;
+  const int want = (o->lo || o->hi || o->zsign || o->alt_lvl || o->alt_lo || o->alt_hi ||
+                    o->g_lo || o->g_hi || o->g_alt || o->scale_lo || o->scale_hi) ? 1 : 0;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  if (nthreads > nslices) nthreads = (int)(nslices > 0 ? nslices : 1);
+  pthread_t th[256];
+  job_t jobs[256];
+  int joinable[256] = {0};
+  int64_t per = nslices / nthreads, extra = nslices % nthreads, b = 0;
+  for (int t = 0; t < nthreads; ++t) {
+    int64_t n = per + (t < extra ? 1 : 0);
+    jobs[t] = (job_t){p, x, p1, p2, o, b, b + n, want, 0};
+    b += n;
+    if (nthreads > 1 && pthread_create(&th[t], NULL, worker, &jobs[t]) == 0)
+      joinable[t] = 1;
+    else
+      worker(&jobs[t]);
+  }
+  int status = 0;
+  for (int t = 0; t < nthreads; ++t) {
+    if (joinable[t]) pthread_join(th[t], NULL);
+    if (jobs[t].status) status = jobs[t].status;
+  }
+  return status;
+}

@@ -1,0 +1,27 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: long-running CPU test")
+    # The oracle and the input generator are plain C built with gcc in a second; build
+    # them here if a checkout has not been built yet.  The HIP library is never built
+    # from the tests.
+    import oracle
+    import synth
+    if not os.path.exists(oracle.LIB_PATH):
+        oracle.build()
+    if not os.path.exists(synth.LIB_PATH):
+        synth.build()
+
+
+@pytest.fixture(scope="session")
+def golden_dir():
+    return os.path.join(ROOT, "tests", "golden")

@@ -1,0 +1,131 @@
+"""The comparator accepts what the tolerance rule allows and rejects the rest (CPU only)."""
+import numpy as np
+
+import oracle
+import synth
+from oracle.compare import compare, unpack_nibbles
+
+
+def _repack(codes):
+    codes = codes.astype(np.uint8)
+    return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+
+
+def _pertoken():
+    w = synth.WORKLOADS["c2"]
+    x, p1, p2 = synth.make_inputs(w, 0, 8)
+    return oracle.run(x, p1, p2, w.dtype, w.mode, w.clip_ratio)
+
+
+def _pergroup():
+    w = synth.WORKLOADS["c3"]
+    x, p1, p2 = synth.make_inputs(w, 0, 8)
+    return oracle.run(x, p1, p2, w.dtype, w.mode, w.clip_ratio, w.dst_type_max)
+
+
+def test_identical_passes():
+    r = _pertoken()
+    assert compare(r, r["packed"], r["scale"])["ok"]
+    g = _pergroup()
+    assert compare(g, g["packed"], g["e8m0"])["ok"]
+
+
+def test_unflagged_code_change_fails():
+    r = _pertoken()
+    codes = unpack_nibbles(r["packed"], r["M"] * r["N"])
+    s, f = np.argwhere(r["lo"] == r["hi"])[0]
+    codes[s, f] = (codes[s, f] + 1) & 0xF
+    assert not compare(r, _repack(codes), r["scale"])["ok"]
+
+
+def test_flagged_one_step_passes_two_steps_fail():
+    r = _pertoken()
+    codes = unpack_nibbles(r["packed"], r["M"] * r["N"])
+    idx = np.argwhere((r["hi"] > r["lvl"]))
+    assert len(idx) > 0
+    s, f = idx[0]
+    c1 = codes.copy()
+    c1[s, f] = (c1[s, f] + 1) & 0xF
+    rep = compare(r, _repack(c1), r["scale"])
+    assert rep["ok"] and rep["mismatch"] == 1
+    c2 = codes.copy()
+    c2[s, f] = (c2[s, f] + 2) & 0xF
+    assert not compare(r, _repack(c2), r["scale"])["ok"]
+
+
+def test_mismatch_cap():
+    r = _pertoken()
+    codes = unpack_nibbles(r["packed"], r["M"] * r["N"])
+    idx = np.argwhere((r["hi"] > r["lvl"]))
+    cap = int(np.ceil(1e-4 * codes.size))
+    if len(idx) <= cap:
+        # force the situation on a copy: mark more elements reachable
+        r = dict(r)
+        r["hi"] = np.minimum(r["lvl"] + 1, 7).astype(np.int8)
+        idx = np.argwhere(r["hi"] > r["lvl"])
+    c = codes.copy()
+    for s, f in idx[: cap + 1]:
+        c[s, f] = (c[s, f] + 1) & 0xF
+    rep = compare(r, _repack(c), r["scale"])
+    assert not rep["ok"] and rep["mismatch"] == cap + 1
+
+
+def test_scale_tolerance():
+    r = _pertoken()
+    ok = r["scale"] * np.float32(1 + 5e-6)
+    assert compare(r, r["packed"], ok)["ok"]
+    bad = r["scale"] * np.float32(1 + 2e-5)
+    assert not compare(r, r["packed"], bad)["ok"]
+
+
+def test_e8m0_change_and_pad():
+    g = _pergroup()
+    e = g["e8m0"].copy()
+    e[0, 0] += 1
+    assert not compare(g, g["packed"], e)["ok"]
+    # a group whose scale is reachable both ways accepts the alternative with its codes
+    r = dict(g)
+    r["g_alt"] = r["g_alt"].copy()
+    r["g_hi"] = r["g_hi"].copy()
+    r["g_alt"][0, 0] = r["e8m0"][0, 0] + 1
+    r["g_hi"][0, 0] = r["e8m0"][0, 0] + 1
+    r["alt_lvl"] = r["alt_lvl"].copy()
+    r["alt_lo"] = r["alt_lo"].copy()
+    r["alt_hi"] = r["alt_hi"].copy()
+    r["alt_lvl"][0, :32] = r["lvl"][0, :32]
+    r["alt_lo"][0, :32] = r["lvl"][0, :32]
+    r["alt_hi"][0, :32] = r["lvl"][0, :32]
+    e = g["e8m0"].copy()
+    e[0, 0] += 1
+    rep = compare(r, g["packed"], e)
+    assert rep["ok"] and rep["alt_groups"] == 1
+
+
+def test_pad_slot_must_be_zero():
+    rng = np.random.default_rng(0)
+    x = synth.round_to(rng.standard_normal((2, 3, 32)), "bf16")
+    eye3 = synth.round_to(np.eye(3), "bf16")
+    eye32 = synth.round_to(np.eye(32), "bf16")
+    g = oracle.run(x, eye3, eye32, "bf16", "fp4")
+    assert compare(g, g["packed"], g["e8m0"])["ok"]
+    e = g["e8m0"].copy()
+    e[1, 3] = 1
+    assert not compare(g, g["packed"], e)["ok"]
+
+
+def test_zero_sign_rule():
+    rng = np.random.default_rng(1)
+    x = synth.round_to(rng.standard_normal((1, 2, 32)) * 4, "bf16")
+    x[0, 0, 5] = 0x0000  # an exact zero in the input: y = 0 exactly, either sign allowed
+    x[0, 0, 7] = synth.round_to(np.array([-1e-3]), "bf16")[0]  # rounds to -0, sign fixed
+    eye2 = synth.round_to(np.eye(2), "bf16")
+    eye32 = synth.round_to(np.eye(32), "bf16")
+    g = oracle.run(x, eye2, eye32, "bf16", "fp4")
+    codes = unpack_nibbles(g["packed"], 64)
+    assert codes[0, 7] == 0x8
+    c = codes.copy()
+    c[0, 5] ^= 0x8
+    assert compare(g, _repack(c), g["e8m0"])["ok"]
+    c = codes.copy()
+    c[0, 7] ^= 0x8
+    assert not compare(g, _repack(c), g["e8m0"])["ok"]

@@ -1,0 +1,411 @@
+"""Pins of the oracle to what the pages and mathematics fix (CPU only).
+
+Each test ties one part of the oracle to something other than itself: values printed on
+the pages (fixtures under tests/golden), an independent library routine, a brute-force
+search, a closed form or an invariant.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from golden_io import keyed, rows
+
+pytestmark = pytest.mark.filterwarnings("ignore")
+
+
+def bf16(vals):
+    return synth.round_to(np.asarray(vals, dtype=np.float64), "bf16")
+
+
+def f32_of_bits(bits):
+    return (np.asarray(bits, dtype=np.uint32) << 16).view(np.float32)
+
+
+# ---------------------------------------------------------------- E2M1 encoder
+
+
+def test_e2m1_magnitudes_match_page_table():
+    mags = [float(v) for v in keyed("e2m1_table.txt")["magnitudes"]]
+    assert mags == [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+    for code in range(16):
+        v = oracle.e2m1_value(code)
+        assert abs(v) == mags[code & 7]
+        assert math.copysign(1.0, v) == (-1.0 if code & 8 else 1.0)
+        # decode -> encode round trip over all 16 codes (-0 keeps its sign bit)
+        assert oracle.e2m1_code(v) == code
+
+
+def test_e2m1_decision_points_from_page():
+    for r in rows("e2m1_table.txt")[1:]:
+        p, below, above, at = (float(t) for t in r)
+        lo = np.nextafter(p, 0.0)
+        hi = np.nextafter(p, np.inf)
+        assert oracle.e2m1_value(oracle.e2m1_code(lo)) == below
+        assert oracle.e2m1_value(oracle.e2m1_code(hi)) == above
+        assert oracle.e2m1_value(oracle.e2m1_code(p)) == at
+        assert oracle.e2m1_value(oracle.e2m1_code(-p)) == -at
+
+
+def _e2m1_by_format_rounding(v):
+    """E2M1 as a binary float format: 1 mantissa bit, exponents 0..2, subnormal quantum
+    0.5; round half to even with numpy's rint at the binade's quantum, saturate at 6."""
+    a = abs(v)
+    if a < 2.0:
+        q = 0.5
+    elif a < 4.0:
+        q = 1.0
+    else:
+        q = 2.0
+    r = float(np.rint(a / q)) * q
+    r = min(r, 6.0)
+    return math.copysign(r, v)
+
+
+def test_e2m1_dense_sweep_against_format_rounding():
+    pts = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0]
+    vals = list(np.linspace(-9, 9, 20001))
+    for p in pts:
+        for s in (-1, 1):
+            x = s * p
+            vals += [x, np.nextafter(x, -np.inf), np.nextafter(x, np.inf)]
+            vals += list(x + np.arange(-4, 5) * 2.0 ** -20)
+    for v in vals:
+        v = float(v)
+        got = oracle.e2m1_value(oracle.e2m1_code(v))
+        want = _e2m1_by_format_rounding(v)
+        assert got == want, (v, got, want)
+
+
+# ---------------------------------------------------------------- int4 encoder
+
+
+def test_int4_rne_examples_from_page():
+    for inp, exp in rows("rne_examples.txt"):
+        assert oracle.int4_code(float(inp)) == int(float(exp))
+
+
+def test_int4_clamp_range_from_page():
+    k = keyed("int4_range.txt")
+    b, lo, hi = int(k["bits"][0]), int(k["min"][0]), int(k["max"][0])
+    assert (lo, hi) == (-(2 ** (b - 1)), 2 ** (b - 1) - 1)
+    assert oracle.int4_code(-100.0) == lo and oracle.int4_code(100.0) == hi
+    assert oracle.int4_code(-8.5) == -8 and oracle.int4_code(7.5) == 7
+    assert oracle.int4_code(-8.49) == -8 and oracle.int4_code(6.51) == 7
+
+
+def test_int4_brute_force_nearest_even():
+    codes = np.arange(-8, 8)
+    grid = list(np.linspace(-9.5, 8.5, 7201))
+    for n in range(-9, 9):
+        t = n + 0.5
+        grid += [t, float(np.nextafter(np.float32(t), np.float32(-np.inf))),
+                 float(np.nextafter(np.float32(t), np.float32(np.inf)))]
+    for q in grid:
+        q32 = float(np.float32(q))
+        d = np.abs(codes - q32)
+        best = codes[d == d.min()]
+        want = best[0] if len(best) == 1 else best[best % 2 == 0][0]
+        assert oracle.int4_code(q32) == want, q32
+
+
+# ---------------------------------------------------------------- dtype rounding
+
+
+def test_round_f32_matches_numpy_cast():
+    rng = np.random.default_rng(1)
+    v = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-40, 38, 20000),
+                        rng.standard_normal(2000) * 1e-42])
+    for x in v:
+        assert oracle.round_f32(float(x)) == float(np.float32(x))
+
+
+def test_round_f16_matches_numpy_cast():
+    rng = np.random.default_rng(2)
+    v = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-8, 5, 20000),
+                        (np.arange(-3000, 3000) + 0.5) * 2.0 ** -24])  # subnormal ties
+    for x in v:
+        want = float(np.float16(x))
+        got = oracle.round_dt(float(x), "f16")
+        assert got == want or (math.isinf(got) and math.isinf(want)), x
+
+
+def test_round_bf16_matches_torch_cast():
+    rng = np.random.default_rng(3)
+    v = (rng.standard_normal(20000) * 10.0 ** rng.integers(-30, 30, 20000)).astype(np.float32)
+    ties = (np.arange(1, 2000, dtype=np.float32) * 2 ** 7 + 2 ** 6).view(np.float32)  # exact ties
+    v = np.concatenate([v, ties[np.isfinite(ties)]])
+    want = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    for x, w in zip(v, want):
+        assert oracle.round_dt(float(x), "bf16") == w, x
+
+
+# ---------------------------------------------------------------- e8m0 scales
+
+
+def test_e8m0_v1_invariant_scaled_max_in_4_8():
+    rng = np.random.default_rng(4)
+    amax = np.float32(np.abs(rng.standard_normal(20000)) * 10.0 ** rng.integers(-30, 30, 20000))
+    for a in amax:
+        if a == 0:
+            continue
+        c = oracle.e8m0_v1(float(a))
+        assert 0 <= c <= 254
+        r = float(a) * 2.0 ** (127 - c)  # scale 2^(c-127) is a power of two by construction
+        assert 4.0 <= r < 8.0, (a, c)
+
+
+def test_e8m0_v2_invariant_scaled_max_in_half_dmax_dmax():
+    rng = np.random.default_rng(5)
+    amax = np.float32(np.abs(rng.standard_normal(20000)) * 10.0 ** rng.integers(-30, 30, 20000))
+    for dmax in (6.0, 7.5, 8.0, 10.0, 12.0):
+        for a in amax:
+            c = oracle.e8m0_v2(float(a), dmax)
+            S = float(np.float32(np.float32(a) / np.float32(dmax)))
+            if S < 2.0 ** -126:
+                continue
+            r = float(a) * 2.0 ** (127 - c)
+            assert dmax / 2 < r <= dmax * (1 + 2.0 ** -23), (a, dmax, c)
+
+
+def test_e8m0_v2_bits_and_frexp_agree():
+    rng = np.random.default_rng(6)
+    vals = list(np.float32(np.abs(rng.standard_normal(50000)) * 10.0 ** rng.integers(-44, 38, 50000)))
+    vals += [np.float32(2.0 ** e) for e in range(-140, 128)]
+    vals += [np.nextafter(np.float32(2.0 ** e), np.float32(0)) for e in range(-120, 128)]
+    vals += [np.float32(0.0), np.float32(1e-45), np.float32(3.4e38)]
+    for dmax in (6.0, 8.0, 11.0, 12.0):
+        for a in vals:
+            assert oracle.e8m0_v2(float(a), dmax, "bits") == oracle.e8m0_v2(float(a), dmax, "frexp"), a
+
+
+def test_v2_dmax8_equals_v1_except_powers_of_two():
+    """With dstTypeMax = 8: S = amax/8 is exact, so V2's ceil exponent equals V1's
+    floor(log2 amax) - 2 unless amax is a power of two, where it is one less."""
+    rng = np.random.default_rng(7)
+    vals = list(np.float32(np.abs(rng.standard_normal(20000)) * 10.0 ** rng.integers(-20, 20, 20000)))
+    vals += [np.float32(2.0 ** e) for e in range(-60, 60)]
+    for a in vals:
+        if a == 0:
+            continue
+        v1 = oracle.e8m0_v1(float(a))
+        v2 = oracle.e8m0_v2(float(a), 8.0)
+        m, _ = math.frexp(float(a))
+        assert v2 == (v1 - 1 if m == 0.5 else v1), a
+
+
+# ---------------------------------------------------------------- transform
+
+
+def _gen_small_exact(rng, M, N):
+    x = rng.integers(-4, 5, size=(1, M, N)).astype(np.float64)
+    p1 = rng.choice([-1.0, -0.5, 0.0, 0.5, 1.0], size=(M, M))
+    p2 = rng.choice([-1.0, -0.5, 0.0, 0.5, 1.0], size=(N, N))
+    return x, p1, p2
+
+
+@pytest.mark.parametrize("M,N", [(1, 2), (2, 2), (3, 4), (4, 8), (8, 8), (5, 6)])
+def test_kronecker_closed_form(M, N):
+    """vec_row(P1 x P2) = (P1 kron P2^T) vec_row(x), with inputs whose intermediate is
+    exact in bf16, so every reading of the intermediate precision agrees."""
+    rng = np.random.default_rng(M * 100 + N)
+    for _ in range(5):
+        x, p1, p2 = _gen_small_exact(rng, M, N)
+        r = oracle.run(bf16(x), bf16(p1), bf16(p2), "bf16", "fp4", want_y=True, ranges=False)
+        want = (np.kron(p1, p2.T) @ x.reshape(-1)).reshape(M, N)
+        assert np.array_equal(r["y"][0].astype(np.float64), want)
+        # left-only equals the two-sided transform with P2 = I
+        r2 = oracle.run(bf16(x), bf16(p1), None, "bf16", "fp4", want_y=True, ranges=False)
+        assert np.array_equal(r2["y"][0].astype(np.float64), p1 @ x[0])
+
+
+def test_transform_order_p2_first_then_p1():
+    """A non-exact intermediate makes the order observable: T = RNE(x P2) first."""
+    rng = np.random.default_rng(11)
+    M, N = 4, 4
+    x = rng.standard_normal((1, M, N))
+    p1 = rng.standard_normal((M, M))
+    p2 = rng.standard_normal((N, N))
+    xb, p1b, p2b = bf16(x), bf16(p1), bf16(p2)
+    r = oracle.run(xb, p1b, p2b, "bf16", "int32", want_y=True, want_t=True, ranges=False)
+    X, P1, P2 = (f32_of_bits(a).astype(np.float64) for a in (xb[0], p1b, p2b))
+    T = torch.from_numpy((X @ P2).astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(f32_of_bits(r["t"][0]).astype(np.float64), T)
+    assert np.array_equal(r["y"][0], (P1 @ T).astype(np.float32))
+
+
+def test_identity_permutation_sign_transforms_are_exact():
+    rng = np.random.default_rng(12)
+    M, N = 16, 32
+    x = synth.gen_x(M, N, "bf16", "gauss", 0.05, 20.0, seed=3, k0=0, k1=2)
+    for trial in range(3):
+        pm = np.eye(M)[rng.permutation(M)] * rng.choice([-1.0, 1.0], size=M)
+        pn = np.eye(N)[rng.permutation(N)] * rng.choice([-1.0, 1.0], size=N)
+        r = oracle.run(x, bf16(pm), bf16(pn), "bf16", "int32", want_y=True)
+        X = f32_of_bits(x).astype(np.float64)
+        want = np.einsum("im,kmn,nj->kij", pm, X, pn)
+        assert np.array_equal(r["y"].astype(np.float64), want)
+        # the transform is exact, so no code is ambiguous through the intermediate
+        assert (r["zsign"] == 0).all()
+
+
+# ---------------------------------------------------------------- per-token mode
+
+
+def test_worked_pertoken_example():
+    k = keyed("worked_pertoken.txt")
+    clip = float(k["clip"][0])
+    x = np.array([float(v) for v in k["x"]]).reshape(1, 2, 6)
+    r = oracle.run(bf16(x), bf16(np.eye(2)), bf16(np.eye(6)), "bf16", "int32", clip_ratio=clip)
+    assert r["scale"][0] == float(k["scale"][0])
+    codes = [int(v) for v in k["codes"]]
+    assert list(r["lvl"][0]) == codes
+    packed = r["packed"][0]
+    nib = [(b >> s) & 0xF for b in packed for s in (0, 4)]
+    assert nib == [c & 0xF for c in codes]
+
+
+@pytest.mark.parametrize("cfg", ["c1", "c2"])
+def test_pertoken_invariants(cfg):
+    w = synth.WORKLOADS[cfg]
+    x, p1, p2 = synth.make_inputs(w, 0, 8)
+    r = oracle.run(x, p1, p2, w.dtype, w.mode, w.clip_ratio, want_y=True)
+    y = r["y"].reshape(8, -1).astype(np.float64)
+    amax = np.abs(y).max(axis=1)
+    s = r["scale"].astype(np.float64)
+    d = float(np.float32(7.0 / w.clip_ratio))
+    assert np.all(np.abs(s * d - amax) <= amax * 2.0 ** -23)  # one fp32 rounding
+    c = r["lvl"].astype(np.float64)
+    unclamped = (c > -8) & (c < 7)
+    assert np.all(np.abs(y - c * s[:, None])[unclamped] <= (s[:, None] * 0.5 * (1 + 1e-6)).repeat(
+        y.shape[1], 1)[unclamped])
+    assert c.min() >= -8 and c.max() <= 7
+
+
+def test_pertoken_clip_below_one_reaches_minus_eight():
+    """clipRatio < 7/7.5 lets |q| exceed 7.5, so the int4 range's -8 is used."""
+    w = synth.WORKLOADS["c2"]
+    x, p1, p2 = synth.make_inputs(w, 0, 64)
+    r = oracle.run(x, p1, p2, w.dtype, w.mode, w.clip_ratio, ranges=False)
+    assert (r["lvl"] == -8).any()
+    r1 = oracle.run(x, p1, p2, w.dtype, w.mode, 1.0, ranges=False)
+    assert not (r1["lvl"] == -8).any()
+
+
+def test_pertoken_zero_slice():
+    x = np.zeros((2, 4, 8), np.uint16)
+    r = oracle.run(x, bf16(np.eye(4)), bf16(np.eye(8)), "bf16", "int32")
+    assert (r["scale"] == 0).all() and (r["packed"] == 0).all()
+    assert (r["lo"] == 0).all() and (r["hi"] == 0).all()
+
+
+# ---------------------------------------------------------------- per-group mode
+
+
+def _hexes(vals):
+    return [int(v, 16) for v in vals]
+
+
+def test_worked_pergroup_examples():
+    k = keyed("worked_pergroup.txt")
+    xa = np.array([float(v) for v in k["xA"]]).reshape(1, 1, 32)
+    one = bf16(np.ones((1, 1)))
+    eye = bf16(np.eye(32))
+
+    def codes(r):
+        return [(b >> s) & 0xF for b in r["packed"][0] for s in (0, 4)]
+
+    ra = oracle.run(bf16(xa), one, eye, "bf16", "fp4", dst_type_max=0.0)
+    assert ra["e8m0"][0, 0] == int(k["e8m0A_v1"][0])
+    assert codes(ra) == _hexes(k["codesA"])
+    xb = bf16(2 * xa)
+    for key, dmax in (("e8m0B_v1", 0.0), ("e8m0B_v2_6", 6.0), ("e8m0B_v2_8", 8.0),
+                      ("e8m0B_v2_10", 10.0)):
+        rb = oracle.run(xb, one, eye, "bf16", "fp4", dst_type_max=dmax)
+        assert rb["e8m0"][0, 0] == int(k[key][0]), key
+        if dmax in (0.0, 6.0, 8.0):
+            assert codes(rb) == _hexes(k["codesA"]), key
+        else:
+            assert codes(rb) == _hexes(k["codesB_v2_10"])
+    # left-only gives the same with an identity P1
+    rl = oracle.run(bf16(xa), one, None, "bf16", "fp4")
+    assert codes(rl) == _hexes(k["codesA"])
+
+
+@pytest.mark.parametrize("dmax,lo,hi", [(0.0, 4.0, 8.0), (6.0, 3.0, 6.0), (8.0, 4.0, 8.0),
+                                        (10.0, 5.0, 10.0), (12.0, 6.0, 12.0)])
+def test_pergroup_scale_invariants(dmax, lo, hi):
+    w = synth.WORKLOADS["c3"]
+    x, p1, p2 = synth.make_inputs(w, 0, 4)
+    r = oracle.run(x, p1, p2, w.dtype, "fp4", dst_type_max=dmax, want_y=True, ranges=False)
+    y = r["y"].reshape(4, -1, 32).astype(np.float64)
+    amax = np.abs(y).max(axis=2)
+    code = r["e8m0"][:, : amax.shape[1]].astype(np.int64)
+    scaled = amax * 2.0 ** (127 - code)
+    if dmax == 0.0:
+        assert np.all((scaled >= lo) & (scaled < hi))
+    else:
+        assert np.all((scaled > lo) & (scaled <= hi * (1 + 2.0 ** -23)))
+
+
+def test_v1_and_v2_at_6_differ_and_v2_at_0_is_v1():
+    """dstTypeMax 0.0 behaves as V1 (floor exponent); 6.0 is the V2 ceil path and gives a
+    different scale for most groups."""
+    w = synth.WORKLOADS["c3"]
+    x, p1, p2 = synth.make_inputs(w, 0, 4)
+    r0 = oracle.run(x, p1, p2, w.dtype, "fp4", dst_type_max=0.0, want_y=True, ranges=False)
+    r6 = oracle.run(x, p1, p2, w.dtype, "fp4", dst_type_max=6.0, ranges=False)
+    y = r0["y"].reshape(4, -1, 32)
+    amax = np.abs(y).max(axis=2)
+    v1 = np.vectorize(lambda a: oracle.e8m0_v1(float(a)))(amax)
+    assert np.array_equal(r0["e8m0"][:, : amax.shape[1]], v1)
+    # V1 puts the group max in [4, 8) of the scale, V2 at 6 in (3, 6]: they differ exactly
+    # for the groups whose V1-scaled max exceeds 6
+    G = amax.shape[1]
+    scaled_v1 = amax.astype(np.float64) * 2.0 ** (127 - r0["e8m0"][:, :G].astype(np.int64))
+    differ = r6["e8m0"][:, :G] != r0["e8m0"][:, :G]
+    assert np.array_equal(differ, scaled_v1 > 6.0)
+    assert differ.any() and not differ.all()
+
+
+def test_partial_group_and_pad_slot():
+    """M*N = 30: one partial group; 96: three groups, so the [.., 2] pair has a pad slot."""
+    rng = np.random.default_rng(13)
+    for M, N in ((3, 10), (3, 32), (1, 2)):
+        x = bf16(rng.standard_normal((2, M, N)) * 3)
+        r = oracle.run(x, bf16(np.eye(M)), bf16(np.eye(N)), "bf16", "fp4", want_y=True)
+        MN = M * N
+        G, GS = -(-MN // 32), 2 * (-(-MN // 64))
+        assert r["e8m0"].shape == (2, GS)
+        if GS > G:
+            assert (r["e8m0"][:, G:] == 0).all()
+        for s in range(2):
+            for g in range(G):
+                a = np.abs(r["y"][s].reshape(-1)[32 * g:32 * g + 32]).max()
+                assert r["e8m0"][s, g] == oracle.e8m0_v1(float(a))
+
+
+# ---------------------------------------------------------------- layouts
+
+
+def test_example_shapes_from_page():
+    k = keyed("example_shapes.txt")
+    K, M, N = (int(v) for v in k["x"][1:])
+    out_shape = tuple(int(v) for v in k["out"][1:])
+    assert out_shape == (K, M, N // 8)
+    assert tuple(int(v) for v in k["quantScale"][1:]) == (K,)
+    x = synth.gen_x(M, N, "f16", "gauss", 0.0, 1.0, 0, 0, K)
+    p = synth.gen_orthogonal(M, "f16", 0, 2)
+    r = oracle.run(x, p, synth.gen_orthogonal(N, "f16", 0, 3), "f16", "int32",
+                   clip_ratio=float(k["clipRatio"][0]), ranges=False)
+    # INT32 [K, M, N/8] holds 8 codes per little-endian word, low nibble first, which is
+    # byte for byte the INT4 [K, M, N] layout (2 per byte, low nibble first)
+    words = r["packed"].reshape(-1).view("<i4").reshape(out_shape)
+    lv = r["lvl"].reshape(K, M, N)
+    for i in range(8):
+        nib = ((words.astype(np.int64) >> (4 * i)) & 0xF)
+        assert np.array_equal(np.where(nib >= 8, nib - 16, nib), lv[:, :, i::8])
+    assert r["scale"].shape == (K,)
