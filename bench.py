@@ -1,0 +1,195 @@
+"""Throughput benchmark of the fused transform + dynamic quantization operator on one GPU.
+
+A step is one fq_run over the whole workload: every slice x_k of x[K, M, N] is
+transformed (P1 . x_k . P2) and quantized, codes and scales written to HBM.  The
+default workload is K=8192, M=N=64 (hidden 4096), bf16 activations N(0,1) with 1% of
+the channels x20, random orthogonal P1/P2, per-token int4 packed in INT32, clipRatio
+0.9.  Inputs are resident in HBM before the timed region; several input/output sets are
+rotated so the 256 MB last-level cache cannot serve the reads.
+
+Prints one JSON line with the metric (Gelem/s of x), the roofline record of the fused
+kernel (its average launch time measured with HIP events on its own stream) and the
+CPU oracle's throughput on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16/fp16 MFMA, TFLOP/s
+
+
+def algorithmic_bytes(w, K=None) -> int:
+    """Bytes one launch must move: read x, P1, P2 once; write codes (0.5 B/elem) and scales."""
+    K = w.K if K is None else K
+    MN = w.M * w.N
+    b = 2 * K * MN + 2 * w.M * w.M + (2 * w.N * w.N if w.two_sided else 0) + K * MN // 2
+    if w.mode == "fp4":
+        b += K * 2 * (-(-MN // 64))
+    else:
+        b += 4 * K
+    return b
+
+
+def algorithmic_flops(w, K=None) -> int:
+    K = w.K if K is None else K
+    f = 2 * w.M * w.M * w.N
+    if w.two_sided:
+        f += 2 * w.M * w.N * w.N
+    return K * f
+
+
+def cpu_baseline(w, x_host, p1, p2, budget_s: float = 10.0):
+    """The oracle (codes and scales only) on the host cores, on a bounded sample of
+    slices of the same workload, scaled to Gelem/s."""
+    import oracle
+
+    threads = max(1, min(os.cpu_count() or 1, 64))
+    n0 = min(w.K, max(threads, 16 if w.M * w.N > 16384 else 64))
+    t = time.perf_counter()
+    oracle.run_codes_only(x_host[:n0], p1, p2, w.dtype, w.mode, w.clip_ratio, w.dst_type_max, threads)
+    dt0 = time.perf_counter() - t
+    n = min(w.K, max(n0, int(n0 * budget_s / max(dt0, 1e-6))))
+    if n > n0:
+        t = time.perf_counter()
+        oracle.run_codes_only(x_host[:n], p1, p2, w.dtype, w.mode, w.clip_ratio, w.dst_type_max, threads)
+        dt = time.perf_counter() - t
+    else:
+        n, dt = n0, dt0
+    elems = n * w.M * w.N
+    return {"value": elems / dt / 1e9, "unit": "Gelem/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {w.K} slices ({elems} elements), {dt:.2f} s wall on {threads} threads"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="c2", help="workload key (c1..c5); c2 is the headline")
+    ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 generic, 2 mfma-small, 3 mfma-wide")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this operator shards over K with no communication, and "
+              "this build runs and reports a single MI355X only (--gpus 1).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import flatquant_transform_quant_amd as fq
+    import synth
+
+    w = synth.WORKLOADS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float16
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(tdt).to(dev)
+
+    x_host, p1, p2 = synth.make_inputs(w)
+    # rotate input/output sets so one lap touches > 2x the 256 MB last-level cache
+    per_set = algorithmic_bytes(w)
+    nsets = int(max(1, min(8, -(-(600 * 2 ** 20) // per_set))))
+    xs = [to_dev(x_host)]
+    for i in range(1, nsets):
+        # distinct buffers with the same values
+        xs.append(xs[0].clone())
+    p1d = to_dev(p1)
+    p2d = to_dev(p2) if p2 is not None else None
+    outs = [fq.empty_outputs(w.K, w.M, w.N, w.mode, dev) for _ in range(nsets)]
+    execs = [fq.Executor(xs[i], p1d, p2d, outs[i][0], outs[i][1], w.mode, w.clip_ratio,
+                         w.dst_type_max, kernel=args.kernel) for i in range(nsets)]
+    kernel_id = execs[0].kernel
+    stream = torch.cuda.Stream(dev)  # the kernels' stream; events are recorded on it
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        execs[i % nsets].run(stream)
+    torch.cuda.synchronize()
+
+    # whole-job timing over exactly `steps` steps
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        execs[i % nsets].run(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+
+    # per-launch duration of the fused kernel: an event pair around each launch
+    n_launch = min(args.steps, 100)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_launch)]
+    torch.cuda.synchronize()
+    for i in range(n_launch):
+        evs[i][0].record(stream)
+        execs[i % nsets].run(stream)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    launch_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    avg_launch_ms = sum(launch_ms) / len(launch_ms)
+
+    elems = w.K * w.M * w.N
+    value = elems * args.steps / (total_ms / 1e3) / 1e9
+    bytes_ = algorithmic_bytes(w)
+    flops = algorithmic_flops(w)
+    gbs = bytes_ / (avg_launch_ms / 1e3) / 1e9
+    tfs = flops / (avg_launch_ms / 1e3) / 1e12
+    hbm_frac = gbs / HBM_PEAK_GBS
+    mfma_frac = tfs / MFMA_BF16_PEAK_TFS
+    bound = "hbm" if bytes_ / (HBM_PEAK_GBS * 1e9) >= flops / (MFMA_BF16_PEAK_TFS * 1e12) else "mfma"
+    roof = ({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(hbm_frac, 4), "traffic": None}
+            if bound == "hbm" else
+            {"bound": "mfma", "achieved": round(tfs, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+             "frac": round(mfma_frac, 4), "traffic": None})
+    roof["kernel"] = {1: "generic_kernel", 2: "mfma_small_kernel", 3: "mfma_wide_kernel"}.get(kernel_id)
+    roof["avg_launch_us"] = round(avg_launch_ms * 1e3, 3)
+    roof["median_launch_us"] = round(launch_ms[len(launch_ms) // 2] * 1e3, 3)
+    roof["algorithmic_bytes"] = bytes_
+    roof["algorithmic_flops"] = flops
+    roof["other_frac"] = round(mfma_frac if bound == "hbm" else hbm_frac, 4)
+
+    for e in execs:
+        e.destroy()
+    cpu = None if args.no_cpu else cpu_baseline(w, x_host, p1, p2, args.cpu_budget)
+    line = {
+        "metric": "Gelem/s quantized (x[K,M,N] elems) + % of HBM/MFMA roofline, 1 MI355X",
+        "value": round(value, 2),
+        "unit": "Gelem/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "K": w.K, "M": w.M, "N": w.N, "mode": w.mode,
+                   "clip_ratio": w.clip_ratio, "dst_type_max": w.dst_type_max,
+                   "two_sided": w.two_sided, "buffer_sets": nsets, "parallelism": "none"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,84 @@
+// Device-side element codecs of libfq: 16-bit loads, rounding of the intermediate to
+// the input dtype, the int4 and E2M1 encoders and the e8m0 scale rules.
+//
+// Operator page "aclnnFlatQuantV2 算子拆解" ([FQV2]), section 拆开算: 第3步 (per-token
+// int4 scale and per-group power-of-two scale), 第4步 (V2 ceil-exponent scale).  The
+// E2M1 magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6} are those of the E2M1 table of the
+// ModelOpt Conv3D page (section 6.1).  Rounding is half-to-even throughout.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "fq_internal.h"
+
+namespace fq {
+
+template <int DT>
+__device__ __forceinline__ float load16(uint16_t bits) {
+  if constexpr (DT == kBF16) {
+    return __uint_as_float(static_cast<uint32_t>(bits) << 16);
+  } else {
+    _Float16 h = __builtin_bit_cast(_Float16, bits);
+    return static_cast<float>(h);
+  }
+}
+
+// fp32 -> dtype, round to nearest even (hardware conversions).
+template <int DT>
+__device__ __forceinline__ uint16_t round16(float v) {
+  if constexpr (DT == kBF16) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
+  } else {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
+  }
+}
+
+// Two fp32 values -> two dtype values packed in one dword (low half = a).
+template <int DT>
+__device__ __forceinline__ uint32_t round16x2(float a, float b) {
+  return static_cast<uint32_t>(round16<DT>(a)) | (static_cast<uint32_t>(round16<DT>(b)) << 16);
+}
+
+// int4 code of q = y / scale: round half to even, clamp to [-8, 7]; returns the 4-bit
+// two's-complement nibble.
+__device__ __forceinline__ uint32_t int4_nibble(float q) {
+  float r = __builtin_rintf(q);
+  r = fminf(fmaxf(r, -8.0f), 7.0f);
+  return static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xFu;
+}
+
+// E2M1 code (sign << 3 | magnitude index) by counting the decision points passed.
+// At a decision point the even index wins: the points in front of an even index
+// (0.75, 1.75, 3.5) are passed at equality, the others (0.25, 1.25, 2.5, 5) only when
+// exceeded.  Above 6 the index stays 7 (saturation).
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = __builtin_fabsf(v);
+  uint32_t i = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
+               (a >= 3.5f) + (a > 5.0f);
+  return ((__float_as_uint(v) >> 28) & 0x8u) | i;
+}
+
+// e8m0 code of a group's max |y|.
+//  V1 (dmax == 0): floor(log2 amax) - 2 + 127 in [0, 254] -- for a normal amax that is
+//    its biased exponent field minus 2; a subnormal or zero amax gives 0.
+//  V2: S = amax / dmax (IEEE fp32); biased exponent E of S, plus one when S is normal,
+//    E < 254 and S's mantissa is non-zero.
+__device__ __forceinline__ uint32_t e8m0_code(float amax, float dmax) {
+  if (dmax == 0.0f) {
+    const int e = static_cast<int>((__float_as_uint(amax) >> 23) & 0xFFu) - 2;
+    return static_cast<uint32_t>(e < 0 ? 0 : (e > 254 ? 254 : e));
+  }
+  const uint32_t s = __float_as_uint(amax / dmax);
+  uint32_t E = (s >> 23) & 0xFFu;
+  if (E >= 1u && E < 254u && (s & 0x7FFFFFu) != 0u) E += 1u;
+  return E;
+}
+
+// y * 2^(127 - code): exact (v_ldexp), the reciprocal of the e8m0 scale.
+__device__ __forceinline__ float apply_e8m0(float y, uint32_t code) {
+  return __builtin_amdgcn_ldexpf(y, 127 - static_cast<int>(code));
+}
+
+}  // namespace fq

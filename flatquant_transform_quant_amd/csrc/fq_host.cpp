@@ -1,0 +1,350 @@
+// libfq host side: the C ABI of include/fq.h -- validation, planning, workspace
+// staging of non-contiguous tensors, and kernel dispatch.
+//
+// The call pattern and the checks follow the page "aclnnFlatQuantV2 算子拆解" (cited
+// as [FQV2]): sections 两段式接口 (two-stage call, the executor carries everything),
+// 参数速查 / 标量参数 (dtypes, shapes, scalar ranges) and 容易踩的坑 (error codes and
+// the order of the checks).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <unordered_set>
+
+#include "fq.h"
+#include "fq_internal.h"
+
+using fq::ceil_div;
+
+namespace {
+
+constexpr uint32_t kLiveMagic = 0xF0A17E55u;
+constexpr uint32_t kDeadMagic = 0xDEADF00Du;
+constexpr int64_t kMaxK = 262144;
+constexpr int64_t kMaxMN = 256;
+
+}  // namespace
+
+struct fq_executor {
+  uint32_t magic;
+  fq::Problem pb;
+  int32_t kernel;       // fq::Kernel actually launched (never kAuto)
+  int32_t repeatable;
+  fq_tensor x, p1, p2, out, scale;
+  bool stage_x, stage_p1, stage_p2, stage_out, stage_scale;
+  uint64_t off_x, off_p1, off_p2, off_out, off_scale, ws_size;
+};
+
+namespace {
+
+bool is_contiguous(const fq_tensor& t) {
+  int64_t expect = 1;
+  for (int d = t.ndim - 1; d >= 0; --d) {
+    if (t.shape[d] != 1 && t.strides[d] != expect) return false;
+    expect *= t.shape[d];
+  }
+  return true;
+}
+
+bool strides_ok(const fq_tensor& t) {
+  if (t.ndim < 0 || t.ndim > 4) return false;
+  for (int d = 0; d < t.ndim; ++d)
+    if (t.shape[d] < 0 || t.strides[d] < 0) return false;
+  return true;
+}
+
+bool shape_is(const fq_tensor& t, int nd, int64_t a, int64_t b = 0, int64_t c = 0) {
+  if (t.ndim != nd) return false;
+  const int64_t want[3] = {a, b, c};
+  for (int d = 0; d < nd; ++d)
+    if (t.shape[d] != want[d]) return false;
+  return true;
+}
+
+uint64_t align256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
+
+// gfx950 check, cached per device id.
+std::mutex g_arch_mu;
+int g_arch_ok[64];  // 0 unknown, 1 yes, -1 no
+
+bool device_is_gfx950() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return false;
+  if (dev < 64) {
+    std::lock_guard<std::mutex> lk(g_arch_mu);
+    if (g_arch_ok[dev]) return g_arch_ok[dev] > 0;
+  }
+  hipDeviceProp_t prop;
+  bool ok = false;
+  if (hipGetDeviceProperties(&prop, dev) == hipSuccess)
+    ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) {
+    std::lock_guard<std::mutex> lk(g_arch_mu);
+    g_arch_ok[dev] = ok ? 1 : -1;
+  }
+  return ok;
+}
+
+// Executors handed out and not yet released.  fq_run and the other calls look a pointer
+// up here before touching it, so a released (single-use, already run) executor is
+// reported as invalid instead of being read after free.
+std::mutex g_live_mu;
+std::unordered_set<const fq_executor*> g_live;
+
+bool live(const fq_executor* e) {
+  if (!e) return false;
+  std::lock_guard<std::mutex> lk(g_live_mu);
+  return g_live.count(e) != 0 && e->magic == kLiveMagic;
+}
+
+bool kernel_supports(int32_t k, const fq::Problem& pb) {
+  switch (k) {
+    case fq::kGeneric: return true;
+    case fq::kMfmaSmall: return fq::mfma_small_supports(pb);
+    case fq::kMfmaWide: return fq::mfma_wide_supports(pb);
+    default: return false;
+  }
+}
+
+int32_t auto_kernel(const fq::Problem& pb) {
+  if (fq::mfma_wide_supports(pb)) return fq::kMfmaWide;
+  if (fq::mfma_small_supports(pb)) return fq::kMfmaSmall;
+  return fq::kGeneric;
+}
+
+}  // namespace
+
+extern "C" {
+
+fq_status fq_get_workspace_size(const fq_tensor* x, const fq_tensor* kroneckerP1,
+                                const fq_tensor* kroneckerP2, double clipRatio, double dstTypeMax,
+                                const fq_tensor* out, const fq_tensor* quantScale,
+                                uint64_t* workspaceSize, fq_executor** executor) {
+  // [FQV2] 容易踩的坑: a NULL among the three inputs and two outputs -> 161001.
+  if (!x || !kroneckerP1 || !kroneckerP2 || !out || !quantScale || !workspaceSize || !executor)
+    return FQ_ERR_PARAM_NULLPTR;
+  const bool p2_empty = kroneckerP2->ndim == 2 && kroneckerP2->shape[0] == 0 &&
+                        kroneckerP2->shape[1] == 0;
+  if (!x->data || !kroneckerP1->data || !out->data || !quantScale->data ||
+      (!kroneckerP2->data && !p2_empty))
+    return FQ_ERR_PARAM_NULLPTR;
+
+  // Then clipRatio in (0, 1] and x's dimension ranges [1,262144] x [1,256] x [1,256].
+  if (!(clipRatio > 0.0 && clipRatio <= 1.0)) return FQ_ERR_PARAM_INVALID;
+  if (x->ndim != 3) return FQ_ERR_PARAM_INVALID;
+  const int64_t K = x->shape[0], M = x->shape[1], N = x->shape[2];
+  if (K < 1 || K > kMaxK || M < 1 || M > kMaxMN || N < 1 || N > kMaxMN) return FQ_ERR_PARAM_INVALID;
+
+  // Then the remaining rules ([FQV2] 参数速查, 标量参数, 容易踩的坑).
+  for (const fq_tensor* t : {x, kroneckerP1, kroneckerP2, out, quantScale})
+    if (!strides_ok(*t)) return FQ_ERR_PARAM_INVALID;
+  const int32_t dt = x->dtype;
+  if (dt != FQ_DT_FLOAT16 && dt != FQ_DT_BFLOAT16) return FQ_ERR_PARAM_INVALID;
+  if (kroneckerP1->dtype != dt || kroneckerP2->dtype != dt) return FQ_ERR_PARAM_INVALID;
+  if (!shape_is(*kroneckerP1, 2, M, M)) return FQ_ERR_PARAM_INVALID;
+  if (!p2_empty && !shape_is(*kroneckerP2, 2, N, N)) return FQ_ERR_PARAM_INVALID;
+
+  int32_t mode;
+  const int64_t MN = M * N;
+  switch (out->dtype) {
+    case FQ_DT_INT32:
+      if (N % 8 != 0 || !shape_is(*out, 3, K, M, N / 8)) return FQ_ERR_PARAM_INVALID;
+      mode = fq::kPerTokenInt32;
+      break;
+    case FQ_DT_INT4:
+      if (N % 2 != 0 || !shape_is(*out, 3, K, M, N)) return FQ_ERR_PARAM_INVALID;
+      mode = fq::kPerTokenInt4;
+      break;
+    case FQ_DT_FLOAT4_E2M1:
+      if (N % 2 != 0 || !shape_is(*out, 2, K, MN)) return FQ_ERR_PARAM_INVALID;
+      mode = fq::kPerGroupFp4;
+      break;
+    default:
+      return FQ_ERR_PARAM_INVALID;
+  }
+  if (mode == fq::kPerGroupFp4) {
+    if (quantScale->dtype != FQ_DT_FLOAT8_E8M0 || !shape_is(*quantScale, 3, K, ceil_div(MN, 64), 2))
+      return FQ_ERR_PARAM_INVALID;
+  } else {
+    if (quantScale->dtype != FQ_DT_FLOAT32 || !shape_is(*quantScale, 1, K)) return FQ_ERR_PARAM_INVALID;
+    if (p2_empty) return FQ_ERR_PARAM_INVALID;  // [0, 0] P2 is for the per-group mode only
+  }
+  if (!(dstTypeMax == 0.0 || (dstTypeMax >= 6.0 && dstTypeMax <= 12.0))) return FQ_ERR_PARAM_INVALID;
+  // 4-bit outputs: innermost stride 1, other strides whole bytes.
+  if (out->dtype == FQ_DT_INT4 || out->dtype == FQ_DT_FLOAT4_E2M1) {
+    if (out->strides[out->ndim - 1] != 1) return FQ_ERR_PARAM_INVALID;
+    for (int d = 0; d + 1 < out->ndim; ++d)
+      if (out->strides[d] % 2 != 0) return FQ_ERR_PARAM_INVALID;
+  }
+
+  fq_executor* e = new (std::nothrow) fq_executor();
+  if (!e) return FQ_ERR_RUNTIME;
+  e->magic = kLiveMagic;
+  e->pb.dtype = dt == FQ_DT_FLOAT16 ? fq::kF16 : fq::kBF16;
+  e->pb.mode = mode;
+  e->pb.K = K;
+  e->pb.M = M;
+  e->pb.N = N;
+  e->pb.two_sided = p2_empty ? 0 : 1;
+  e->pb.d = static_cast<float>(7.0 / clipRatio);
+  e->pb.dmax = static_cast<float>(dstTypeMax);
+  e->kernel = auto_kernel(e->pb);
+  e->repeatable = 0;
+  e->x = *x;
+  e->p1 = *kroneckerP1;
+  e->p2 = *kroneckerP2;
+  e->out = *out;
+  e->scale = *quantScale;
+  e->stage_x = !is_contiguous(*x);
+  e->stage_p1 = !is_contiguous(*kroneckerP1);
+  e->stage_p2 = !p2_empty && !is_contiguous(*kroneckerP2);
+  e->stage_out = !is_contiguous(*out);
+  e->stage_scale = !is_contiguous(*quantScale);
+  uint64_t off = 0;
+  auto take = [&](bool need, uint64_t bytes) -> uint64_t {
+    if (!need) return 0;
+    uint64_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  e->off_x = take(e->stage_x, uint64_t(K * MN) * 2);
+  e->off_p1 = take(e->stage_p1, uint64_t(M * M) * 2);
+  e->off_p2 = take(e->stage_p2, uint64_t(N * N) * 2);
+  e->off_out = take(e->stage_out, uint64_t(K * MN / 2));
+  e->off_scale = take(e->stage_scale, mode == fq::kPerGroupFp4
+                                          ? uint64_t(K * fq::e8m0_bytes_per_slice(MN))
+                                          : uint64_t(K) * 4);
+  e->ws_size = off;
+  {
+    std::lock_guard<std::mutex> lk(g_live_mu);
+    g_live.insert(e);
+  }
+  *workspaceSize = off;
+  *executor = e;
+  return FQ_SUCCESS;
+}
+
+static void release(fq_executor* e) {
+  {
+    std::lock_guard<std::mutex> lk(g_live_mu);
+    g_live.erase(e);
+  }
+  e->magic = kDeadMagic;
+  delete e;
+}
+
+fq_status fq_run(void* workspace, uint64_t workspaceSize, fq_executor* executor, hipStream_t stream) {
+  if (!executor) return FQ_ERR_PARAM_NULLPTR;
+  if (!live(executor)) return FQ_ERR_PARAM_INVALID;
+  fq_executor* e = executor;
+  fq_status st = FQ_SUCCESS;
+  do {
+    if (e->ws_size > 0 && !workspace) { st = FQ_ERR_PARAM_NULLPTR; break; }
+    if (workspaceSize < e->ws_size) { st = FQ_ERR_PARAM_INVALID; break; }
+    if (!device_is_gfx950()) { st = FQ_ERR_RUNTIME; break; }
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    const fq::Problem& pb = e->pb;
+    const int64_t MN = pb.M * pb.N;
+    fq::Buffers b;
+    hipError_t err = hipSuccess;
+    auto gather = [&](const fq_tensor& t, bool stage, uint64_t off, int nd) -> const uint16_t* {
+      if (!stage) return static_cast<const uint16_t*>(t.data);
+      int64_t shape[3] = {1, 1, 1}, strides[3] = {0, 0, 0};
+      for (int d = 0; d < nd; ++d) {
+        shape[3 - nd + d] = t.shape[d];
+        strides[3 - nd + d] = t.strides[d];
+      }
+      uint16_t* dst = reinterpret_cast<uint16_t*>(ws + off);
+      if (err == hipSuccess) err = fq::launch_gather16(static_cast<const uint16_t*>(t.data), dst, shape,
+                                                       strides, stream);
+      return dst;
+    };
+    b.x = gather(e->x, e->stage_x, e->off_x, 3);
+    b.p1 = gather(e->p1, e->stage_p1, e->off_p1, 2);
+    b.p2 = pb.two_sided ? gather(e->p2, e->stage_p2, e->off_p2, 2) : nullptr;
+    b.codes = e->stage_out ? ws + e->off_out : static_cast<uint8_t*>(e->out.data);
+    b.scale = e->stage_scale ? static_cast<void*>(ws + e->off_scale) : e->scale.data;
+    if (err != hipSuccess) { st = FQ_ERR_RUNTIME; break; }
+    switch (e->kernel) {
+      case fq::kMfmaSmall: err = fq::launch_mfma_small(pb, b, stream); break;
+      case fq::kMfmaWide: err = fq::launch_mfma_wide(pb, b, stream); break;
+      default: err = fq::launch_generic(pb, b, stream); break;
+    }
+    if (err != hipSuccess) { st = FQ_ERR_RUNTIME; break; }
+    if (e->stage_out) {
+      // The codes as bytes: INT32 [K, M, N/8] words, INT4 [K, M, N/2] and
+      // FLOAT4_E2M1 [K, M*N/2] byte rows (strides in 4-bit elements halve).
+      int64_t shape[3], strides[3];
+      int eb;
+      if (e->out.dtype == FQ_DT_INT32) {
+        eb = 4;
+        for (int d = 0; d < 3; ++d) { shape[d] = e->out.shape[d]; strides[d] = e->out.strides[d]; }
+      } else if (e->out.dtype == FQ_DT_INT4) {
+        eb = 1;
+        shape[0] = pb.K; shape[1] = pb.M; shape[2] = pb.N / 2;
+        strides[0] = e->out.strides[0] / 2; strides[1] = e->out.strides[1] / 2; strides[2] = 1;
+      } else {
+        eb = 1;
+        shape[0] = 1; shape[1] = pb.K; shape[2] = MN / 2;
+        strides[0] = 0; strides[1] = e->out.strides[0] / 2; strides[2] = 1;
+      }
+      err = fq::launch_scatter(b.codes, e->out.data, eb, shape, strides, stream);
+    }
+    if (err == hipSuccess && e->stage_scale) {
+      int64_t shape[3], strides[3];
+      int eb;
+      if (pb.mode == fq::kPerGroupFp4) {
+        eb = 1;
+        for (int d = 0; d < 3; ++d) { shape[d] = e->scale.shape[d]; strides[d] = e->scale.strides[d]; }
+      } else {
+        eb = 4;
+        shape[0] = 1; shape[1] = 1; shape[2] = pb.K;
+        strides[0] = 0; strides[1] = 0; strides[2] = e->scale.strides[0];
+      }
+      err = fq::launch_scatter(b.scale, e->scale.data, eb, shape, strides, stream);
+    }
+    if (err != hipSuccess) { st = FQ_ERR_RUNTIME; break; }
+  } while (false);
+  if (!e->repeatable) release(e);
+  return st;
+}
+
+void fq_executor_destroy(fq_executor* executor) {
+  if (live(executor)) release(executor);
+}
+
+fq_status fq_executor_set_repeatable(fq_executor* executor, int32_t repeat) {
+  if (!executor) return FQ_ERR_PARAM_NULLPTR;
+  if (!live(executor)) return FQ_ERR_PARAM_INVALID;
+  executor->repeatable = repeat ? 1 : 0;
+  return FQ_SUCCESS;
+}
+
+fq_status fq_executor_set_kernel(fq_executor* executor, int32_t variant) {
+  if (!executor) return FQ_ERR_PARAM_NULLPTR;
+  if (!live(executor)) return FQ_ERR_PARAM_INVALID;
+  int32_t k = variant == fq::kAuto ? auto_kernel(executor->pb) : variant;
+  if (!kernel_supports(k, executor->pb)) return FQ_ERR_PARAM_INVALID;
+  executor->kernel = k;
+  return FQ_SUCCESS;
+}
+
+int32_t fq_executor_kernel(const fq_executor* executor) {
+  if (!live(executor)) return -1;
+  return executor->kernel;
+}
+
+const char* fq_status_string(fq_status status) {
+  switch (status) {
+    case FQ_SUCCESS: return "FQ_SUCCESS";
+    case FQ_ERR_PARAM_NULLPTR: return "FQ_ERR_PARAM_NULLPTR: a required pointer is NULL";
+    case FQ_ERR_PARAM_INVALID: return "FQ_ERR_PARAM_INVALID: a parameter failed validation";
+    case FQ_ERR_RUNTIME: return "FQ_ERR_RUNTIME: device is not gfx950 or a HIP call failed";
+    default: return "unknown libfq status";
+  }
+}
+
+}  // extern "C"

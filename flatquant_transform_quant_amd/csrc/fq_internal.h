@@ -1,0 +1,54 @@
+// Internal interface between the libfq host code and its HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace fq {
+
+enum Dtype16 : int32_t { kF16 = 1, kBF16 = 2 };
+enum Mode : int32_t { kPerTokenInt32 = 0, kPerTokenInt4 = 1, kPerGroupFp4 = 2 };
+enum Kernel : int32_t { kAuto = 0, kGeneric = 1, kMfmaSmall = 2, kMfmaWide = 3 };
+
+// One planned problem, as the kernels see it (all tensors contiguous).
+struct Problem {
+  int32_t dtype;      // kF16 | kBF16
+  int32_t mode;       // Mode
+  int64_t K, M, N;
+  int32_t two_sided;  // 0: P2 is [0, 0], the right multiply is skipped
+  float d;            // fl32(7 / clipRatio), the per-token divisor
+  float dmax;         // fl32(dstTypeMax); 0 selects V1
+};
+
+// Device buffers of one launch, in the packed contiguous layouts:
+//   x [K, M, N], p1 [M, M], p2 [N, N] (16-bit bits);
+//   codes: K * M*N/2 bytes, low nibble = lower flattened index;
+//   scale: float [K] (per token) or uint8 [K, 2*ceil(M*N/64)] (e8m0).
+struct Buffers {
+  const uint16_t* x;
+  const uint16_t* p1;
+  const uint16_t* p2;
+  uint8_t* codes;
+  void* scale;
+};
+
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ inline int64_t e8m0_bytes_per_slice(int64_t MN) { return 2 * ceil_div(MN, 64); }
+
+// Launchers (enqueue only; return the launch status).
+hipError_t launch_generic(const Problem& pb, const Buffers& b, hipStream_t s);
+bool mfma_small_supports(const Problem& pb);
+hipError_t launch_mfma_small(const Problem& pb, const Buffers& b, hipStream_t s);
+bool mfma_wide_supports(const Problem& pb);
+hipError_t launch_mfma_wide(const Problem& pb, const Buffers& b, hipStream_t s);
+
+// Strided 16-bit gather into a contiguous buffer: dst[i0, i1, i2] = src[i0*s0 + i1*s1 + i2*s2].
+hipError_t launch_gather16(const uint16_t* src, uint16_t* dst, const int64_t shape[3],
+                           const int64_t strides[3], hipStream_t s);
+// Strided scatter of a contiguous buffer of 1- or 4-byte elements:
+// dst[i0*s0 + i1*s1 + i2*s2] = src[i0, i1, i2].
+hipError_t launch_scatter(const void* src, void* dst, int elem_bytes, const int64_t shape[3],
+                          const int64_t strides[3], hipStream_t s);
+
+}  // namespace fq

@@ -1,0 +1,149 @@
+/*
+ * libfq -- fused small-matrix transform + dynamic low-bit quantization for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operator is the one stated on the page "aclnnFlatQuantV2 算子拆解：两步矩阵乘 +
+ * 动态量化，CANN 上怎么写一次讲清" (cited as [FQV2] with the page's section names).
+ * For every slice x_k [M, N] of x [K, M, N]:
+ *
+ *   T   = round_to_dtype(x_k . P2)          [FQV2] 拆开算, 第1步 (skipped when P2 is [0, 0])
+ *   y_k = P1 . T   (fp32, never stored)     [FQV2] 拆开算, 第2步
+ *
+ * then one of two dynamic quantizations ([FQV2] 拆开算, 第3步 and 第4步):
+ *
+ *   per token (out INT32 or INT4):
+ *       quantScale[k] = max|y_k| / (7 / clipRatio)              (fp32)
+ *       code          = clamp(round_half_even(y / quantScale[k]), -8, 7)
+ *   per group of 32 consecutive elements of the flattened slice (out FLOAT4_E2M1):
+ *       dstTypeMax == 0  (V1): e8m0 = floor(log2(group max)) - 2 + 127, clamped to [0, 254]
+ *       dstTypeMax in [6, 12] (V2): S = group max / dstTypeMax (fp32); e8m0 = the biased
+ *           exponent of S, plus one when S is normal, the exponent is below 254 and the
+ *           mantissa is non-zero
+ *       code = E2M1(y * 2^(127 - e8m0)), round half to even, saturating at +-6
+ *
+ * Readings of points the page leaves open: the intermediate T is rounded to x's dtype
+ * (the transforms must have x's dtype), y stays fp32, rounding is half-to-even
+ * everywhere, int4 clamps to [-8, 7], the V1 exponent offset is 2 (E2M1's largest value
+ * 6 = 1.5 * 2^2), 4-bit codes are packed low nibble first (INT32 words little-endian),
+ * groups may span rows, a last partial group uses the elements present, the pad byte of
+ * an odd group count is 0, and an all-zero slice or group gets scale 0 and codes 0.
+ *
+ * Calling pattern ([FQV2] 两段式接口): the first call validates, sizes the workspace
+ * and returns an executor that holds every parameter; the caller allocates the
+ * workspace only when its size is non-zero; the second call enqueues the work on a HIP
+ * stream and takes no tensors.
+ */
+#ifndef FQ_H
+#define FQ_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ([FQV2] 容易踩的坑) ------------------------------------------
+ * FQ_ERR_PARAM_NULLPTR: one of the five tensors (or its data pointer) is NULL, or an
+ *   output pointer of the call is NULL.
+ * FQ_ERR_PARAM_INVALID: every other failed check -- shape, dtype, clipRatio,
+ *   dstTypeMax, an empty P2 outside the per-group mode, a workspace that is too small,
+ *   an executor that is not live.
+ * FQ_ERR_RUNTIME: the device is not gfx950, or a HIP call failed while enqueueing. */
+typedef int32_t fq_status;
+#define FQ_SUCCESS 0
+#define FQ_ERR_PARAM_NULLPTR 161001
+#define FQ_ERR_PARAM_INVALID 161002
+#define FQ_ERR_RUNTIME 161003
+
+/* ---- tensor descriptors ----------------------------------------------------------
+ * [FQV2] 参数速查: all tensors are ND.
+ *   x            FLOAT16 | BFLOAT16       [K, M, N], 1 <= K <= 262144, 1 <= M, N <= 256
+ *   kroneckerP1  same dtype as x          [M, M]
+ *   kroneckerP2  same dtype as x          [N, N], or [0, 0] (per-group mode only)
+ *   out          INT32        [K, M, N/8]  (N % 8 == 0; 8 int4 codes per word)
+ *                INT4         [K, M, N]    (N even; 2 codes per byte)
+ *                FLOAT4_E2M1  [K, M*N]     (N even; 2 codes per byte)
+ *   quantScale   FLOAT32      [K]                          with INT32 / INT4 out
+ *                FLOAT8_E8M0  [K, ceilDiv(M*N, 64), 2]     with FLOAT4_E2M1 out
+ * `data` is a device pointer; it is never dereferenced by fq_get_workspace_size.
+ * `strides` are in elements of the tensor's dtype (for INT4 and FLOAT4_E2M1, in 4-bit
+ * elements).  Inputs may have any non-negative strides.  Outputs may be strided too,
+ * but the innermost dimension of INT4 / FLOAT4_E2M1 must have stride 1 and their other
+ * strides must be even (whole bytes).  Non-contiguous tensors are staged through the
+ * workspace.  The caller owns all tensor memory; it must stay valid until the work
+ * enqueued by fq_run has completed on the stream. */
+typedef enum {
+  FQ_DT_FLOAT16 = 1,
+  FQ_DT_BFLOAT16 = 2,
+  FQ_DT_FLOAT32 = 3,
+  FQ_DT_INT32 = 4,
+  FQ_DT_INT4 = 5,
+  FQ_DT_FLOAT4_E2M1 = 6,
+  FQ_DT_FLOAT8_E8M0 = 7
+} fq_dtype;
+
+typedef struct {
+  void* data;
+  int32_t dtype;      /* fq_dtype */
+  int32_t ndim;       /* 0 .. 4 */
+  int64_t shape[4];
+  int64_t strides[4];
+} fq_tensor;
+
+typedef struct fq_executor fq_executor; /* opaque, owned by the library */
+
+/* ---- first stage ([FQV2] 两段式接口, 容易踩的坑) ------------------------------------
+ * Validates the call, chooses the kernels and sizes the workspace.
+ *   clipRatio   in (0, 1]; used by the per-token mode only ([FQV2] 标量参数).
+ *   dstTypeMax  0.0 or in [6.0, 12.0]; used by the FLOAT4_E2M1 mode only; 0.0 is V1.
+ * Checks run in this order: NULL pointers (FQ_ERR_PARAM_NULLPTR), then clipRatio and
+ * the ranges of x's dimensions, then dtypes, shapes and dstTypeMax
+ * (FQ_ERR_PARAM_INVALID).  On success *workspaceSize holds the bytes fq_run needs (0
+ * when every tensor is contiguous) and *executor a new executor.  On failure no
+ * executor is created.  Host only: makes no HIP call and may run without a GPU. */
+fq_status fq_get_workspace_size(const fq_tensor* x, const fq_tensor* kroneckerP1,
+                                const fq_tensor* kroneckerP2, double clipRatio, double dstTypeMax,
+                                const fq_tensor* out, const fq_tensor* quantScale,
+                                uint64_t* workspaceSize, fq_executor** executor);
+
+/* ---- second stage ------------------------------------------------------------------
+ * Enqueues the fused computation on `stream` (0 = the null stream) and returns without
+ * synchronizing.  `workspace` is device memory of at least workspaceSize bytes (may be
+ * NULL when the planned size is 0).  By default the executor is single-use: fq_run
+ * releases it, whether it succeeds or fails.  A repeatable executor
+ * (fq_executor_set_repeatable) survives and must be released with fq_executor_destroy.
+ * Results are deterministic: the same inputs give the same bits on every run.
+ * Errors: NULL executor -> FQ_ERR_PARAM_NULLPTR; workspace NULL while needed ->
+ * FQ_ERR_PARAM_NULLPTR; workspace too small or executor not live ->
+ * FQ_ERR_PARAM_INVALID; not a gfx950 device, or a launch failure -> FQ_ERR_RUNTIME.
+ * Calls with distinct executors may come from different host threads. */
+fq_status fq_run(void* workspace, uint64_t workspaceSize, fq_executor* executor, hipStream_t stream);
+
+/* Releases an executor that will not be run (or a repeatable one).  NULL is a no-op. */
+void fq_executor_destroy(fq_executor* executor);
+
+/* Keeps the executor alive across fq_run calls (repeat != 0), e.g. to launch the same
+ * problem many times.  Returns FQ_ERR_PARAM_NULLPTR / FQ_ERR_PARAM_INVALID for a NULL or
+ * dead executor. */
+fq_status fq_executor_set_repeatable(fq_executor* executor, int32_t repeat);
+
+/* Kernel variant the executor will launch: 0 = the automatic choice, 1 = the generic
+ * kernel (any shape), 2 = the small-slice MFMA kernel, 3 = the whole-workgroup MFMA
+ * kernel for 256-class slices.  Selecting a variant that does not support the planned
+ * problem returns FQ_ERR_PARAM_INVALID and leaves the executor unchanged.  Meant for
+ * tests and benchmarks. */
+fq_status fq_executor_set_kernel(fq_executor* executor, int32_t variant);
+
+/* The variant the executor will launch (1, 2 or 3), or a negative value for NULL. */
+int32_t fq_executor_kernel(const fq_executor* executor);
+
+/* A static, human-readable name for a status code. */
+const char* fq_status_string(fq_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FQ_H */

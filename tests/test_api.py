@@ -1,0 +1,261 @@
+"""The C ABI: exported symbols, validation matrix, check order, workspace sizing and
+executor lifetime (CPU only: planning never touches a device).
+
+Error codes and the check order follow the aclnnFlatQuantV2 page, section 容易踩的坑:
+a NULL among the five tensors gives 161001; every other failure 161002; clipRatio and
+x's dimension ranges are checked before the other rules.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import flatquant_transform_quant_amd as fq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+DUMMY = 0x10000  # never dereferenced by the planner
+NULLP, INVAL, OK = fq.FQ_ERR_PARAM_NULLPTR, fq.FQ_ERR_PARAM_INVALID, fq.FQ_SUCCESS
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "fq.h"), encoding="utf-8").read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fq_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert "fq_get_workspace_size" in names and "fq_run" in names
+    for n in names:
+        assert hasattr(fq.lib, n), n
+    assert set(names) == set(fq.EXPORTS)
+
+
+def tens(dtype, shape, strides=None, data=DUMMY):
+    return fq.make_tensor(data, dtype, shape, strides)
+
+
+def problem(K=4, M=16, N=16, dt=fq.DT_BFLOAT16, mode="int32", p2_empty=False):
+    x = tens(dt, (K, M, N))
+    p1 = tens(dt, (M, M))
+    p2 = tens(dt, (0, 0), data=0) if p2_empty else tens(dt, (N, N))
+    if mode == "int32":
+        out, sc = tens(fq.DT_INT32, (K, M, N // 8)), tens(fq.DT_FLOAT32, (K,))
+    elif mode == "int4":
+        out, sc = tens(fq.DT_INT4, (K, M, N)), tens(fq.DT_FLOAT32, (K,))
+    else:
+        out = tens(fq.DT_FLOAT4_E2M1, (K, M * N))
+        sc = tens(fq.DT_FLOAT8_E8M0, (K, -(-(M * N) // 64), 2))
+    return dict(x=x, p1=p1, p2=p2, out=out, sc=sc)
+
+
+def plan(p, clip=1.0, dmax=0.0):
+    st, ws, ex = fq.fq_get_workspace_size(p["x"], p["p1"], p["p2"], clip, dmax, p["out"], p["sc"])
+    if ex:
+        fq.fq_executor_destroy(ex)
+    return st, ws
+
+
+@pytest.mark.parametrize("mode", ["int32", "int4", "fp4"])
+def test_valid_plans_have_zero_workspace(mode):
+    st, ws = plan(problem(mode=mode))
+    assert (st, ws) == (OK, 0)
+
+
+def test_example_problem_from_page_plans():
+    # fp16 x [16,16,16], P [16,16], out INT32 [16,16,2], scale [16], clip 1.0, dstTypeMax 0.0
+    assert plan(problem(16, 16, 16, fq.DT_FLOAT16, "int32")) == (OK, 0)
+
+
+@pytest.mark.parametrize("which", ["x", "p1", "p2", "out", "sc"])
+def test_null_tensor_is_161001(which):
+    p = problem()
+    p[which] = None
+    assert plan(p)[0] == NULLP
+    p = problem()
+    p[which] = tens(p[which].dtype, list(p[which].shape)[: p[which].ndim], data=0)
+    assert plan(p)[0] == NULLP
+
+
+def test_null_out_params_are_161001():
+    p = problem()
+    P = ctypes.byref
+    ws = ctypes.c_uint64()
+    ex = ctypes.c_void_p()
+    assert fq.lib.fq_get_workspace_size(P(p["x"]), P(p["p1"]), P(p["p2"]), 1.0, 0.0, P(p["out"]),
+                                        P(p["sc"]), None, P(ex)) == NULLP
+    assert fq.lib.fq_get_workspace_size(P(p["x"]), P(p["p1"]), P(p["p2"]), 1.0, 0.0, P(p["out"]),
+                                        P(p["sc"]), P(ws), None) == NULLP
+
+
+def test_null_beats_invalid():
+    p = problem()
+    p["out"] = None
+    assert plan(p, clip=5.0)[0] == NULLP
+
+
+@pytest.mark.parametrize("clip", [0.0, -0.5, 1.0000001, 2.0, float("nan"), float("inf")])
+def test_clip_ratio_range(clip):
+    assert plan(problem(), clip=clip)[0] == INVAL
+
+
+@pytest.mark.parametrize("clip", [1e-6, 0.5, 0.9, 1.0])
+def test_clip_ratio_ok(clip):
+    assert plan(problem(), clip=clip)[0] == OK
+
+
+@pytest.mark.parametrize("K,M,N", [(0, 16, 16), (262145, 16, 16), (4, 0, 16), (4, 257, 16),
+                                   (4, 16, 0), (4, 16, 264)])
+def test_x_dimension_ranges(K, M, N):
+    p = problem()
+    p["x"] = tens(fq.DT_BFLOAT16, (K, M, N))
+    assert plan(p)[0] == INVAL
+
+
+def test_x_dimension_extremes_ok():
+    assert plan(problem(262144, 1, 8))[0] == OK
+    assert plan(problem(1, 256, 256))[0] == OK
+    assert plan(problem(1, 1, 2, mode="fp4"))[0] == OK
+
+
+def test_order_clip_before_dtype():
+    # both clipRatio and the P1 dtype are wrong; either way 161002 (same class)
+    p = problem()
+    p["p1"] = tens(fq.DT_FLOAT16, (16, 16))
+    assert plan(p, clip=0.0)[0] == INVAL
+
+
+@pytest.mark.parametrize("bad", ["xdt", "p1dt", "p2dt", "p1shape", "p2shape", "xndim"])
+def test_dtype_and_shape_rules(bad):
+    p = problem()
+    if bad == "xdt":
+        p["x"] = tens(fq.DT_FLOAT32, (4, 16, 16))
+    elif bad == "p1dt":
+        p["p1"] = tens(fq.DT_FLOAT16, (16, 16))
+    elif bad == "p2dt":
+        p["p2"] = tens(fq.DT_FLOAT16, (16, 16))
+    elif bad == "p1shape":
+        p["p1"] = tens(fq.DT_BFLOAT16, (16, 8))
+    elif bad == "p2shape":
+        p["p2"] = tens(fq.DT_BFLOAT16, (8, 8))
+    elif bad == "xndim":
+        p["x"] = tens(fq.DT_BFLOAT16, (4, 256))
+    assert plan(p)[0] == INVAL
+
+
+def test_out_shape_rules():
+    p = problem(N=12, mode="int32")  # N % 8 != 0
+    p["out"] = tens(fq.DT_INT32, (4, 16, 1))
+    assert plan(p)[0] == INVAL
+    p = problem(N=16, mode="int32")
+    p["out"] = tens(fq.DT_INT32, (4, 16, 4))
+    assert plan(p)[0] == INVAL
+    p = problem(M=4, N=6, mode="int4")  # INT4 needs N even and out == x's shape
+    assert plan(p)[0] == OK
+    p["out"] = tens(fq.DT_INT4, (4, 4, 5))
+    assert plan(p)[0] == INVAL
+    p = problem(M=4, N=5, mode="fp4")
+    p["out"] = tens(fq.DT_FLOAT4_E2M1, (4, 20))
+    assert plan(p)[0] == INVAL  # N odd
+    p = problem(M=4, N=6, mode="fp4")
+    p["out"] = tens(fq.DT_FLOAT4_E2M1, (4, 4, 6))
+    assert plan(p)[0] == INVAL  # FLOAT4_E2M1 out is 2-D [K, M*N]
+
+
+def test_scale_rules():
+    p = problem(mode="int32")
+    p["sc"] = tens(fq.DT_FLOAT8_E8M0, (4, 4, 2))
+    assert plan(p)[0] == INVAL
+    p = problem(mode="int32")
+    p["sc"] = tens(fq.DT_FLOAT32, (4, 1))
+    assert plan(p)[0] == INVAL
+    p = problem(mode="fp4")
+    p["sc"] = tens(fq.DT_FLOAT32, (4,))  # not the [K] FP32 habit in the per-group mode
+    assert plan(p)[0] == INVAL
+    p = problem(M=3, N=32, mode="fp4")  # 96 elements: ceilDiv(96, 64) = 2
+    assert plan(p)[0] == OK
+    p["sc"] = tens(fq.DT_FLOAT8_E8M0, (4, 1, 2))
+    assert plan(p)[0] == INVAL
+
+
+def test_p2_empty_only_for_per_group():
+    assert plan(problem(mode="fp4", p2_empty=True))[0] == OK
+    assert plan(problem(mode="int32", p2_empty=True))[0] == INVAL
+    assert plan(problem(mode="int4", p2_empty=True))[0] == INVAL
+
+
+@pytest.mark.parametrize("dmax,ok", [(0.0, True), (6.0, True), (8.0, True), (12.0, True), (5.99, False),
+                                     (12.01, False), (-1.0, False), (3.0, False),
+                                     (float("nan"), False)])
+def test_dst_type_max_values(dmax, ok):
+    for mode in ("fp4", "int32"):  # validated in every mode, used by fp4 only
+        assert plan(problem(mode=mode), dmax=dmax)[0] == (OK if ok else INVAL)
+
+
+def test_strided_inputs_get_a_workspace():
+    p = problem()
+    p["x"] = tens(fq.DT_BFLOAT16, (4, 16, 16), (16, 64 * 16, 1))  # K and M axes swapped
+    st, ws = plan(p)
+    assert st == OK and ws >= 4 * 16 * 16 * 2
+    p = problem()
+    p["p2"] = tens(fq.DT_BFLOAT16, (16, 16), (1, 16))  # transposed view
+    st, ws = plan(p)
+    assert st == OK and ws >= 16 * 16 * 2
+
+
+def test_strided_outputs():
+    p = problem(mode="int4")
+    p["out"] = tens(fq.DT_INT4, (4, 16, 16), (2 * 16 * 32, 32, 1))  # padded rows
+    st, ws = plan(p)
+    assert st == OK and ws >= 4 * 16 * 16 // 2
+    p["out"] = tens(fq.DT_INT4, (4, 16, 16), (16 * 16, 16, 2))  # nibble-strided innermost
+    assert plan(p)[0] == INVAL
+    p["out"] = tens(fq.DT_INT4, (4, 16, 16), (16 * 17, 17, 1))  # odd row stride
+    assert plan(p)[0] == INVAL
+
+
+def test_negative_stride_rejected():
+    p = problem()
+    p["x"] = tens(fq.DT_BFLOAT16, (4, 16, 16), (256, -16, 1))
+    assert plan(p)[0] == INVAL
+
+
+def test_run_argument_checks_without_device():
+    p = problem()
+    st, ws, ex = fq.fq_get_workspace_size(p["x"], p["p1"], p["p2"], 1.0, 0.0, p["out"], p["sc"])
+    assert st == OK
+    assert fq.fq_run(0, 0, 0, 0) == NULLP  # NULL executor
+    # a strided problem needs its workspace
+    p2 = problem()
+    p2["x"] = tens(fq.DT_BFLOAT16, (4, 16, 16), (16, 64 * 16, 1))
+    st, ws2, ex2 = fq.fq_get_workspace_size(p2["x"], p2["p1"], p2["p2"], 1.0, 0.0, p2["out"], p2["sc"])
+    assert st == OK and ws2 > 0
+    assert fq.fq_executor_set_repeatable(ex2, True) == OK
+    assert fq.fq_run(0, ws2, ex2, 0) == NULLP          # NULL workspace while needed
+    assert fq.fq_run(DUMMY, ws2 - 1, ex2, 0) == INVAL  # too small
+    fq.fq_executor_destroy(ex2)
+    assert fq.fq_executor_set_repeatable(ex2, True) == INVAL  # released
+    # single-use executor: released by fq_run even when it fails (here: no device)
+    st = fq.fq_run(0, 0, ex, 0)
+    assert st in (fq.FQ_ERR_RUNTIME, OK)
+    assert fq.fq_run(0, 0, ex, 0) == INVAL
+    assert fq.fq_executor_kernel(ex) < 0
+
+
+def test_kernel_selection_api():
+    st, ws, ex = fq.fq_get_workspace_size(*[problem()[k] for k in ("x", "p1", "p2")], 1.0, 0.0,
+                                          problem()["out"], problem()["sc"])
+    assert st == OK
+    assert fq.fq_executor_kernel(ex) in (1, 2, 3)
+    assert fq.fq_executor_set_kernel(ex, fq.KERNEL_GENERIC) == OK
+    assert fq.fq_executor_kernel(ex) == fq.KERNEL_GENERIC
+    assert fq.fq_executor_set_kernel(ex, 99) == INVAL
+    assert fq.fq_executor_kernel(ex) == fq.KERNEL_GENERIC
+    fq.fq_executor_destroy(ex)
+    assert fq.fq_executor_set_kernel(0, 1) == NULLP
+
+
+def test_status_strings():
+    for s in (OK, NULLP, INVAL, fq.FQ_ERR_RUNTIME, 42):
+        assert isinstance(fq.status_string(s), str) and fq.status_string(s)
