@@ -100,18 +100,26 @@ bool live(const fq_executor* e) {
   return g_live.count(e) != 0 && e->magic == kLiveMagic;
 }
 
-bool kernel_supports(int32_t k, const fq::Problem& pb) {
+// The MFMA kernels load x 16 bytes at a time and store codes and scales up to 4 bytes
+// at a time; staged tensors live in the (256-byte aligned) workspace.
+bool vector_aligned(const fq_executor* e) {
+  auto al = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; };
+  return (e->stage_x || al(e->x.data, 16)) && (e->stage_out || al(e->out.data, 4)) &&
+         (e->stage_scale || al(e->scale.data, 4));
+}
+
+bool kernel_supports(int32_t k, const fq_executor* e) {
   switch (k) {
     case fq::kGeneric: return true;
-    case fq::kMfmaSmall: return fq::mfma_small_supports(pb);
-    case fq::kMfmaWide: return fq::mfma_wide_supports(pb);
+    case fq::kMfmaSmall: return vector_aligned(e) && fq::mfma_small_supports(e->pb);
+    case fq::kMfmaWide: return vector_aligned(e) && fq::mfma_wide_supports(e->pb);
     default: return false;
   }
 }
 
-int32_t auto_kernel(const fq::Problem& pb) {
-  if (fq::mfma_wide_supports(pb)) return fq::kMfmaWide;
-  if (fq::mfma_small_supports(pb)) return fq::kMfmaSmall;
+int32_t auto_kernel(const fq_executor* e) {
+  if (kernel_supports(fq::kMfmaWide, e)) return fq::kMfmaWide;
+  if (kernel_supports(fq::kMfmaSmall, e)) return fq::kMfmaSmall;
   return fq::kGeneric;
 }
 
@@ -191,7 +199,6 @@ fq_status fq_get_workspace_size(const fq_tensor* x, const fq_tensor* kroneckerP1
   e->pb.two_sided = p2_empty ? 0 : 1;
   e->pb.d = static_cast<float>(7.0 / clipRatio);
   e->pb.dmax = static_cast<float>(dstTypeMax);
-  e->kernel = auto_kernel(e->pb);
   e->repeatable = 0;
   e->x = *x;
   e->p1 = *kroneckerP1;
@@ -218,6 +225,7 @@ fq_status fq_get_workspace_size(const fq_tensor* x, const fq_tensor* kroneckerP1
                                           ? uint64_t(K * fq::e8m0_bytes_per_slice(MN))
                                           : uint64_t(K) * 4);
   e->ws_size = off;
+  e->kernel = auto_kernel(e);
   {
     std::lock_guard<std::mutex> lk(g_live_mu);
     g_live.insert(e);
@@ -326,8 +334,8 @@ fq_status fq_executor_set_repeatable(fq_executor* executor, int32_t repeat) {
 fq_status fq_executor_set_kernel(fq_executor* executor, int32_t variant) {
   if (!executor) return FQ_ERR_PARAM_NULLPTR;
   if (!live(executor)) return FQ_ERR_PARAM_INVALID;
-  int32_t k = variant == fq::kAuto ? auto_kernel(executor->pb) : variant;
-  if (!kernel_supports(k, executor->pb)) return FQ_ERR_PARAM_INVALID;
+  int32_t k = variant == fq::kAuto ? auto_kernel(executor) : variant;
+  if (!kernel_supports(k, executor)) return FQ_ERR_PARAM_INVALID;
   executor->kernel = k;
   return FQ_SUCCESS;
 }

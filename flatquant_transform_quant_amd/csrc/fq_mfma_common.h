@@ -1,0 +1,125 @@
+// Shared device helpers of the MFMA kernels: operand types, the 16x16x32 MFMA for either
+// dtype, wave-level reductions and the packed int4 / E2M1 encoders.
+//
+// gfx950 v_mfma_f32_16x16x32_{bf16,f16} lane layout (wave64, l = lane):
+//   A (16 x 32):  lane l holds row l%16, k = 8*(l/16) .. 8*(l/16)+7
+//   B (32 x 16):  lane l holds column l%16, k = 8*(l/16) .. 8*(l/16)+7
+//   C (16 x 16):  lane l holds column l%16, rows 4*(l/16) .. 4*(l/16)+3
+// The contraction index k may be relabelled freely as long as A and B agree; the
+// kernels use that to feed one product's accumulators into the next product without
+// moving data between lanes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "fq_codec.h"
+#include "fq_internal.h"
+
+namespace fq {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+
+template <int DT>
+__device__ __forceinline__ f32x4_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
+  if constexpr (DT == kBF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+}
+
+// DPP lane moves inside 16-lane rows.
+enum : int {
+  kDppQuadXor1 = 0xB1,    // quad_perm [1,0,3,2]
+  kDppQuadXor2 = 0x4E,    // quad_perm [2,3,0,1]
+  kDppRowHalfMirror = 0x141,
+  kDppRowMirror = 0x140,
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+
+// Max over aligned groups of SPAN consecutive lanes of a 16-lane row (SPAN = 1, 2, 4, 8, 16).
+template <int SPAN>
+__device__ __forceinline__ float group_max(float v) {
+  if constexpr (SPAN >= 2) v = fmaxf(v, dpp_f<kDppQuadXor1>(v));
+  if constexpr (SPAN >= 4) v = fmaxf(v, dpp_f<kDppQuadXor2>(v));
+  if constexpr (SPAN >= 8) v = fmaxf(v, dpp_f<kDppRowHalfMirror>(v));
+  if constexpr (SPAN >= 16) v = fmaxf(v, dpp_f<kDppRowMirror>(v));
+  return v;
+}
+
+// Max over the whole wave; every lane gets the result.
+__device__ __forceinline__ float wave_max(float v) {
+  v = group_max<16>(v);
+  {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  return v;
+}
+
+// ---- per-token int4 ------------------------------------------------------------------
+// RNE(y * inv) with the round-to-integer done by the fp32 adder: fma(y, inv, 1.5*2^23 + 8)
+// rounds the exact product once at unit spacing (ties to even, as 1.5*2^23 + 8 is even),
+// leaving code + 8 in the low mantissa bits.  The clamp to [-8, 7] is an integer clamp of
+// the bit pattern (needed only when 7/clipRatio can reach 7.5).  Result: low nibble =
+// code + 8, bits 4..7 zero, bits above are the constant's (ignored by the packers).
+constexpr float kInt4Magic = 12582920.0f;  // 1.5 * 2^23 + 8
+constexpr uint32_t kInt4MagicLo = 0x4B400000u;  // bits of 1.5 * 2^23 (code -8)
+constexpr uint32_t kInt4MagicHi = 0x4B40000Fu;  // code +7
+
+template <bool CLAMP>
+__device__ __forceinline__ uint32_t int4_biased(float y, float inv) {
+  uint32_t b = __float_as_uint(__builtin_fmaf(y, inv, kInt4Magic));
+  if constexpr (CLAMP) b = min(max(b, kInt4MagicLo), kInt4MagicHi);
+  return b;
+}
+
+// Two biased codes -> one byte (low nibble = first), in the low byte of the result.
+__device__ __forceinline__ uint32_t pair_byte(uint32_t lo, uint32_t hi) { return lo | (hi << 4); }
+
+// Low bytes of four dwords -> one dword (byte i from d_i).
+__device__ __forceinline__ uint32_t gather4(uint32_t d0, uint32_t d1, uint32_t d2, uint32_t d3) {
+  const uint32_t a = __builtin_amdgcn_perm(d1, d0, 0x0C0C0400u);  // [d0.b0, d1.b0, 0, 0]
+  const uint32_t b = __builtin_amdgcn_perm(d3, d2, 0x0C0C0400u);  // [d2.b0, d3.b0, 0, 0]
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);               // [a.b0, a.b1, b.b0, b.b1]
+}
+
+// Biased nibbles (code + 8) -> two's complement nibbles.
+__device__ __forceinline__ uint32_t unbias(uint32_t packed) { return packed ^ 0x88888888u; }
+
+// ---- per-group E2M1 ----------------------------------------------------------------------
+// The e8m0 scale 2^(code - 127) as an fp32 value (code 0 is the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_to_float(uint32_t code) {
+  return code ? __uint_as_float(code << 23) : __uint_as_float(0x00400000u);
+}
+
+// v_cvt_scalef32_pk_fp4_f32: two values divided by the power-of-two scale, rounded to
+// E2M1 (nearest, ties to even, saturating at 6, sign kept), packed into byte SEL of
+// `old` with the first value in the low nibble.  Bit-identical to e2m1_code(ldexp(v,
+// 127 - code)) for every fp32 input -- checked on the device over all 2^32 patterns.
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2(uint32_t old, float a, float b, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, scale, SEL);
+}
+
+}  // namespace fq

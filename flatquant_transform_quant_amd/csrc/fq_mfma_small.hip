@@ -1,0 +1,305 @@
+// Small-slice MFMA kernel: one wave per slice x_k [M, N] for M in {16, 32, 64, 128},
+// N in {32, 64, 128}, M*N <= 8192, both modes, both dtypes.
+//
+// [FQV2] 拆开算 第1步/第2步 on the matrix cores, fused with 第3步/第4步:
+//   GEMM1  T = x_k . P2   A = x rows (straight from HBM, 16 B per lane),
+//                         B = P2 fragments (LDS), fp32 accumulate, then RNE to the dtype.
+//   GEMM2  y = P1 . T     A = P1 fragments (LDS), B = T taken directly from GEMM1's
+//                         accumulator registers: the contraction index m is relabelled
+//                         so that a lane's two 4-row accumulator blocks are its 8
+//                         k-slots, and P1's columns are stored in the same order.
+//   The epilogue quantizes y from registers; y is never stored.
+// Column labelling: output column c of n-tile nt is the real column R*c + nt (R = N/16),
+// so after the last n-tile every lane holds R consecutive columns of 4 rows -- R/2 code
+// bytes per row, and a 32-group spans 32/R neighbouring lanes.
+// An empty P2 ([0, 0]) is run as P2 = I: T = RNE(x * 1) = x exactly.
+//
+// Workgroups of 4 waves share P1/P2 fragments staged once in LDS in operand order (one
+// 16-byte read per lane, conflict-free); the grid is persistent, each wave walking the
+// slices wave_id, wave_id + total_waves, ...  The next slice's x is requested while the
+// current slice's GEMM2 and epilogue run.
+#include <hip/hip_runtime.h>
+
+#include "fq_mfma_common.h"
+
+namespace fq {
+namespace {
+
+constexpr int kSmallWaves = 4;
+constexpr int kSmallThreads = 64 * kSmallWaves;
+
+template <int DT, int M, int N, bool PG, bool CLAMP>
+__global__ __launch_bounds__(kSmallThreads, 2) void mfma_small_kernel(Problem pb, Buffers b) {
+  constexpr int MT = M / 16, NT = N / 16, R = N / 16;
+  constexpr int KS1 = N / 32;              // GEMM1 k-steps over j
+  constexpr int KS2 = (M + 31) / 32;       // GEMM2 k-steps over m
+  constexpr int MN = M * N;
+  constexpr int SPAN = 32 / R;             // lanes per 32-group (per-group mode)
+  static_assert(N % 32 == 0 && M % 16 == 0 && R >= 2, "unsupported shape");
+
+  __shared__ u32x4_t frag2[KS1 * NT * 64];  // B fragments of P2 (or of I)
+  __shared__ u32x4_t frag1[MT * KS2 * 64];  // A fragments of P1 (k relabelled)
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int c = lane & 15, g = lane >> 4;
+
+  // ---- stage P2 / P1 fragments (once per workgroup) ----
+  const uint16_t one = DT == kBF16 ? uint16_t(0x3F80) : uint16_t(0x3C00);
+  for (int idx = tid; idx < KS1 * NT * 64; idx += kSmallThreads) {
+    const int l = idx & 63, f = idx >> 6, ks = f / NT, nt = f % NT;
+    const int n = R * (l & 15) + nt, j0 = 32 * ks + 8 * (l >> 4);
+    uint32_t w[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      uint16_t v[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int j = j0 + 2 * p + h;
+        v[h] = pb.two_sided ? b.p2[j * N + n] : (j == n ? one : uint16_t(0));
+      }
+      w[p] = uint32_t(v[0]) | (uint32_t(v[1]) << 16);
+    }
+    frag2[idx] = u32x4_t{w[0], w[1], w[2], w[3]};
+  }
+  for (int idx = tid; idx < MT * KS2 * 64; idx += kSmallThreads) {
+    const int l = idx & 63, f = idx >> 6, it = f / KS2, ks2 = f % KS2;
+    const int i = 16 * it + (l & 15), gg = l >> 4;
+    uint32_t w[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      uint16_t v[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int t = 2 * p + h;
+        const int m = 32 * ks2 + (t < 4 ? 4 * gg + t : 16 + 4 * gg + (t - 4));
+        v[h] = m < M ? b.p1[i * M + m] : uint16_t(0);
+      }
+      w[p] = uint32_t(v[0]) | (uint32_t(v[1]) << 16);
+    }
+    frag1[idx] = u32x4_t{w[0], w[1], w[2], w[3]};
+  }
+  __syncthreads();
+
+  const int64_t waves = int64_t(gridDim.x) * kSmallWaves;
+  int64_t s = int64_t(blockIdx.x) * kSmallWaves + (tid >> 6);
+  if (s >= pb.K) return;
+
+  // x operands of one slice: xa[mt][ks] = x[16mt + c, 32ks + 8g .. +7]
+  u32x4_t xa[MT][KS1];
+  auto load_x = [&](int64_t slice) {
+    const uint16_t* xs = b.x + slice * MN;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < KS1; ++ks)
+        xa[mt][ks] = *reinterpret_cast<const u32x4_t*>(xs + (16 * mt + c) * N + 32 * ks + 8 * g);
+  };
+  load_x(s);
+
+  for (; s < pb.K; s += waves) {
+    // Keep the P fragments in LDS: without this the compiler hoists the loop-invariant
+    // fragment reads into registers, which costs occupancy.
+    asm volatile("" ::: "memory");
+    // ---- GEMM1: T = x . P2 (fp32), rounded to the dtype and written straight into the
+    // GEMM2 B operands: bt[ks2][nt] = {T rows 32ks2 + 4g + 0..3, T rows 32ks2 + 16 + 4g + 0..3}
+    // of column R*c + nt (2 x 16 bit per dword).
+    u32x4_t bt[KS2][NT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      // For wide P2 re-read its fragments per row tile rather than holding them all.
+      if constexpr (KS1 * NT > 8) asm volatile("" ::: "memory");
+      f32x4_t acc[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS1; ++ks)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          acc[nt] = mfma16x16x32<DT>(xa[mt][ks], frag2[(ks * NT + nt) * 64 + lane], acc[nt]);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int h = 2 * (mt & 1);
+        bt[mt >> 1][nt][h] = round16x2<DT>(acc[nt][0], acc[nt][1]);
+        bt[mt >> 1][nt][h + 1] = round16x2<DT>(acc[nt][2], acc[nt][3]);
+        if (MT == 1) {  // M = 16: the second half of the k-step is empty
+          bt[0][nt][2] = 0u;
+          bt[0][nt][3] = 0u;
+        }
+      }
+    }
+    // request the next slice's x while this slice finishes
+    const int64_t s_next = s + waves;
+    if (s_next < pb.K) load_x(s_next);
+
+    uint8_t* codes = b.codes + s * (MN / 2);
+    if constexpr (!PG) {
+      // ---- GEMM2: y = P1 . T, all of y (the scale needs max|y| over the slice) ----
+      f32x4_t y[MT][NT];
+#pragma unroll
+      for (int it = 0; it < MT; ++it)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) y[it][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks2 = 0; ks2 < KS2; ++ks2)
+#pragma unroll
+        for (int it = 0; it < MT; ++it) {
+          const u32x4_t a = frag1[(it * KS2 + ks2) * 64 + lane];
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) y[it][nt] = mfma16x16x32<DT>(a, bt[ks2][nt], y[it][nt]);
+        }
+      // [FQV2] 第3步 pertoken: scale = max|y| / (7/clipRatio); code = RNE(y / scale)
+      float amax = 0.0f;
+#pragma unroll
+      for (int it = 0; it < MT; ++it)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) amax = fmaxf(amax, __builtin_fabsf(y[it][nt][i]));
+      amax = wave_max(amax);
+      const float scale = amax / pb.d;
+      const float inv = scale > 0.0f ? 1.0f / scale : 0.0f;
+      if (lane == 0) static_cast<float*>(b.scale)[s] = scale;
+#pragma unroll
+      for (int it = 0; it < MT; ++it)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * it + 4 * g + i;
+          uint32_t by[R / 2];
+#pragma unroll
+          for (int p = 0; p < R / 2; ++p)
+            by[p] = pair_byte(int4_biased<CLAMP>(y[it][2 * p][i], inv),
+                              int4_biased<CLAMP>(y[it][2 * p + 1][i], inv));
+          uint8_t* dst = codes + row * (N / 2) + (R / 2) * c;
+          if constexpr (R == 2) {
+            *dst = static_cast<uint8_t>(by[0] ^ 0x88u);
+          } else if constexpr (R == 4) {
+            *reinterpret_cast<uint16_t*>(dst) =
+                static_cast<uint16_t>(unbias(__builtin_amdgcn_perm(by[1], by[0], 0x0C0C0400u)));
+          } else {
+            *reinterpret_cast<uint32_t*>(dst) = unbias(gather4(by[0], by[1], by[2], by[3]));
+          }
+        }
+    } else {
+      // [FQV2] 第3步 pergroup / 第4步: one e8m0 scale per 32 consecutive elements of a row.
+      // GEMM2 and the encoding run one 16-row tile at a time.
+      uint8_t* e8 = static_cast<uint8_t*>(b.scale) + s * e8m0_bytes_per_slice(MN);
+#pragma unroll
+      for (int it = 0; it < MT; ++it) {
+        f32x4_t y[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) y[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks2 = 0; ks2 < KS2; ++ks2) {
+          const u32x4_t a = frag1[(it * KS2 + ks2) * 64 + lane];
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) y[nt] = mfma16x16x32<DT>(a, bt[ks2][nt], y[nt]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * it + 4 * g + i;
+          float amax = 0.0f;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) amax = fmaxf(amax, __builtin_fabsf(y[nt][i]));
+          amax = group_max<SPAN>(amax);
+          const uint32_t code = e8m0_code(amax, pb.dmax);
+          const float sc = e8m0_to_float(code);
+          uint32_t packed = 0;
+          packed = fp4x2<0>(packed, y[0][i], y[1][i], sc);
+          if constexpr (R >= 4) packed = fp4x2<1>(packed, y[2][i], y[3][i], sc);
+          if constexpr (R >= 8) {
+            packed = fp4x2<2>(packed, y[4][i], y[5][i], sc);
+            packed = fp4x2<3>(packed, y[6][i], y[7][i], sc);
+          }
+          uint8_t* dst = codes + row * (N / 2) + (R / 2) * c;
+          if constexpr (R == 2) {
+            *dst = static_cast<uint8_t>(packed);
+          } else if constexpr (R == 4) {
+            *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(packed);
+          } else {
+            *reinterpret_cast<uint32_t*>(dst) = packed;
+          }
+          if ((c % SPAN) == 0) e8[(row * N + R * c) / 32] = static_cast<uint8_t>(code);
+        }
+      }
+      // (M*N/32 is even for every supported shape, so there is no pad byte)
+    }
+  }
+}
+
+template <int DT, int M, int N, bool PG, bool CLAMP>
+hipError_t launch_one(const Problem& pb, const Buffers& b, hipStream_t s) {
+  static int grid_cap = 0;  // workgroups that fit the device at once (per instantiation)
+  if (grid_cap == 0) {
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_small_kernel<DT, M, N, PG, CLAMP>,
+                                                       kSmallThreads, 0);
+    if (e != hipSuccess) return e;
+    grid_cap = cus * (per_cu > 0 ? per_cu : 1);
+  }
+  const int64_t need = (pb.K + kSmallWaves - 1) / kSmallWaves;
+  const int grid = static_cast<int>(need < grid_cap ? need : grid_cap);
+  mfma_small_kernel<DT, M, N, PG, CLAMP><<<grid, kSmallThreads, 0, s>>>(pb, b);
+  return hipGetLastError();
+}
+
+template <int DT, int M, int N, bool PG>
+hipError_t dispatch_clamp(const Problem& pb, const Buffers& b, hipStream_t s) {
+  if constexpr (PG) {
+    return launch_one<DT, M, N, true, false>(pb, b, s);
+  } else {
+    // The int4 clamp can only bite when (7/clipRatio) * (1 + 4 ulp) reaches 7.5.
+    if (pb.d >= 7.4999f) return launch_one<DT, M, N, false, true>(pb, b, s);
+    return launch_one<DT, M, N, false, false>(pb, b, s);
+  }
+}
+
+template <int DT, int M, int N>
+hipError_t dispatch_mode(const Problem& pb, const Buffers& b, hipStream_t s) {
+  if (pb.mode == kPerGroupFp4) return dispatch_clamp<DT, M, N, true>(pb, b, s);
+  if constexpr (M * N <= 4096) return dispatch_clamp<DT, M, N, false>(pb, b, s);
+  return hipErrorNotSupported;
+}
+
+template <int DT, int M>
+hipError_t dispatch_n(const Problem& pb, const Buffers& b, hipStream_t s) {
+  switch (pb.N) {
+    case 32: return dispatch_mode<DT, M, 32>(pb, b, s);
+    case 64: return dispatch_mode<DT, M, 64>(pb, b, s);
+    case 128:
+      if constexpr (M * 128 <= 8192) return dispatch_mode<DT, M, 128>(pb, b, s);
+      break;
+  }
+  return hipErrorNotSupported;
+}
+
+template <int DT>
+hipError_t dispatch_m(const Problem& pb, const Buffers& b, hipStream_t s) {
+  switch (pb.M) {
+    case 16: return dispatch_n<DT, 16>(pb, b, s);
+    case 32: return dispatch_n<DT, 32>(pb, b, s);
+    case 64: return dispatch_n<DT, 64>(pb, b, s);
+    case 128: return dispatch_n<DT, 128>(pb, b, s);
+  }
+  return hipErrorNotSupported;
+}
+
+}  // namespace
+
+bool mfma_small_supports(const Problem& pb) {
+  const bool m_ok = pb.M == 16 || pb.M == 32 || pb.M == 64 || pb.M == 128;
+  const bool n_ok = pb.N == 32 || pb.N == 64 || pb.N == 128;
+  // registers: the per-token path keeps all of y (M*N/64 fp32 per lane)
+  const int64_t cap = pb.mode == kPerGroupFp4 ? 8192 : 4096;
+  return m_ok && n_ok && pb.M * pb.N <= cap;
+}
+
+hipError_t launch_mfma_small(const Problem& pb, const Buffers& b, hipStream_t s) {
+  if (!mfma_small_supports(pb)) return hipErrorNotSupported;
+  return pb.dtype == kBF16 ? dispatch_m<kBF16>(pb, b, s) : dispatch_m<kF16>(pb, b, s);
+}
+
+}  // namespace fq

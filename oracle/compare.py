@@ -8,7 +8,9 @@ The rule (per element of x[K, M, N]):
     int4 value, or one E2M1 magnitude of the same sign, or the sign of an E2M1 zero when
     the value is within error of 0), and it must lie in the reachable range;
   * such differences may make up at most ceil(1e-4 * elements) of a result;
-  * per-token fp32 scales agree within 1e-5 relative;
+  * per-token fp32 scales agree within 1e-5 relative -- or, for a slice whose largest
+    element is itself moved by a reachable rounding tie of the intermediate, lie inside the
+    oracle's reachable scale interval (counted as "scale_ties");
   * an e8m0 code equals the oracle's, or is the oracle's alternative code when the group's
     max is within error (or 1e-6 relative) of a power-of-two boundary; that group's
     codes are then checked against the oracle's encoding under the alternative code;
@@ -69,9 +71,15 @@ def compare(orc: dict, gpu_packed: np.ndarray, gpu_scale: np.ndarray, max_report
             rel = np.where(os_ == 0, np.where(gs == 0, 0.0, np.inf),
                            np.abs(gs.astype(np.float64) - os_) / np.abs(os_.astype(np.float64)))
         rep["max_scale_rel"] = float(rel.max()) if rel.size else 0.0
-        bad = np.nonzero(rel > SCALE_REL_TOL)[0]
+        tight = rel <= SCALE_REL_TOL
+        in_range = np.zeros_like(tight)
+        if "scale_lo" in orc:
+            in_range = (gs >= orc["scale_lo"]) & (gs <= orc["scale_hi"])
+        rep["scale_ties"] = int((~tight & in_range).sum())
+        bad = np.nonzero(~tight & ~in_range)[0]
         for s in bad[:max_report]:
-            errs.append(f"slice {s}: scale {gs[s]!r} vs oracle {os_[s]!r}")
+            errs.append(f"slice {s}: scale {gs[s]!r} vs oracle {os_[s]!r} "
+                        f"(reachable {orc.get('scale_lo', os_)[s]!r}..{orc.get('scale_hi', os_)[s]!r})")
         if bad.size:
             rep["scale_fail"] = int(bad.size)
     else:

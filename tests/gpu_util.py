@@ -74,5 +74,5 @@ def check(x, p1, p2, dt, mode, clip, dmax, kernel=fq.KERNEL_AUTO, label="", slic
     rep = compare(orc, packed[idx], scale[idx])
     say(f"[gpu]   -> mismatches {rep['mismatch']} (in stated window {rep['mismatch_in_stated_window']}, "
         f"cap {rep['mismatch_cap']}), flagged {rep['flagged']}, alt groups {rep['alt_groups']}, "
-        f"max scale rel {rep['max_scale_rel']:.2e}, ok={rep['ok']}")
+        f"max scale rel {rep['max_scale_rel']:.2e}, scale ties {rep.get('scale_ties', 0)}, ok={rep['ok']}")
     return rep

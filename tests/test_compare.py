@@ -11,9 +11,9 @@ def _repack(codes):
     return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
 
 
-def _pertoken():
+def _pertoken(K=8):
     w = synth.WORKLOADS["c2"]
-    x, p1, p2 = synth.make_inputs(w, 0, 8)
+    x, p1, p2 = synth.make_inputs(w, 0, K)
     return oracle.run(x, p1, p2, w.dtype, w.mode, w.clip_ratio)
 
 
@@ -71,11 +71,35 @@ def test_mismatch_cap():
 
 
 def test_scale_tolerance():
-    r = _pertoken()
+    r = _pertoken(64)
     ok = r["scale"] * np.float32(1 + 5e-6)
     assert compare(r, r["packed"], ok)["ok"]
-    bad = r["scale"] * np.float32(1 + 2e-5)
-    assert not compare(r, r["packed"], bad)["ok"]
+    # beyond 1e-5 and beyond the reachable interval: rejected
+    lo, hi = r["scale_lo"].astype(np.float64), r["scale_hi"].astype(np.float64)
+    out = np.maximum(hi * (1 + 1e-6), r["scale"] * (1 + 2e-5)).astype(np.float32)
+    rep = compare(r, r["packed"], out)
+    assert not rep["ok"] and rep.get("scale_fail") == r["S"]
+    # beyond 1e-5 but inside the reachable interval of a slice whose intermediate rounding
+    # is ambiguous: accepted and counted
+    sc = r["scale"].astype(np.float64)
+    dev = np.maximum(hi - sc, sc - lo) / sc
+    s = int(np.argmax(dev))
+    assert dev[s] > 1.5e-5
+    g = r["scale"].copy()
+    g[s] = np.float32(hi[s] if hi[s] - sc[s] >= sc[s] - lo[s] else lo[s])
+    rep = compare(r, r["packed"], g)
+    assert rep["ok"] and rep["scale_ties"] == 1
+
+
+def test_scale_interval_is_tight_without_intermediate_ties():
+    """With P2 = I the intermediate is exact: the reachable scale interval is then set by
+    the fp32 summation bound of the second product alone and stays within 1e-5."""
+    w = synth.WORKLOADS["c2"]
+    x, p1, _ = synth.make_inputs(w, 0, 8)
+    eye = synth.round_to(np.eye(w.N), "bf16")
+    r = oracle.run(x, p1, eye, w.dtype, w.mode, w.clip_ratio)
+    width = (r["scale_hi"].astype(np.float64) - r["scale_lo"]) / r["scale"]
+    assert width.max() < 2e-5
 
 
 def test_e8m0_change_and_pad():
