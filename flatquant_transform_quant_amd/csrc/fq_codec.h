@@ -35,10 +35,18 @@ __device__ __forceinline__ uint16_t round16(float v) {
   }
 }
 
-// Two fp32 values -> two dtype values packed in one dword (low half = a).
+// Two fp32 values -> two dtype values packed in one dword (low half = a), one
+// v_cvt_pk_{bf16,f16}_f32 (round to nearest even).
 template <int DT>
 __device__ __forceinline__ uint32_t round16x2(float a, float b) {
-  return static_cast<uint32_t>(round16<DT>(a)) | (static_cast<uint32_t>(round16<DT>(b)) << 16);
+  typedef __attribute__((ext_vector_type(2))) float f32x2;
+  if constexpr (DT == kBF16) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 b16x2;
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, b16x2));
+  } else {
+    typedef __attribute__((ext_vector_type(2))) _Float16 h16x2;
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, h16x2));
+  }
 }
 
 // int4 code of q = y / scale: round half to even, clamp to [-8, 7]; returns the 4-bit

@@ -100,12 +100,13 @@ bool live(const fq_executor* e) {
   return g_live.count(e) != 0 && e->magic == kLiveMagic;
 }
 
-// The MFMA kernels load x 16 bytes at a time and store codes and scales up to 4 bytes
-// at a time; staged tensors live in the (256-byte aligned) workspace.
+// The MFMA kernels load x, P1 and P2 16 bytes at a time and store codes and scales up
+// to 4 bytes at a time; staged tensors live in the (256-byte aligned) workspace.
 bool vector_aligned(const fq_executor* e) {
   auto al = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; };
-  return (e->stage_x || al(e->x.data, 16)) && (e->stage_out || al(e->out.data, 4)) &&
-         (e->stage_scale || al(e->scale.data, 4));
+  return (e->stage_x || al(e->x.data, 16)) && (e->stage_p1 || al(e->p1.data, 16)) &&
+         (!e->pb.two_sided || e->stage_p2 || al(e->p2.data, 16)) &&
+         (e->stage_out || al(e->out.data, 4)) && (e->stage_scale || al(e->scale.data, 4));
 }
 
 bool kernel_supports(int32_t k, const fq_executor* e) {

@@ -28,6 +28,13 @@ namespace {
 constexpr int kSmallWaves = 4;
 constexpr int kSmallThreads = 64 * kSmallWaves;
 
+// Slices of x kept in flight per wave: two for small slices (the next two slices are
+// requested before the current one's products start), one where registers are short.
+template <int M, int N, bool PG>
+constexpr int prefetch_depth() {
+  return (M * N <= 4096) ? 2 : 1;
+}
+
 template <int DT, int M, int N, bool PG, bool CLAMP>
 __global__ __launch_bounds__(kSmallThreads, 2) void mfma_small_kernel(Problem pb, Buffers b) {
   constexpr int MT = M / 16, NT = N / 16, R = N / 16;
@@ -39,65 +46,141 @@ __global__ __launch_bounds__(kSmallThreads, 2) void mfma_small_kernel(Problem pb
 
   __shared__ u32x4_t frag2[KS1 * NT * 64];  // B fragments of P2 (or of I)
   __shared__ u32x4_t frag1[MT * KS2 * 64];  // A fragments of P1 (k relabelled)
+  // per-wave staging of one slice's output: codes (M*N/2 bytes), then e8m0 bytes
+  constexpr int CODE_BYTES = MN / 2;
+  constexpr int E8_BYTES = PG ? MN / 32 : 0;
+  constexpr int STAGE_BYTES = (CODE_BYTES + E8_BYTES + 15) / 16 * 16;
+  __shared__ u32x4_t stage[kSmallWaves][STAGE_BYTES / 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int c = lane & 15, g = lane >> 4;
 
-  // ---- stage P2 / P1 fragments (once per workgroup) ----
-  const uint16_t one = DT == kBF16 ? uint16_t(0x3F80) : uint16_t(0x3C00);
-  for (int idx = tid; idx < KS1 * NT * 64; idx += kSmallThreads) {
-    const int l = idx & 63, f = idx >> 6, ks = f / NT, nt = f % NT;
-    const int n = R * (l & 15) + nt, j0 = 32 * ks + 8 * (l >> 4);
-    uint32_t w[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      uint16_t v[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int j = j0 + 2 * p + h;
-        v[h] = pb.two_sided ? b.p2[j * N + n] : (j == n ? one : uint16_t(0));
-      }
-      w[p] = uint32_t(v[0]) | (uint32_t(v[1]) << 16);
-    }
-    frag2[idx] = u32x4_t{w[0], w[1], w[2], w[3]};
-  }
-  for (int idx = tid; idx < MT * KS2 * 64; idx += kSmallThreads) {
-    const int l = idx & 63, f = idx >> 6, it = f / KS2, ks2 = f % KS2;
-    const int i = 16 * it + (l & 15), gg = l >> 4;
-    uint32_t w[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      uint16_t v[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int t = 2 * p + h;
-        const int m = 32 * ks2 + (t < 4 ? 4 * gg + t : 16 + 4 * gg + (t - 4));
-        v[h] = m < M ? b.p1[i * M + m] : uint16_t(0);
-      }
-      w[p] = uint32_t(v[0]) | (uint32_t(v[1]) << 16);
-    }
-    frag1[idx] = u32x4_t{w[0], w[1], w[2], w[3]};
-  }
-  __syncthreads();
-
   const int64_t waves = int64_t(gridDim.x) * kSmallWaves;
-  int64_t s = int64_t(blockIdx.x) * kSmallWaves + (tid >> 6);
-  if (s >= pb.K) return;
+  // the slice index is wave-uniform: keep it (and every base pointer) in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int64_t s = int64_t(blockIdx.x) * kSmallWaves + wave;
 
-  // x operands of one slice: xa[mt][ks] = x[16mt + c, 32ks + 8g .. +7]
-  u32x4_t xa[MT][KS1];
-  auto load_x = [&](int64_t slice) {
+  // x operands of a slice: xa[buf][mt][ks] = x[16mt + c, 32ks + 8g .. +7]
+  constexpr int PF = prefetch_depth<M, N, PG>();
+  u32x4_t xa[PF][MT][KS1];
+  auto load_x = [&](int buf, int64_t slice) {
     const uint16_t* xs = b.x + slice * MN;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int ks = 0; ks < KS1; ++ks)
-        xa[mt][ks] = *reinterpret_cast<const u32x4_t*>(xs + (16 * mt + c) * N + 32 * ks + 8 * g);
+        xa[buf][mt][ks] = *reinterpret_cast<const u32x4_t*>(xs + (16 * mt + c) * N + 32 * ks + 8 * g);
   };
-  load_x(s);
+  // With two slices in flight the first loads are issued before the P staging, so the
+  // two memory latencies overlap; with one (large slices) registers are too short.
+  if constexpr (PF == 2) {
+#pragma unroll
+    for (int q = 0; q < PF; ++q)
+      if (s + q * waves < pb.K) load_x(q, s + q * waves);
+  }
 
-  for (; s < pb.K; s += waves) {
+  // ---- stage P2 / P1 fragments (once per workgroup) ----
+  // All coalesced 16-byte loads of P1 and P2 are issued first (one memory latency), then
+  // each 2-byte value is written to its fragment slot:
+  //   P2[j, n]  -> frag2[(ks*NT + nt)*64 + 16*g + c], element t   (j = 32ks + 8g + t, n = R*c + nt)
+  //   P1[i, m]  -> frag1[(it*KS2 + ks2)*64 + 16*g + i%16], element t, where m = 32ks2 + w and
+  //                w = 4g + t (t < 4) or 16 + 4g + (t - 4) (t >= 4)
+  {
+    constexpr int C2 = N * N / 8, C1 = M * M / 8;  // 16-byte chunks of P2 and P1
+    constexpr int L2 = (C2 + kSmallThreads - 1) / kSmallThreads;
+    constexpr int L1 = (C1 + kSmallThreads - 1) / kSmallThreads;
+    u32x4_t r2[L2], r1[L1];
+    const bool two = pb.two_sided != 0;
+#pragma unroll
+    for (int q = 0; q < L2; ++q) {
+      const int ch = tid + q * kSmallThreads;
+      if (two && ch < C2) r2[q] = reinterpret_cast<const u32x4_t*>(b.p2)[ch];
+    }
+#pragma unroll
+    for (int q = 0; q < L1; ++q) {
+      const int ch = tid + q * kSmallThreads;
+      if (ch < C1) r1[q] = reinterpret_cast<const u32x4_t*>(b.p1)[ch];
+    }
+    uint16_t* f2 = reinterpret_cast<uint16_t*>(frag2);
+    uint16_t* f1 = reinterpret_cast<uint16_t*>(frag1);
+    if (two) {
+#pragma unroll
+      for (int q = 0; q < L2; ++q) {
+        const int ch = tid + q * kSmallThreads;
+        if (ch < C2) {
+          const int j = ch / (N / 8), n0 = (ch % (N / 8)) * 8;
+          const int ks = j >> 5, gg = (j >> 3) & 3, t = j & 7;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int n = n0 + e, cc = n / R, nt = n % R;
+            f2[((ks * NT + nt) * 64 + 16 * gg + cc) * 8 + t] =
+                static_cast<uint16_t>(r2[q][e >> 1] >> (16 * (e & 1)));
+          }
+        }
+      }
+    } else {
+      // an empty P2 is run as the identity
+      const uint16_t one = DT == kBF16 ? uint16_t(0x3F80) : uint16_t(0x3C00);
+      for (int idx = tid; idx < KS1 * NT * 64; idx += kSmallThreads) {
+        const int l = idx & 63, f = idx >> 6, ks = f / NT, nt = f % NT;
+        const int n = R * (l & 15) + nt, j0 = 32 * ks + 8 * (l >> 4);
+        uint32_t w[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          w[p] = uint32_t(j0 + 2 * p == n ? one : 0) | (uint32_t(j0 + 2 * p + 1 == n ? one : 0) << 16);
+        frag2[idx] = u32x4_t{w[0], w[1], w[2], w[3]};
+      }
+    }
+    // P1 columns beyond M (M = 16: the second half of the k-step) hold zeros
+    if (M < 32)
+      for (int idx = tid; idx < MT * KS2 * 64; idx += kSmallThreads) frag1[idx] = u32x4_t{0u, 0u, 0u, 0u};
+    if (M < 32) __syncthreads();
+#pragma unroll
+    for (int q = 0; q < L1; ++q) {
+      const int ch = tid + q * kSmallThreads;
+      if (ch < C1) {
+        const int i = ch / (M / 8), m0 = (ch % (M / 8)) * 8;
+        const int it = i >> 4, r = i & 15;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int m = m0 + e, ks2 = m >> 5, w = m & 31;
+          const int gg = w < 16 ? (w >> 2) : ((w - 16) >> 2);
+          const int t = w < 16 ? (w & 3) : 4 + ((w - 16) & 3);
+          f1[((it * KS2 + ks2) * 64 + 16 * gg + r) * 8 + t] =
+              static_cast<uint16_t>(r1[q][e >> 1] >> (16 * (e & 1)));
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (s >= pb.K) return;
+  if constexpr (PF == 1) load_x(0, s);
+
+  uint8_t* const st = reinterpret_cast<uint8_t*>(stage[wave]);
+  // write the staged output of slice `slice` with 16-byte stores
+  auto flush = [&](int64_t slice) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    u32x4_t* gcodes = reinterpret_cast<u32x4_t*>(b.codes + slice * CODE_BYTES);
+#pragma unroll
+    for (int q = 0; q < CODE_BYTES / 16 / 64; ++q) gcodes[q * 64 + lane] = stage[wave][q * 64 + lane];
+    if constexpr ((CODE_BYTES / 16) % 64 != 0) {
+      constexpr int q = CODE_BYTES / 16 / 64;
+      if (q * 64 + lane < CODE_BYTES / 16) gcodes[q * 64 + lane] = stage[wave][q * 64 + lane];
+    }
+    if constexpr (PG) {
+      const uint32_t* se = reinterpret_cast<const uint32_t*>(st + CODE_BYTES);
+      uint32_t* ge = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(b.scale) +
+                                                 slice * e8m0_bytes_per_slice(MN));
+      for (int q = lane; q < E8_BYTES / 4; q += 64) ge[q] = se[q];
+    }
+    // the staging buffer is reused by the next slice
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  auto process = [&](const int buf, const int64_t s) {
     // Keep the P fragments in LDS: without this the compiler hoists the loop-invariant
     // fragment reads into registers, which costs occupancy.
     asm volatile("" ::: "memory");
@@ -107,16 +190,17 @@ __global__ __launch_bounds__(kSmallThreads, 2) void mfma_small_kernel(Problem pb
     u32x4_t bt[KS2][NT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      // For wide P2 re-read its fragments per row tile rather than holding them all.
-      if constexpr (KS1 * NT > 8) asm volatile("" ::: "memory");
       f32x4_t acc[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS1; ++ks)
+      for (int ks = 0; ks < KS1; ++ks) {
+        // bound the fragment reads in flight to one k-step (register pressure)
+        if constexpr (KS1 * NT > 8) asm volatile("" ::: "memory");
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
-          acc[nt] = mfma16x16x32<DT>(xa[mt][ks], frag2[(ks * NT + nt) * 64 + lane], acc[nt]);
+          acc[nt] = mfma16x16x32<DT>(xa[buf][mt][ks], frag2[(ks * NT + nt) * 64 + lane], acc[nt]);
+      }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int h = 2 * (mt & 1);
@@ -128,11 +212,10 @@ __global__ __launch_bounds__(kSmallThreads, 2) void mfma_small_kernel(Problem pb
         }
       }
     }
-    // request the next slice's x while this slice finishes
-    const int64_t s_next = s + waves;
-    if (s_next < pb.K) load_x(s_next);
+    // this buffer is free again: request the slice PF steps ahead
+    const int64_t s_next = s + PF * waves;
+    if (s_next < pb.K) load_x(buf, s_next);
 
-    uint8_t* codes = b.codes + s * (MN / 2);
     if constexpr (!PG) {
       // ---- GEMM2: y = P1 . T, all of y (the scale needs max|y| over the slice) ----
       f32x4_t y[MT][NT];
@@ -170,7 +253,7 @@ __global__ __launch_bounds__(kSmallThreads, 2) void mfma_small_kernel(Problem pb
           for (int p = 0; p < R / 2; ++p)
             by[p] = pair_byte(int4_biased<CLAMP>(y[it][2 * p][i], inv),
                               int4_biased<CLAMP>(y[it][2 * p + 1][i], inv));
-          uint8_t* dst = codes + row * (N / 2) + (R / 2) * c;
+          uint8_t* dst = st + row * (N / 2) + (R / 2) * c;
           if constexpr (R == 2) {
             *dst = static_cast<uint8_t>(by[0] ^ 0x88u);
           } else if constexpr (R == 4) {
@@ -183,9 +266,9 @@ __global__ __launch_bounds__(kSmallThreads, 2) void mfma_small_kernel(Problem pb
     } else {
       // [FQV2] 第3步 pergroup / 第4步: one e8m0 scale per 32 consecutive elements of a row.
       // GEMM2 and the encoding run one 16-row tile at a time.
-      uint8_t* e8 = static_cast<uint8_t*>(b.scale) + s * e8m0_bytes_per_slice(MN);
 #pragma unroll
       for (int it = 0; it < MT; ++it) {
+        if constexpr (MT * NT > 16) asm volatile("" ::: "memory");  // one row tile live at a time
         f32x4_t y[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) y[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -211,7 +294,7 @@ __global__ __launch_bounds__(kSmallThreads, 2) void mfma_small_kernel(Problem pb
             packed = fp4x2<2>(packed, y[4][i], y[5][i], sc);
             packed = fp4x2<3>(packed, y[6][i], y[7][i], sc);
           }
-          uint8_t* dst = codes + row * (N / 2) + (R / 2) * c;
+          uint8_t* dst = st + row * (N / 2) + (R / 2) * c;
           if constexpr (R == 2) {
             *dst = static_cast<uint8_t>(packed);
           } else if constexpr (R == 4) {
@@ -219,10 +302,19 @@ __global__ __launch_bounds__(kSmallThreads, 2) void mfma_small_kernel(Problem pb
           } else {
             *reinterpret_cast<uint32_t*>(dst) = packed;
           }
-          if ((c % SPAN) == 0) e8[(row * N + R * c) / 32] = static_cast<uint8_t>(code);
+          if ((c % SPAN) == 0) st[CODE_BYTES + (row * N + R * c) / 32] = static_cast<uint8_t>(code);
         }
       }
       // (M*N/32 is even for every supported shape, so there is no pad byte)
+    }
+    flush(s);
+  };
+
+  for (; s < pb.K; s += PF * waves) {
+    process(0, s);
+    if constexpr (PF == 2) {
+      if (s + waves >= pb.K) break;
+      process(1, s + waves);
     }
   }
 }

@@ -1,6 +1,225 @@
-// Whole-workgroup MFMA kernel for 256-class slices (placeholder until implemented).
-#include "fq_internal.h"
+// Whole-workgroup MFMA kernel for 256 x 256 slices with both transforms.
+//
+// [FQV2] 拆开算 第1步/第2步 fused with 第3步/第4步 for M = N = 256.  One workgroup of 4
+// waves (one per SIMD, 512 registers each) owns one slice at a time (persistent grid,
+// one workgroup per CU):
+//   * P1 is staged once in LDS as GEMM2 A fragments (128 KB), with the contraction index
+//     relabelled to match GEMM1's accumulator layout;
+//   * wave w owns the 64 output columns 64w .. 64w+63 and keeps its strip of P2 as GEMM1
+//     B fragments in registers (column label c of n-tile nt is column 64w + 4c + nt, so a
+//     lane holds 4 neighbouring columns);
+//   * x streams through LDS in chunks of 32 rows (16 KB, XOR-swizzled 16-byte slots so the
+//     A-fragment reads are conflict-free), the next chunk prefetched into registers;
+//   * per chunk c: T_c = x[32c..32c+31, :] . P2[:, strip] (GEMM1, 64 MFMAs), rounded to
+//     the dtype in registers, then y[:, strip] += P1[:, 32c..32c+31] . T_c (GEMM2, 64
+//     MFMAs) -- the full intermediate T never exists;
+//   * y (256 x 64 per wave, fp32) stays in registers; per token, max|y| is reduced across
+//     the 4 waves through LDS; per group, a 32-group is 8 neighbouring lanes of one row.
+#include <hip/hip_runtime.h>
+
+#include "fq_mfma_common.h"
+
 namespace fq {
-bool mfma_wide_supports(const Problem&) { return false; }
-hipError_t launch_mfma_wide(const Problem&, const Buffers&, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+constexpr int kWideWaves = 4;
+constexpr int kNT = 4;        // n-tiles per wave (64 columns)
+constexpr int kWideThreads = 64 * kWideWaves;
+constexpr int kW = 256;       // M = N
+constexpr int kChunk = 32;    // rows of x per chunk
+constexpr int kNChunk = kW / kChunk;
+constexpr int kIT = kW / 16;  // 16-row tiles of y
+
+template <int DT, bool PG, bool CLAMP>
+__global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb, Buffers b) {
+  __shared__ u32x4_t frag1[kIT * kNChunk * 64];   // 128 KB: P1 A fragments
+  __shared__ u32x4_t xs[kChunk * 32];             // 16 KB: one x chunk, 32 slots of 16 B per row
+  __shared__ float red[kWideWaves];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane & 15, g = lane >> 4;
+
+  // ---- P1 -> LDS fragments: P1[i, m] -> frag1[(it*8 + ch)*64 + 16*gg + i%16] element t,
+  // m = 32ch + (t < 4 ? 4gg + t : 16 + 4gg + t - 4) ----
+  {
+    uint16_t* f1 = reinterpret_cast<uint16_t*>(frag1);
+    for (int base = 0; base < kW * kW / 8; base += kWideThreads * 4) {
+      u32x4_t r[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) r[q] = reinterpret_cast<const u32x4_t*>(b.p1)[base + q * kWideThreads + tid];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int ch16 = base + q * kWideThreads + tid;
+        const int i = ch16 >> 5, m0 = (ch16 & 31) * 8;
+        const int it = i >> 4, rr = i & 15;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int m = m0 + e, ch = m >> 5, wv = m & 31;
+          const int gg = wv < 16 ? (wv >> 2) : ((wv - 16) >> 2);
+          const int t = wv < 16 ? (wv & 3) : 4 + ((wv - 16) & 3);
+          f1[((it * kNChunk + ch) * 64 + 16 * gg + rr) * 8 + t] =
+              static_cast<uint16_t>(r[q][e >> 1] >> (16 * (e & 1)));
+        }
+      }
+    }
+  }
+  // ---- this wave's P2 strip as GEMM1 B fragments: p2f[ks][nt] element t =
+  // P2[32ks + 8g + t, 64w + 4c + nt] ----
+  u32x4_t p2f[kW / 32][kNT];
+#pragma unroll
+  for (int ks = 0; ks < kW / 32; ++ks)
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+      const uint16_t* col = b.p2 + (32 * ks + 8 * g) * kW + 64 * w + 4 * c + nt;
+      uint32_t v[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) v[p] = uint32_t(col[(2 * p) * kW]) | (uint32_t(col[(2 * p + 1) * kW]) << 16);
+      p2f[ks][nt] = u32x4_t{v[0], v[1], v[2], v[3]};
+    }
+
+  // x chunk prefetch: thread t moves 16-byte slots t + 256h, h = 0..3, of the chunk
+  constexpr int XR = kChunk * kW * 2 / 16 / kWideThreads;
+  u32x4_t xr[XR];
+  auto load_chunk = [&](int64_t slice, int ch) {
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(b.x + slice * (kW * kW) + ch * (kChunk * kW));
+#pragma unroll
+    for (int h = 0; h < XR; ++h) xr[h] = src[tid + h * kWideThreads];
+  };
+  auto store_chunk = [&]() {
+#pragma unroll
+    for (int h = 0; h < XR; ++h) {
+      const int gi = tid + h * kWideThreads, row = gi >> 5, q = gi & 31;
+      xs[row * 32 + (q ^ row)] = xr[h];
+    }
+  };
+
+  int64_t s = blockIdx.x;
+  if (s < pb.K) load_chunk(s, 0);
+  for (; s < pb.K; s += gridDim.x) {
+    f32x4_t y[kIT][kNT];
+#pragma unroll
+    for (int it = 0; it < kIT; ++it)
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) y[it][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (int ch = 0; ch < kNChunk; ++ch) {
+      __syncthreads();  // every wave is done with the previous chunk (and with `red`)
+      store_chunk();
+      __syncthreads();  // the chunk is in LDS
+      if (ch + 1 < kNChunk)
+        load_chunk(s, ch + 1);
+      else if (s + gridDim.x < pb.K)
+        load_chunk(s + gridDim.x, 0);
+
+      // GEMM1: T rows 32ch + 16h + (4g .. 4g+3), h = 0, 1, of the wave's columns
+      f32x4_t acc[2][kNT];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) acc[h][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const int row = 16 * h + c;
+#pragma unroll
+        for (int ks = 0; ks < kW / 32; ++ks) {
+          const u32x4_t a = xs[row * 32 + ((4 * ks + g) ^ row)];
+#pragma unroll
+          for (int nt = 0; nt < kNT; ++nt) acc[h][nt] = mfma16x16x32<DT>(a, p2f[ks][nt], acc[h][nt]);
+        }
+      }
+      u32x4_t tb[kNT];
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt)
+        tb[nt] = u32x4_t{round16x2<DT>(acc[0][nt][0], acc[0][nt][1]), round16x2<DT>(acc[0][nt][2], acc[0][nt][3]),
+                         round16x2<DT>(acc[1][nt][0], acc[1][nt][1]), round16x2<DT>(acc[1][nt][2], acc[1][nt][3])};
+      // GEMM2: y += P1[:, chunk] . T_chunk
+#pragma unroll
+      for (int it = 0; it < kIT; ++it) {
+        const u32x4_t a = frag1[(it * kNChunk + ch) * 64 + lane];
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) y[it][nt] = mfma16x16x32<DT>(a, tb[nt], y[it][nt]);
+      }
+    }
+
+    uint8_t* codes = b.codes + s * (kW * kW / 2);
+    if constexpr (!PG) {
+      // [FQV2] 第3步 pertoken: max|y| over the slice (4 waves), scale, codes
+      float amax = 0.0f;
+#pragma unroll
+      for (int it = 0; it < kIT; ++it)
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) amax = fmaxf(amax, __builtin_fabsf(y[it][nt][i]));
+      amax = wave_max(amax);
+      if (lane == 0) red[w] = amax;
+      __syncthreads();
+      amax = red[0];
+#pragma unroll
+      for (int q = 1; q < kWideWaves; ++q) amax = fmaxf(amax, red[q]);
+      const float scale = amax / pb.d;
+      const float inv = scale > 0.0f ? 1.0f / scale : 0.0f;
+      if (tid == 0) static_cast<float*>(b.scale)[s] = scale;
+#pragma unroll
+      for (int it = 0; it < kIT; ++it)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * it + 4 * g + i;
+          const uint32_t b0 = pair_byte(int4_biased<CLAMP>(y[it][0][i], inv), int4_biased<CLAMP>(y[it][1][i], inv));
+          const uint32_t b1 = pair_byte(int4_biased<CLAMP>(y[it][2][i], inv), int4_biased<CLAMP>(y[it][3][i], inv));
+          *reinterpret_cast<uint16_t*>(codes + row * (kW / 2) + 32 * w + 2 * c) =
+              static_cast<uint16_t>(unbias(__builtin_amdgcn_perm(b1, b0, 0x0C0C0400u)));
+        }
+    } else {
+      // [FQV2] 第3步 pergroup / 第4步: a 32-group is 8 neighbouring lanes of one row
+      uint8_t* e8 = static_cast<uint8_t*>(b.scale) + s * e8m0_bytes_per_slice(kW * kW);
+#pragma unroll
+      for (int it = 0; it < kIT; ++it)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * it + 4 * g + i;
+          float amax = fmaxf(fmaxf(__builtin_fabsf(y[it][0][i]), __builtin_fabsf(y[it][1][i])),
+                             fmaxf(__builtin_fabsf(y[it][2][i]), __builtin_fabsf(y[it][3][i])));
+          amax = group_max<8>(amax);
+          const uint32_t code = e8m0_code(amax, pb.dmax);
+          const float sc = e8m0_to_float(code);
+          uint32_t packed = fp4x2<0>(0u, y[it][0][i], y[it][1][i], sc);
+          packed = fp4x2<1>(packed, y[it][2][i], y[it][3][i], sc);
+          *reinterpret_cast<uint16_t*>(codes + row * (kW / 2) + 32 * w + 2 * c) = static_cast<uint16_t>(packed);
+          if ((c & 7) == 0) e8[row * (kW / 32) + 2 * w + (c >> 3)] = static_cast<uint8_t>(code);
+        }
+    }
+  }
+}
+
+template <int DT, bool PG, bool CLAMP>
+hipError_t launch_w2(const Problem& pb, const Buffers& b, hipStream_t s) {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+  }
+  const int grid = static_cast<int>(pb.K < cus ? pb.K : cus);
+  mfma_wide2_kernel<DT, PG, CLAMP><<<grid, kWideThreads, 0, s>>>(pb, b);
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t dispatch_w2(const Problem& pb, const Buffers& b, hipStream_t s) {
+  if (pb.mode == kPerGroupFp4) return launch_w2<DT, true, false>(pb, b, s);
+  if (pb.d >= 7.4999f) return launch_w2<DT, false, true>(pb, b, s);
+  return launch_w2<DT, false, false>(pb, b, s);
+}
+
+}  // namespace
+
+bool mfma_wide_supports(const Problem& pb) { return pb.M == kW && pb.N == kW && pb.two_sided; }
+
+hipError_t launch_mfma_wide(const Problem& pb, const Buffers& b, hipStream_t s) {
+  if (!mfma_wide_supports(pb)) return hipErrorNotSupported;
+  return pb.dtype == kBF16 ? dispatch_w2<kBF16>(pb, b, s) : dispatch_w2<kF16>(pb, b, s);
+}
+
 }  // namespace fq
