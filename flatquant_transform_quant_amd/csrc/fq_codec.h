@@ -84,6 +84,16 @@ __device__ __forceinline__ uint32_t e8m0_code(float amax, float dmax) {
   return E;
 }
 
+// As e8m0_code, with dinv = 1/dmax when dmax is a power of two (0 otherwise): then
+// amax * dinv is exactly the IEEE quotient amax / dmax and the division is skipped.
+__device__ __forceinline__ uint32_t e8m0_code_fast(float amax, float dmax, float dinv) {
+  if (dmax == 0.0f || dinv == 0.0f) return e8m0_code(amax, dmax);
+  const uint32_t s = __float_as_uint(amax * dinv);
+  uint32_t E = (s >> 23) & 0xFFu;
+  if (E >= 1u && E < 254u && (s & 0x7FFFFFu) != 0u) E += 1u;
+  return E;
+}
+
 // y * 2^(127 - code): exact (v_ldexp), the reciprocal of the e8m0 scale.
 __device__ __forceinline__ float apply_e8m0(float y, uint32_t code) {
   return __builtin_amdgcn_ldexpf(y, 127 - static_cast<int>(code));

@@ -200,6 +200,11 @@ fq_status fq_get_workspace_size(const fq_tensor* x, const fq_tensor* kroneckerP1
   e->pb.two_sided = p2_empty ? 0 : 1;
   e->pb.d = static_cast<float>(7.0 / clipRatio);
   e->pb.dmax = static_cast<float>(dstTypeMax);
+  {
+    int ex = 0;
+    const double mant = std::frexp(dstTypeMax, &ex);
+    e->pb.dmax_inv = (dstTypeMax > 0.0 && mant == 0.5) ? static_cast<float>(1.0 / dstTypeMax) : 0.0f;
+  }
   e->repeatable = 0;
   e->x = *x;
   e->p1 = *kroneckerP1;

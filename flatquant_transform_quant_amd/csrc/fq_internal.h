@@ -19,6 +19,7 @@ struct Problem {
   int32_t two_sided;  // 0: P2 is [0, 0], the right multiply is skipped
   float d;            // fl32(7 / clipRatio), the per-token divisor
   float dmax;         // fl32(dstTypeMax); 0 selects V1
+  float dmax_inv;     // 1/dmax when dmax is a power of two (then exact), else 0
 };
 
 // Device buffers of one launch, in the packed contiguous layouts:

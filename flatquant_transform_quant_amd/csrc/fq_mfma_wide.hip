@@ -1,4 +1,4 @@
-// Whole-workgroup MFMA kernel for 256 x 256 slices with both transforms.
+// Whole-workgroup MFMA kernels for 256 x 256 slices: both transforms, or P1 only.
 //
 // [FQV2] 拆开算 第1步/第2步 fused with 第3步/第4步 for M = N = 256.  One workgroup of 4
 // waves (one per SIMD, 512 registers each) owns one slice at a time (persistent grid,
@@ -192,6 +192,131 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb,
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Left-only 256 x 256 slices (P2 = [0, 0], per-group mode): y = P1 . x.
+//   * P1 is staged once in LDS as A fragments in natural k order (128 KB);
+//   * x streams through two 16 KB LDS buffers of 32 rows (one chunk is consumed while the
+//     next is written), the chunk after that prefetched into registers;
+//   * wave w computes rows 128*(w&1) .. +127 of columns 128*(w>>1) .. +127.  x is the B
+//     operand with the contraction over rows, so each lane reads 8 rows x 16 bytes
+//     (8 neighbouring columns) and transposes them in registers (v_perm_b32); MFMA u of a
+//     k-step then takes column 8c + u of the lane's block, so after the 8 MFMAs a lane
+//     holds 8 neighbouring columns of 4 rows: one 4-byte E2M1 run per row, and a 32-group
+//     spans 4 neighbouring lanes.
+template <int DT>
+__global__ __launch_bounds__(kWideThreads, 1) void mfma_wide1_kernel(Problem pb, Buffers b) {
+  __shared__ u32x4_t frag1[kIT * kNChunk * 64];  // 128 KB: P1 A fragments (natural k order)
+  __shared__ u32x4_t xs[2][kChunk * 32];         // 2 x 16 KB: x chunks, row-major 16-byte slots
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane & 15, g = lane >> 4;
+  const int rh = w & 1, sc = w >> 1;  // row half, column half
+
+  // P1[i, 32ch + 8gg .. +7] -> frag1[(it*8 + ch)*64 + 16*gg + i%16]
+  for (int q = tid; q < kW * kW / 8; q += kWideThreads) {
+    const int i = q >> 5, m0 = (q & 31) * 8;
+    const int it = i >> 4, ch = m0 >> 5, gg = (m0 & 31) >> 3;
+    frag1[(it * kNChunk + ch) * 64 + 16 * gg + (i & 15)] = reinterpret_cast<const u32x4_t*>(b.p1)[q];
+  }
+
+  constexpr int XR = kChunk * kW * 2 / 16 / kWideThreads;
+  u32x4_t xr[XR];
+  // global chunk index gc = slice_round * 8 + ch, slice = blockIdx.x + round * gridDim.x
+  auto load_chunk = [&](int64_t slice, int ch) {
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(b.x + slice * (kW * kW) + ch * (kChunk * kW));
+#pragma unroll
+    for (int h = 0; h < XR; ++h) xr[h] = src[tid + h * kWideThreads];
+  };
+  auto store_chunk = [&](int buf) {
+#pragma unroll
+    for (int h = 0; h < XR; ++h) xs[buf][tid + h * kWideThreads] = xr[h];
+  };
+
+  int64_t s = blockIdx.x;
+  if (s >= pb.K) return;
+  load_chunk(s, 0);
+  store_chunk(0);
+  if (kNChunk > 1) load_chunk(s, 1);
+  int buf = 0;
+  const float dinv = pb.dmax_inv;
+  for (; s < pb.K; s += gridDim.x) {
+    f32x4_t y[kIT / 2][8];
+#pragma unroll
+    for (int it = 0; it < kIT / 2; ++it)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) y[it][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (int ch = 0; ch < kNChunk; ++ch) {
+      __syncthreads();  // chunk ch is in xs[buf]; every wave is done with xs[buf ^ 1]
+      // the chunk after this one: regs -> the free buffer; then prefetch the one after
+      const bool more = ch + 1 < kNChunk || s + gridDim.x < pb.K;
+      if (more) store_chunk(buf ^ 1);
+      if (ch + 2 < kNChunk)
+        load_chunk(s, ch + 2);
+      else if (s + gridDim.x < pb.K)
+        load_chunk(s + gridDim.x, ch + 2 - kNChunk);
+
+      // B operands: rows 8g .. 8g+7 of the chunk, columns 128sc + 8c .. +7, transposed
+      u32x4_t rows[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) rows[t] = xs[buf][(8 * g + t) * 32 + 16 * sc + c];
+      u32x4_t bx[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t sel = (u & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          bx[u][q] = __builtin_amdgcn_perm(rows[2 * q + 1][u >> 1], rows[2 * q][u >> 1], sel);
+      }
+#pragma unroll
+      for (int it = 0; it < kIT / 2; ++it) {
+        const u32x4_t a = frag1[((8 * rh + it) * kNChunk + ch) * 64 + lane];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) y[it][u] = mfma16x16x32<DT>(a, bx[u], y[it][u]);
+      }
+      buf ^= 1;
+    }
+
+    // [FQV2] 第3步 pergroup / 第4步: 32-groups of 4 neighbouring lanes
+    uint8_t* codes = b.codes + s * (kW * kW / 2);
+    uint8_t* e8 = static_cast<uint8_t*>(b.scale) + s * e8m0_bytes_per_slice(kW * kW);
+#pragma unroll
+    for (int it = 0; it < kIT / 2; ++it)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 128 * rh + 16 * it + 4 * g + i;
+        float amax = 0.0f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) amax = fmaxf(amax, __builtin_fabsf(y[it][u][i]));
+        amax = group_max<4>(amax);
+        const uint32_t code = e8m0_code_fast(amax, pb.dmax, dinv);
+        const float scf = e8m0_to_float(code);
+        uint32_t packed = fp4x2<0>(0u, y[it][0][i], y[it][1][i], scf);
+        packed = fp4x2<1>(packed, y[it][2][i], y[it][3][i], scf);
+        packed = fp4x2<2>(packed, y[it][4][i], y[it][5][i], scf);
+        packed = fp4x2<3>(packed, y[it][6][i], y[it][7][i], scf);
+        *reinterpret_cast<uint32_t*>(codes + row * (kW / 2) + 64 * sc + 4 * c) = packed;
+        if ((c & 3) == 0) e8[row * (kW / 32) + 4 * sc + (c >> 2)] = static_cast<uint8_t>(code);
+      }
+  }
+}
+
+template <int DT>
+hipError_t launch_w1(const Problem& pb, const Buffers& b, hipStream_t s) {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+  }
+  const int grid = static_cast<int>(pb.K < cus ? pb.K : cus);
+  mfma_wide1_kernel<DT><<<grid, kWideThreads, 0, s>>>(pb, b);
+  return hipGetLastError();
+}
+
 template <int DT, bool PG, bool CLAMP>
 hipError_t launch_w2(const Problem& pb, const Buffers& b, hipStream_t s) {
   static int cus = 0;
@@ -215,10 +340,13 @@ hipError_t dispatch_w2(const Problem& pb, const Buffers& b, hipStream_t s) {
 
 }  // namespace
 
-bool mfma_wide_supports(const Problem& pb) { return pb.M == kW && pb.N == kW && pb.two_sided; }
+bool mfma_wide_supports(const Problem& pb) {
+  return pb.M == kW && pb.N == kW && (pb.two_sided || pb.mode == kPerGroupFp4);
+}
 
 hipError_t launch_mfma_wide(const Problem& pb, const Buffers& b, hipStream_t s) {
   if (!mfma_wide_supports(pb)) return hipErrorNotSupported;
+  if (!pb.two_sided) return pb.dtype == kBF16 ? launch_w1<kBF16>(pb, b, s) : launch_w1<kF16>(pb, b, s);
   return pb.dtype == kBF16 ? dispatch_w2<kBF16>(pb, b, s) : dispatch_w2<kF16>(pb, b, s);
 }
 
