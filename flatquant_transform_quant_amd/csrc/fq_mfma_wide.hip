@@ -194,9 +194,10 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb,
 
 // ---------------------------------------------------------------------------------------
 // Left-only 256 x 256 slices (P2 = [0, 0], per-group mode): y = P1 . x.
+//   * x moves HBM -> registers -> LDS in chunks of 32 rows (16 KB): four chunks (64 KB per
+//     CU) are in flight in registers while one is in LDS being used and the next is
+//     written to the other LDS buffer, so the HBM stream never waits on the products;
 //   * P1 is staged once in LDS as A fragments in natural k order (128 KB);
-//   * x streams through two 16 KB LDS buffers of 32 rows (one chunk is consumed while the
-//     next is written), the chunk after that prefetched into registers;
 //   * wave w computes rows 128*(w&1) .. +127 of columns 128*(w>>1) .. +127.  x is the B
 //     operand with the contraction over rows, so each lane reads 8 rows x 16 bytes
 //     (8 neighbouring columns) and transposes them in registers (v_perm_b32); MFMA u of a
@@ -206,14 +207,30 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb,
 template <int DT>
 __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide1_kernel(Problem pb, Buffers b) {
   __shared__ u32x4_t frag1[kIT * kNChunk * 64];  // 128 KB: P1 A fragments (natural k order)
-  __shared__ u32x4_t xs[2][kChunk * 32];         // 2 x 16 KB: x chunks, row-major 16-byte slots
+  __shared__ u32x4_t xs[2][kChunk * 32];         // 2 x 16 KB, row-major 16-byte slots
+  constexpr int D = 4;                    // chunks in flight in registers (divides 8)
+  constexpr int XR = kChunk * kW * 2 / 16 / kWideThreads;  // 16-byte pieces per thread per chunk
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, g = lane >> 4;
   const int rh = w & 1, sc = w >> 1;  // row half, column half
+  const int64_t stride = gridDim.x;
 
+  u32x4_t xr[D][XR];
+  // chunk j of this workgroup: slice blockIdx.x + (j / 8) * gridDim.x, rows 32 * (j % 8)
+  auto load_chunk = [&](int64_t j, u32x4_t* r) {
+    const int64_t slice = blockIdx.x + (j >> 3) * stride;
+    if (slice >= pb.K) return;
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(b.x + slice * (kW * kW) + (j & 7) * (kChunk * kW));
+#pragma unroll
+    for (int h = 0; h < XR; ++h) r[h] = src[tid + h * kWideThreads];
+  };
+  auto store_chunk = [&](const u32x4_t* r, u32x4_t* dst) {
+#pragma unroll
+    for (int h = 0; h < XR; ++h) dst[tid + h * kWideThreads] = r[h];
+  };
   // P1[i, 32ch + 8gg .. +7] -> frag1[(it*8 + ch)*64 + 16*gg + i%16]
   for (int q = tid; q < kW * kW / 8; q += kWideThreads) {
     const int i = q >> 5, m0 = (q & 31) * 8;
@@ -221,47 +238,36 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide1_kernel(Problem pb,
     frag1[(it * kNChunk + ch) * 64 + 16 * gg + (i & 15)] = reinterpret_cast<const u32x4_t*>(b.p1)[q];
   }
 
-  constexpr int XR = kChunk * kW * 2 / 16 / kWideThreads;
-  u32x4_t xr[XR];
-  // global chunk index gc = slice_round * 8 + ch, slice = blockIdx.x + round * gridDim.x
-  auto load_chunk = [&](int64_t slice, int ch) {
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(b.x + slice * (kW * kW) + ch * (kChunk * kW));
-#pragma unroll
-    for (int h = 0; h < XR; ++h) xr[h] = src[tid + h * kWideThreads];
-  };
-  auto store_chunk = [&](int buf) {
-#pragma unroll
-    for (int h = 0; h < XR; ++h) xs[buf][tid + h * kWideThreads] = xr[h];
-  };
-
   int64_t s = blockIdx.x;
   if (s >= pb.K) return;
-  load_chunk(s, 0);
-  store_chunk(0);
-  if (kNChunk > 1) load_chunk(s, 1);
-  int buf = 0;
+  // prologue: chunk 0 in LDS, chunks 1 .. D in registers (chunk k in xr[k % D])
+  load_chunk(0, xr[0]);
+  store_chunk(xr[0], xs[0]);
+#pragma unroll
+  for (int k = 1; k <= D; ++k) load_chunk(k, xr[k % D]);
+
   const float dinv = pb.dmax_inv;
-  for (; s < pb.K; s += gridDim.x) {
+  int64_t j0 = 0;  // chunk index of this slice's chunk 0
+  for (; s < pb.K; s += stride, j0 += kNChunk) {
     f32x4_t y[kIT / 2][8];
 #pragma unroll
     for (int it = 0; it < kIT / 2; ++it)
 #pragma unroll
       for (int u = 0; u < 8; ++u) y[it][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+#pragma unroll
     for (int ch = 0; ch < kNChunk; ++ch) {
-      __syncthreads();  // chunk ch is in xs[buf]; every wave is done with xs[buf ^ 1]
-      // the chunk after this one: regs -> the free buffer; then prefetch the one after
-      const bool more = ch + 1 < kNChunk || s + gridDim.x < pb.K;
-      if (more) store_chunk(buf ^ 1);
-      if (ch + 2 < kNChunk)
-        load_chunk(s, ch + 2);
-      else if (s + gridDim.x < pb.K)
-        load_chunk(s + gridDim.x, ch + 2 - kNChunk);
+      // chunk ch is in xs[ch & 1]; every wave is done with the other buffer
+      __syncthreads();
+      // chunk ch + 1: registers -> the free buffer; then request chunk ch + 1 + D into
+      // the registers it frees
+      store_chunk(xr[(ch + 1) % D], xs[(ch + 1) & 1]);
+      load_chunk(j0 + ch + 1 + D, xr[(ch + 1) % D]);
 
       // B operands: rows 8g .. 8g+7 of the chunk, columns 128sc + 8c .. +7, transposed
       u32x4_t rows[8];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) rows[t] = xs[buf][(8 * g + t) * 32 + 16 * sc + c];
+      for (int t = 0; t < 8; ++t) rows[t] = xs[ch & 1][(8 * g + t) * 32 + 16 * sc + c];
       u32x4_t bx[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -276,7 +282,6 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide1_kernel(Problem pb,
 #pragma unroll
         for (int u = 0; u < 8; ++u) y[it][u] = mfma16x16x32<DT>(a, bx[u], y[it][u]);
       }
-      buf ^= 1;
     }
 
     // [FQV2] 第3步 pergroup / 第4步: 32-groups of 4 neighbouring lanes
