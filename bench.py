@@ -47,6 +47,35 @@ def algorithmic_flops(w, K=None) -> int:
     return K * f
 
 
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources; the profile summaries record it beside their counters."""
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "flatquant_transform_quant_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(w):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of this workload
+    (FETCH_SIZE and WRITE_SIZE, each scaled against a copy kernel of known size), or None
+    when there is none or the kernels have changed since the counters were taken."""
+    import glob
+
+    for f in glob.glob(os.path.join(ROOT, "profiles", f"*_{w.name}.md")):
+        with open(f, encoding="utf-8") as fh:
+            for line in fh:
+                if line.startswith("machine-readable:"):
+                    info = json.loads(line.split(":", 1)[1])
+                    if info.get("source_hash") == kernel_source_hash():
+                        return info.get("traffic_bytes_per_dispatch")
+    return None
+
+
 def cpu_baseline(w, x_host, p1, p2, budget_s: float = 10.0):
     """The oracle (codes and scales only) on the host cores, on a bounded sample of
     slices of the same workload, scaled to Gelem/s."""
@@ -145,11 +174,12 @@ def main() -> int:
     hbm_frac = gbs / HBM_PEAK_GBS
     mfma_frac = tfs / MFMA_BF16_PEAK_TFS
     bound = "hbm" if bytes_ / (HBM_PEAK_GBS * 1e9) >= flops / (MFMA_BF16_PEAK_TFS * 1e12) else "mfma"
+    traffic = profiled_traffic(w)
     roof = ({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-             "frac": round(hbm_frac, 4), "traffic": None}
+             "frac": round(hbm_frac, 4), "traffic": traffic}
             if bound == "hbm" else
             {"bound": "mfma", "achieved": round(tfs, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-             "frac": round(mfma_frac, 4), "traffic": None})
+             "frac": round(mfma_frac, 4), "traffic": traffic})
     roof["kernel"] = {1: "generic_kernel", 2: "mfma_small_kernel", 3: "mfma_wide_kernel"}.get(kernel_id)
     roof["avg_launch_us"] = round(avg_launch_ms * 1e3, 3)
     roof["algorithmic_bytes"] = bytes_
