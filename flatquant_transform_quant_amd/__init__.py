@@ -39,12 +39,22 @@ class FqTensor(ctypes.Structure):
 class FqError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
-        super().__init__(f"{what}: {status_string(status)} ({status})")
+        detail = lib.fq_last_error().decode() if status == FQ_ERR_RUNTIME else ""
+        self.detail = detail
+        super().__init__(f"{what}: {status_string(status)} ({status})" + (f": {detail}" if detail else ""))
 
 
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libfq is not built ({LIB_PATH} missing): run __graft_entry__.build()")
+    # torch ships its own HIP runtime under the same soname as the system one.  Loading
+    # torch first makes libfq bind to that copy, so the process holds one HIP runtime and
+    # the device pointers and streams torch hands over are valid handles in libfq too.
+    # (Loaded the other way round, two runtimes coexist, each with its own device state.)
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER(FqTensor)
     vp = ctypes.c_void_p
@@ -63,12 +73,14 @@ def _load():
     L.fq_executor_kernel.restype = ctypes.c_int32
     L.fq_status_string.argtypes = [ctypes.c_int32]
     L.fq_status_string.restype = ctypes.c_char_p
+    L.fq_last_error.argtypes = []
+    L.fq_last_error.restype = ctypes.c_char_p
     return L
 
 
 lib = _load()
 EXPORTS = ("fq_get_workspace_size", "fq_run", "fq_executor_destroy", "fq_executor_set_repeatable",
-           "fq_executor_set_kernel", "fq_executor_kernel", "fq_status_string")
+           "fq_executor_set_kernel", "fq_executor_kernel", "fq_status_string", "fq_last_error")
 
 
 def status_string(status: int) -> str:
@@ -127,6 +139,10 @@ def fq_executor_kernel(executor: int) -> int:
 
 def fq_status_string(status: int) -> str:
     return status_string(status)
+
+
+def fq_last_error() -> str:
+    return lib.fq_last_error().decode()
 
 
 # ---- torch marshalling ---------------------------------------------------------------

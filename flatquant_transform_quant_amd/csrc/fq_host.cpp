@@ -9,6 +9,7 @@
 
 #include <atomic>
 #include <cmath>
+#include <cstdio>
 #include <cstring>
 #include <mutex>
 #include <new>
@@ -65,6 +66,15 @@ bool shape_is(const fq_tensor& t, int nd, int64_t a, int64_t b = 0, int64_t c = 
 }
 
 uint64_t align256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
+
+// Detail of the last runtime failure on this thread (fq_last_error).
+thread_local char g_last_error[256];
+
+fq_status fail_runtime(const char* what, hipError_t err) {
+  std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s (hipError %d)", what,
+                err == hipSuccess ? "failed" : hipGetErrorString(err), static_cast<int>(err));
+  return FQ_ERR_RUNTIME;
+}
 
 // gfx950 check, cached per device id.
 std::mutex g_arch_mu;
@@ -132,6 +142,7 @@ fq_status fq_get_workspace_size(const fq_tensor* x, const fq_tensor* kroneckerP1
                                 const fq_tensor* kroneckerP2, double clipRatio, double dstTypeMax,
                                 const fq_tensor* out, const fq_tensor* quantScale,
                                 uint64_t* workspaceSize, fq_executor** executor) {
+  g_last_error[0] = '\0';
   // [FQV2] 容易踩的坑: a NULL among the three inputs and two outputs -> 161001.
   if (!x || !kroneckerP1 || !kroneckerP2 || !out || !quantScale || !workspaceSize || !executor)
     return FQ_ERR_PARAM_NULLPTR;
@@ -190,7 +201,7 @@ fq_status fq_get_workspace_size(const fq_tensor* x, const fq_tensor* kroneckerP1
   }
 
   fq_executor* e = new (std::nothrow) fq_executor();
-  if (!e) return FQ_ERR_RUNTIME;
+  if (!e) return fail_runtime("executor allocation", hipErrorOutOfMemory);
   e->magic = kLiveMagic;
   e->pb.dtype = dt == FQ_DT_FLOAT16 ? fq::kF16 : fq::kBF16;
   e->pb.mode = mode;
@@ -251,6 +262,7 @@ static void release(fq_executor* e) {
 }
 
 fq_status fq_run(void* workspace, uint64_t workspaceSize, fq_executor* executor, hipStream_t stream) {
+  g_last_error[0] = '\0';
   if (!executor) return FQ_ERR_PARAM_NULLPTR;
   if (!live(executor)) return FQ_ERR_PARAM_INVALID;
   fq_executor* e = executor;
@@ -258,7 +270,7 @@ fq_status fq_run(void* workspace, uint64_t workspaceSize, fq_executor* executor,
   do {
     if (e->ws_size > 0 && !workspace) { st = FQ_ERR_PARAM_NULLPTR; break; }
     if (workspaceSize < e->ws_size) { st = FQ_ERR_PARAM_INVALID; break; }
-    if (!device_is_gfx950()) { st = FQ_ERR_RUNTIME; break; }
+    if (!device_is_gfx950()) { st = fail_runtime("the current device is not gfx950", hipSuccess); break; }
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     const fq::Problem& pb = e->pb;
     const int64_t MN = pb.M * pb.N;
@@ -281,13 +293,13 @@ fq_status fq_run(void* workspace, uint64_t workspaceSize, fq_executor* executor,
     b.p2 = pb.two_sided ? gather(e->p2, e->stage_p2, e->off_p2, 2) : nullptr;
     b.codes = e->stage_out ? ws + e->off_out : static_cast<uint8_t*>(e->out.data);
     b.scale = e->stage_scale ? static_cast<void*>(ws + e->off_scale) : e->scale.data;
-    if (err != hipSuccess) { st = FQ_ERR_RUNTIME; break; }
+    if (err != hipSuccess) { st = fail_runtime("strided input gather launch", err); break; }
     switch (e->kernel) {
       case fq::kMfmaSmall: err = fq::launch_mfma_small(pb, b, stream); break;
       case fq::kMfmaWide: err = fq::launch_mfma_wide(pb, b, stream); break;
       default: err = fq::launch_generic(pb, b, stream); break;
     }
-    if (err != hipSuccess) { st = FQ_ERR_RUNTIME; break; }
+    if (err != hipSuccess) { st = fail_runtime("transform-quantize kernel launch", err); break; }
     if (e->stage_out) {
       // The codes as bytes: INT32 [K, M, N/8] words, INT4 [K, M, N/2] and
       // FLOAT4_E2M1 [K, M*N/2] byte rows (strides in 4-bit elements halve).
@@ -320,7 +332,7 @@ fq_status fq_run(void* workspace, uint64_t workspaceSize, fq_executor* executor,
       }
       err = fq::launch_scatter(b.scale, e->scale.data, eb, shape, strides, stream);
     }
-    if (err != hipSuccess) { st = FQ_ERR_RUNTIME; break; }
+    if (err != hipSuccess) { st = fail_runtime("strided output scatter launch", err); break; }
   } while (false);
   if (!e->repeatable) release(e);
   return st;
@@ -350,6 +362,8 @@ int32_t fq_executor_kernel(const fq_executor* executor) {
   if (!live(executor)) return -1;
   return executor->kernel;
 }
+
+const char* fq_last_error(void) { return g_last_error; }
 
 const char* fq_status_string(fq_status status) {
   switch (status) {

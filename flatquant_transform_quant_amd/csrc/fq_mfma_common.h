@@ -24,6 +24,9 @@ typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 
+// Word 3 of a raw buffer resource on gfx9-class devices (32-bit data format, no swizzle).
+constexpr int32_t kBufferWord3 = 0x00020000;
+
 template <int DT>
 __device__ __forceinline__ f32x4_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
   if constexpr (DT == kBF16) {

@@ -28,8 +28,10 @@ namespace {
 constexpr int kSmallWaves = 4;
 constexpr int kSmallThreads = 64 * kSmallWaves;
 
-// Slices of x kept in flight per wave: two for small slices (the next two slices are
-// requested before the current one's products start), one where registers are short.
+// Slices of x kept in flight per wave: two for small slices (the loads of the slice two
+// ahead are issued as soon as the current one's first product has consumed its
+// registers), one where registers are short.  (Three measured slower: the extra slice
+// every wave queues at the start delays every wave's first slice.)
 template <int M, int N, bool PG>
 constexpr int prefetch_depth() {
   return (M * N <= 4096) ? 2 : 1;
@@ -62,45 +64,57 @@ __global__ __launch_bounds__(kSmallThreads, 2) void mfma_small_kernel(Problem pb
   int64_t s = int64_t(blockIdx.x) * kSmallWaves + wave;
 
   // x operands of a slice: xa[buf][mt][ks] = x[16mt + c, 32ks + 8g .. +7]
+  // The loads go through a buffer resource that covers exactly the requested slice, or
+  // nothing when the index is at or past K: such a request returns zeros and touches no
+  // memory.  The loads are therefore issued unconditionally, which keeps the count of
+  // memory operations in flight the same on every path, so the compiler's waits for a
+  // buffer cover that buffer's loads only and not the ones issued after them.
   constexpr int PF = prefetch_depth<M, N, PG>();
   u32x4_t xa[PF][MT][KS1];
   auto load_x = [&](int buf, int64_t slice) {
-    const uint16_t* xs = b.x + slice * MN;
+    const bool in = slice < pb.K;
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(b.x + (in ? slice : 0) * MN),
+                                                        static_cast<int16_t>(0), in ? MN * 2 : 0,
+                                                        kBufferWord3);
+    // row tile in the scalar offset, k-step in the immediate: one address register
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int ks = 0; ks < KS1; ++ks)
-        xa[buf][mt][ks] = *reinterpret_cast<const u32x4_t*>(xs + (16 * mt + c) * N + 32 * ks + 8 * g);
+        xa[buf][mt][ks] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (c * N + 32 * ks + 8 * g) * 2,
+                                                                16 * mt * N * 2, 0);
   };
-  // With two slices in flight the first loads are issued before the P staging, so the
-  // two memory latencies overlap; with one (large slices) registers are too short.
-  if constexpr (PF == 2) {
-#pragma unroll
-    for (int q = 0; q < PF; ++q)
-      if (s + q * waves < pb.K) load_x(q, s + q * waves);
-  }
-
   // ---- stage P2 / P1 fragments (once per workgroup) ----
   // All coalesced 16-byte loads of P1 and P2 are issued first (one memory latency), then
   // each 2-byte value is written to its fragment slot:
   //   P2[j, n]  -> frag2[(ks*NT + nt)*64 + 16*g + c], element t   (j = 32ks + 8g + t, n = R*c + nt)
   //   P1[i, m]  -> frag1[(it*KS2 + ks2)*64 + 16*g + i%16], element t, where m = 32ks2 + w and
   //                w = 4g + t (t < 4) or 16 + 4g + (t - 4) (t >= 4)
+  // The P loads go first and the x loads of the first slices right after them, so the
+  // staging below waits for P alone (the memory counter completes in issue order) while
+  // x is still arriving.  Chunks past the end of P1/P2 (or all of P2 when it is empty)
+  // read zeros through bounded buffer resources, so no load is conditional.
   {
     constexpr int C2 = N * N / 8, C1 = M * M / 8;  // 16-byte chunks of P2 and P1
     constexpr int L2 = (C2 + kSmallThreads - 1) / kSmallThreads;
     constexpr int L1 = (C1 + kSmallThreads - 1) / kSmallThreads;
     u32x4_t r2[L2], r1[L1];
     const bool two = pb.two_sided != 0;
+    const auto rs2 = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(two ? b.p2 : b.p1),
+                                                      static_cast<int16_t>(0), two ? N * N * 2 : 0,
+                                                      kBufferWord3);
+    const auto rs1 = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(b.p1), static_cast<int16_t>(0),
+                                                      M * M * 2, kBufferWord3);
 #pragma unroll
-    for (int q = 0; q < L2; ++q) {
-      const int ch = tid + q * kSmallThreads;
-      if (two && ch < C2) r2[q] = reinterpret_cast<const u32x4_t*>(b.p2)[ch];
-    }
+    for (int q = 0; q < L2; ++q) r2[q] = __builtin_amdgcn_raw_buffer_load_b128(rs2, (tid + q * kSmallThreads) * 16, 0, 0);
 #pragma unroll
-    for (int q = 0; q < L1; ++q) {
-      const int ch = tid + q * kSmallThreads;
-      if (ch < C1) r1[q] = reinterpret_cast<const u32x4_t*>(b.p1)[ch];
+    for (int q = 0; q < L1; ++q) r1[q] = __builtin_amdgcn_raw_buffer_load_b128(rs1, (tid + q * kSmallThreads) * 16, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);  // keep the issue order: P, then x
+    // With two slices in flight their loads are issued now, overlapping the staging; with
+    // one (large slices) registers are too short and the load waits for the slice loop.
+    if constexpr (PF > 1) {
+#pragma unroll
+      for (int q = 0; q < PF; ++q) load_x(q, s + q * waves);
     }
     uint16_t* f2 = reinterpret_cast<uint16_t*>(frag2);
     uint16_t* f1 = reinterpret_cast<uint16_t*>(frag1);
@@ -184,6 +198,13 @@ __global__ __launch_bounds__(kSmallThreads, 2) void mfma_small_kernel(Problem pb
     // Keep the P fragments in LDS: without this the compiler hoists the loop-invariant
     // fragment reads into registers, which costs occupancy.
     asm volatile("" ::: "memory");
+    // The lane's offsets into the staging buffer (codes of row 4g, column group R*c; its
+    // e8m0 byte).  Made opaque per slice so the per-row addresses are formed here, with
+    // the row as an immediate offset, instead of being hoisted out of the slice loop and
+    // held in registers.
+    int code_off = 4 * g * (N / 2) + (R / 2) * c;
+    int e8_off = CODE_BYTES + 4 * g * (N / 32) + (R * c) / 32;
+    asm volatile("" : "+v"(code_off), "+v"(e8_off));
     // ---- GEMM1: T = x . P2 (fp32), rounded to the dtype and written straight into the
     // GEMM2 B operands: bt[ks2][nt] = {T rows 32ks2 + 4g + 0..3, T rows 32ks2 + 16 + 4g + 0..3}
     // of column R*c + nt (2 x 16 bit per dword).
@@ -213,8 +234,7 @@ __global__ __launch_bounds__(kSmallThreads, 2) void mfma_small_kernel(Problem pb
       }
     }
     // this buffer is free again: request the slice PF steps ahead
-    const int64_t s_next = s + PF * waves;
-    if (s_next < pb.K) load_x(buf, s_next);
+    load_x(buf, s + PF * waves);
 
     if constexpr (!PG) {
       // ---- GEMM2: y = P1 . T, all of y (the scale needs max|y| over the slice) ----
@@ -247,13 +267,13 @@ __global__ __launch_bounds__(kSmallThreads, 2) void mfma_small_kernel(Problem pb
       for (int it = 0; it < MT; ++it)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int row = 16 * it + 4 * g + i;
+          const int r0 = 16 * it + i;  // row - 4g
           uint32_t by[R / 2];
 #pragma unroll
           for (int p = 0; p < R / 2; ++p)
             by[p] = pair_byte(int4_biased<CLAMP>(y[it][2 * p][i], inv),
                               int4_biased<CLAMP>(y[it][2 * p + 1][i], inv));
-          uint8_t* dst = st + row * (N / 2) + (R / 2) * c;
+          uint8_t* dst = st + code_off + r0 * (N / 2);
           if constexpr (R == 2) {
             *dst = static_cast<uint8_t>(by[0] ^ 0x88u);
           } else if constexpr (R == 4) {
@@ -280,7 +300,7 @@ __global__ __launch_bounds__(kSmallThreads, 2) void mfma_small_kernel(Problem pb
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int row = 16 * it + 4 * g + i;
+          const int r0 = 16 * it + i;  // row - 4g
           float amax = 0.0f;
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) amax = fmaxf(amax, __builtin_fabsf(y[nt][i]));
@@ -294,7 +314,7 @@ __global__ __launch_bounds__(kSmallThreads, 2) void mfma_small_kernel(Problem pb
             packed = fp4x2<2>(packed, y[4][i], y[5][i], sc);
             packed = fp4x2<3>(packed, y[6][i], y[7][i], sc);
           }
-          uint8_t* dst = st + row * (N / 2) + (R / 2) * c;
+          uint8_t* dst = st + code_off + r0 * (N / 2);
           if constexpr (R == 2) {
             *dst = static_cast<uint8_t>(packed);
           } else if constexpr (R == 4) {
@@ -302,7 +322,9 @@ __global__ __launch_bounds__(kSmallThreads, 2) void mfma_small_kernel(Problem pb
           } else {
             *reinterpret_cast<uint32_t*>(dst) = packed;
           }
-          if ((c % SPAN) == 0) st[CODE_BYTES + (row * N + R * c) / 32] = static_cast<uint8_t>(code);
+          // Group index (row*N + R*c)/32.  Every lane of a group holds the same code, so
+          // all of them store it (no branch).
+          st[e8_off + r0 * (N / 32)] = static_cast<uint8_t>(code);
         }
       }
       // (M*N/32 is even for every supported shape, so there is no pad byte)
@@ -310,13 +332,14 @@ __global__ __launch_bounds__(kSmallThreads, 2) void mfma_small_kernel(Problem pb
     flush(s);
   };
 
-  for (; s < pb.K; s += PF * waves) {
-    process(0, s);
-    if constexpr (PF == 2) {
-      if (s + waves >= pb.K) break;
-      process(1, s + waves);
-    }
+  // PF slices per iteration, then the last few: no exit from the middle of the loop body
+  for (; s + (PF - 1) * waves < pb.K; s += PF * waves) {
+#pragma unroll
+    for (int q = 0; q < PF; ++q) process(q, s + q * waves);
   }
+#pragma unroll
+  for (int q = 0; q + 1 < PF; ++q)
+    if (s + q * waves < pb.K) process(q, s + q * waves);
 }
 
 template <int DT, int M, int N, bool PG, bool CLAMP>

@@ -142,6 +142,11 @@ int32_t fq_executor_kernel(const fq_executor* executor);
 /* A static, human-readable name for a status code. */
 const char* fq_status_string(fq_status status);
 
+/* Detail of the last FQ_ERR_RUNTIME returned on the calling thread: the HIP call that
+ * failed and the runtime's error text, or "" when there was none.  The string is owned by
+ * the library and stays valid until the thread's next call into it. */
+const char* fq_last_error(void);
+
 #ifdef __cplusplus
 }
 #endif

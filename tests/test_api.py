@@ -8,6 +8,8 @@ x's dimension ranges are checked before the other rules.
 import ctypes
 import os
 import re
+import subprocess
+import sys
 
 import pytest
 
@@ -259,3 +261,14 @@ def test_kernel_selection_api():
 def test_status_strings():
     for s in (OK, NULLP, INVAL, fq.FQ_ERR_RUNTIME, 42):
         assert isinstance(fq.status_string(s), str) and fq.status_string(s)
+
+
+def test_one_hip_runtime_per_process():
+    """Importing the binding before torch must not leave two HIP runtimes mapped: torch's
+    copy and the system one share a soname, and handles from one are invalid in the other."""
+    code = ("import flatquant_transform_quant_amd, torch\n"
+            "paths = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+            "print(len(paths))\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip().splitlines()[-1] == "1"
