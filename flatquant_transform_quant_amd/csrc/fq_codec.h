@@ -84,14 +84,24 @@ __device__ __forceinline__ uint32_t e8m0_code(float amax, float dmax) {
   return E;
 }
 
-// As e8m0_code, with dinv = 1/dmax when dmax is a power of two (0 otherwise): then
-// amax * dinv is exactly the IEEE quotient amax / dmax and the division is skipped.
-__device__ __forceinline__ uint32_t e8m0_code_fast(float amax, float dmax, float dinv) {
-  if (dmax == 0.0f || dinv == 0.0f) return e8m0_code(amax, dmax);
-  const uint32_t s = __float_as_uint(amax * dinv);
-  uint32_t E = (s >> 23) & 0xFFu;
-  if (E >= 1u && E < 254u && (s & 0x7FFFFFu) != 0u) E += 1u;
-  return E;
+// The e8m0 rule as a compile-time variant, so a kernel's epilogue has no branch on it:
+//   kE8V1     dmax == 0: the V1 rule;
+//   kE8V2Pow2 dmax a power of two, dinv = 1/dmax: amax * dinv is exactly the IEEE
+//             quotient amax / dmax, so the division is skipped;
+//   kE8V2Div  any other dmax: the quotient by division.
+enum E8Variant : int { kE8V1 = 0, kE8V2Pow2 = 1, kE8V2Div = 2 };
+
+template <int SV>
+__device__ __forceinline__ uint32_t e8m0_code_v(float amax, float dmax, float dinv) {
+  if constexpr (SV == kE8V1) {
+    const int e = static_cast<int>((__float_as_uint(amax) >> 23) & 0xFFu) - 2;
+    return static_cast<uint32_t>(e < 0 ? 0 : (e > 254 ? 254 : e));
+  } else {
+    const uint32_t s = __float_as_uint(SV == kE8V2Pow2 ? amax * dinv : amax / dmax);
+    uint32_t E = (s >> 23) & 0xFFu;
+    if (E >= 1u && E < 254u && (s & 0x7FFFFFu) != 0u) E += 1u;
+    return E;
+  }
 }
 
 // y * 2^(127 - code): exact (v_ldexp), the reciprocal of the e8m0 scale.

@@ -35,6 +35,10 @@ struct Buffers {
 };
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Which e8m0 rule a per-group launch compiles in (the E8Variant of the codec):
+// 0 = V1 (dmax 0), 1 = V2 with dmax a power of two, 2 = V2 with a division.
+inline int e8m0_variant(const Problem& pb) { return pb.dmax == 0.0f ? 0 : (pb.dmax_inv != 0.0f ? 1 : 2); }
 __host__ __device__ inline int64_t e8m0_bytes_per_slice(int64_t MN) { return 2 * ceil_div(MN, 64); }
 
 // Launchers (enqueue only; return the launch status).

@@ -27,6 +27,17 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 // Word 3 of a raw buffer resource on gfx9-class devices (32-bit data format, no swizzle).
 constexpr int32_t kBufferWord3 = 0x00020000;
 
+// Workgroup barrier that orders LDS accesses only.  The workgroup-scope fence of
+// __syncthreads also waits for every earlier global store, and since loads and stores
+// share one in-order memory counter, for every load issued before them: a barrier after
+// a slice's output stores would drain all the input prefetched behind them.  Nothing in
+// these kernels passes data between waves through global memory.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <int DT>
 __device__ __forceinline__ f32x4_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
   if constexpr (DT == kBF16) {
@@ -44,6 +55,9 @@ enum : int {
   kDppQuadXor2 = 0x4E,    // quad_perm [2,3,0,1]
   kDppRowHalfMirror = 0x141,
   kDppRowMirror = 0x140,
+  kDppRowRor4 = 0x124,    // rotate by 4 / 8 / 12 lanes within the row
+  kDppRowRor8 = 0x128,
+  kDppRowRor12 = 0x12C,
 };
 
 template <int CTRL>

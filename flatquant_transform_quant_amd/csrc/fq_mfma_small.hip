@@ -37,7 +37,8 @@ constexpr int prefetch_depth() {
   return (M * N <= 4096) ? 2 : 1;
 }
 
-template <int DT, int M, int N, bool PG, bool CLAMP>
+// CLAMP (per token): the int4 clamp is compiled in.  SV (per group): the e8m0 rule.
+template <int DT, int M, int N, bool PG, bool CLAMP, int SV>
 __global__ __launch_bounds__(kSmallThreads, 2) void mfma_small_kernel(Problem pb, Buffers b) {
   constexpr int MT = M / 16, NT = N / 16, R = N / 16;
   constexpr int KS1 = N / 32;              // GEMM1 k-steps over j
@@ -113,8 +114,12 @@ __global__ __launch_bounds__(kSmallThreads, 2) void mfma_small_kernel(Problem pb
     // With two slices in flight their loads are issued now, overlapping the staging; with
     // one (large slices) registers are too short and the load waits for the slice loop.
     if constexpr (PF > 1) {
+      // in slice order (the loop's first wait is for the first slice)
 #pragma unroll
-      for (int q = 0; q < PF; ++q) load_x(q, s + q * waves);
+      for (int q = 0; q < PF; ++q) {
+        load_x(q, s + q * waves);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     uint16_t* f2 = reinterpret_cast<uint16_t*>(frag2);
     uint16_t* f1 = reinterpret_cast<uint16_t*>(frag1);
@@ -149,7 +154,7 @@ __global__ __launch_bounds__(kSmallThreads, 2) void mfma_small_kernel(Problem pb
     // P1 columns beyond M (M = 16: the second half of the k-step) hold zeros
     if (M < 32)
       for (int idx = tid; idx < MT * KS2 * 64; idx += kSmallThreads) frag1[idx] = u32x4_t{0u, 0u, 0u, 0u};
-    if (M < 32) __syncthreads();
+    if (M < 32) lds_barrier();
 #pragma unroll
     for (int q = 0; q < L1; ++q) {
       const int ch = tid + q * kSmallThreads;
@@ -167,7 +172,7 @@ __global__ __launch_bounds__(kSmallThreads, 2) void mfma_small_kernel(Problem pb
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
   if (s >= pb.K) return;
   if constexpr (PF == 1) load_x(0, s);
 
@@ -305,7 +310,7 @@ __global__ __launch_bounds__(kSmallThreads, 2) void mfma_small_kernel(Problem pb
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) amax = fmaxf(amax, __builtin_fabsf(y[nt][i]));
           amax = group_max<SPAN>(amax);
-          const uint32_t code = e8m0_code(amax, pb.dmax);
+          const uint32_t code = e8m0_code_v<SV>(amax, pb.dmax, pb.dmax_inv);
           const float sc = e8m0_to_float(code);
           uint32_t packed = 0;
           packed = fp4x2<0>(packed, y[0][i], y[1][i], sc);
@@ -342,7 +347,7 @@ __global__ __launch_bounds__(kSmallThreads, 2) void mfma_small_kernel(Problem pb
     if (s + q * waves < pb.K) process(q, s + q * waves);
 }
 
-template <int DT, int M, int N, bool PG, bool CLAMP>
+template <int DT, int M, int N, bool PG, bool CLAMP, int SV>
 hipError_t launch_one(const Problem& pb, const Buffers& b, hipStream_t s) {
   static int grid_cap = 0;  // workgroups that fit the device at once (per instantiation)
   if (grid_cap == 0) {
@@ -350,25 +355,29 @@ hipError_t launch_one(const Problem& pb, const Buffers& b, hipStream_t s) {
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e == hipSuccess)
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_small_kernel<DT, M, N, PG, CLAMP>,
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_small_kernel<DT, M, N, PG, CLAMP, SV>,
                                                        kSmallThreads, 0);
     if (e != hipSuccess) return e;
     grid_cap = cus * (per_cu > 0 ? per_cu : 1);
   }
   const int64_t need = (pb.K + kSmallWaves - 1) / kSmallWaves;
   const int grid = static_cast<int>(need < grid_cap ? need : grid_cap);
-  mfma_small_kernel<DT, M, N, PG, CLAMP><<<grid, kSmallThreads, 0, s>>>(pb, b);
+  mfma_small_kernel<DT, M, N, PG, CLAMP, SV><<<grid, kSmallThreads, 0, s>>>(pb, b);
   return hipGetLastError();
 }
 
 template <int DT, int M, int N, bool PG>
 hipError_t dispatch_clamp(const Problem& pb, const Buffers& b, hipStream_t s) {
   if constexpr (PG) {
-    return launch_one<DT, M, N, true, false>(pb, b, s);
+    switch (e8m0_variant(pb)) {
+      case kE8V1: return launch_one<DT, M, N, true, false, kE8V1>(pb, b, s);
+      case kE8V2Pow2: return launch_one<DT, M, N, true, false, kE8V2Pow2>(pb, b, s);
+      default: return launch_one<DT, M, N, true, false, kE8V2Div>(pb, b, s);
+    }
   } else {
     // The int4 clamp can only bite when (7/clipRatio) * (1 + 4 ulp) reaches 7.5.
-    if (pb.d >= 7.4999f) return launch_one<DT, M, N, false, true>(pb, b, s);
-    return launch_one<DT, M, N, false, false>(pb, b, s);
+    if (pb.d >= 7.4999f) return launch_one<DT, M, N, false, true, kE8V1>(pb, b, s);
+    return launch_one<DT, M, N, false, false, kE8V1>(pb, b, s);
   }
 }
 

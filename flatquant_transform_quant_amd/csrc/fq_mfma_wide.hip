@@ -17,6 +17,8 @@
 //     the 4 waves through LDS; per group, a 32-group is 8 neighbouring lanes of one row.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "fq_mfma_common.h"
 
 namespace fq {
@@ -30,7 +32,8 @@ constexpr int kChunk = 32;    // rows of x per chunk
 constexpr int kNChunk = kW / kChunk;
 constexpr int kIT = kW / 16;  // 16-row tiles of y
 
-template <int DT, bool PG, bool CLAMP>
+// CLAMP (per token): the int4 clamp is compiled in.  SV (per group): the e8m0 rule.
+template <int DT, bool PG, bool CLAMP, int SV>
 __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb, Buffers b) {
   __shared__ u32x4_t frag1[kIT * kNChunk * 64];   // 128 KB: P1 A fragments
   __shared__ u32x4_t xs[kChunk * 32];             // 16 KB: one x chunk, 32 slots of 16 B per row
@@ -105,9 +108,9 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb,
       for (int nt = 0; nt < kNT; ++nt) y[it][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     for (int ch = 0; ch < kNChunk; ++ch) {
-      __syncthreads();  // every wave is done with the previous chunk (and with `red`)
+      lds_barrier();  // every wave is done with the previous chunk (and with `red`)
       store_chunk();
-      __syncthreads();  // the chunk is in LDS
+      lds_barrier();  // the chunk is in LDS
       if (ch + 1 < kNChunk)
         load_chunk(s, ch + 1);
       else if (s + gridDim.x < pb.K)
@@ -141,7 +144,13 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb,
       }
     }
 
-    uint8_t* codes = b.codes + s * (kW * kW / 2);
+    // Output stores go through buffer resources for this slice: a per-lane offset (made
+    // opaque per slice, so no per-row address is hoisted out of the slice loop and held in
+    // registers) plus the row as a scalar offset.
+    const auto rs_codes = __builtin_amdgcn_make_buffer_rsrc(b.codes + s * (kW * kW / 2), static_cast<int16_t>(0),
+                                                            kW * kW / 2, kBufferWord3);
+    int code_off = 4 * g * (kW / 2) + 32 * w + 2 * c;
+    asm volatile("" : "+v"(code_off));
     if constexpr (!PG) {
       // [FQV2] 第3步 pertoken: max|y| over the slice (4 waves), scale, codes
       float amax = 0.0f;
@@ -153,7 +162,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb,
           for (int i = 0; i < 4; ++i) amax = fmaxf(amax, __builtin_fabsf(y[it][nt][i]));
       amax = wave_max(amax);
       if (lane == 0) red[w] = amax;
-      __syncthreads();
+      lds_barrier();
       amax = red[0];
 #pragma unroll
       for (int q = 1; q < kWideWaves; ++q) amax = fmaxf(amax, red[q]);
@@ -164,29 +173,34 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb,
       for (int it = 0; it < kIT; ++it)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int row = 16 * it + 4 * g + i;
+          const int r0 = 16 * it + i;  // row - 4g
           const uint32_t b0 = pair_byte(int4_biased<CLAMP>(y[it][0][i], inv), int4_biased<CLAMP>(y[it][1][i], inv));
           const uint32_t b1 = pair_byte(int4_biased<CLAMP>(y[it][2][i], inv), int4_biased<CLAMP>(y[it][3][i], inv));
-          *reinterpret_cast<uint16_t*>(codes + row * (kW / 2) + 32 * w + 2 * c) =
+          *reinterpret_cast<uint16_t*>(b.codes + s * (kW * kW / 2) + (r0 + 4 * g) * (kW / 2) + 32 * w + 2 * c) =
               static_cast<uint16_t>(unbias(__builtin_amdgcn_perm(b1, b0, 0x0C0C0400u)));
         }
     } else {
       // [FQV2] 第3步 pergroup / 第4步: a 32-group is 8 neighbouring lanes of one row
-      uint8_t* e8 = static_cast<uint8_t*>(b.scale) + s * e8m0_bytes_per_slice(kW * kW);
+      const auto rs_e8 = __builtin_amdgcn_make_buffer_rsrc(
+          static_cast<uint8_t*>(b.scale) + s * e8m0_bytes_per_slice(kW * kW), static_cast<int16_t>(0),
+          static_cast<int>(e8m0_bytes_per_slice(kW * kW)), kBufferWord3);
+      int e8_off = 4 * g * (kW / 32) + 2 * w + (c >> 3);
+      asm volatile("" : "+v"(e8_off));
 #pragma unroll
       for (int it = 0; it < kIT; ++it)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int row = 16 * it + 4 * g + i;
+          const int r0 = 16 * it + i;  // row - 4g
           float amax = fmaxf(fmaxf(__builtin_fabsf(y[it][0][i]), __builtin_fabsf(y[it][1][i])),
                              fmaxf(__builtin_fabsf(y[it][2][i]), __builtin_fabsf(y[it][3][i])));
           amax = group_max<8>(amax);
-          const uint32_t code = e8m0_code(amax, pb.dmax);
+          const uint32_t code = e8m0_code_v<SV>(amax, pb.dmax, pb.dmax_inv);
           const float sc = e8m0_to_float(code);
           uint32_t packed = fp4x2<0>(0u, y[it][0][i], y[it][1][i], sc);
           packed = fp4x2<1>(packed, y[it][2][i], y[it][3][i], sc);
-          *reinterpret_cast<uint16_t*>(codes + row * (kW / 2) + 32 * w + 2 * c) = static_cast<uint16_t>(packed);
-          if ((c & 7) == 0) e8[row * (kW / 32) + 2 * w + (c >> 3)] = static_cast<uint8_t>(code);
+          __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(packed), rs_codes, code_off, r0 * (kW / 2), 0);
+          // the 8 lanes of a group hold the same code and all store it (no branch)
+          __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(code), rs_e8, e8_off, r0 * (kW / 32), 0);
         }
     }
   }
@@ -203,12 +217,12 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb,
 //     (8 neighbouring columns) and transposes them in registers (v_perm_b32); MFMA u of a
 //     k-step then takes column 8c + u of the lane's block, so after the 8 MFMAs a lane
 //     holds 8 neighbouring columns of 4 rows: one 4-byte E2M1 run per row, and a 32-group
-//     spans 4 neighbouring lanes.
-template <int DT>
+//     spans 4 neighbouring lanes (a quad).
+template <int DT, int SV>
 __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide1_kernel(Problem pb, Buffers b) {
   __shared__ u32x4_t frag1[kIT * kNChunk * 64];  // 128 KB: P1 A fragments (natural k order)
   __shared__ u32x4_t xs[2][kChunk * 32];         // 2 x 16 KB, row-major 16-byte slots
-  constexpr int D = 4;                    // chunks in flight in registers (divides 8)
+  constexpr int D = 2;                    // chunks in flight in registers (divides 8)
   constexpr int XR = kChunk * kW * 2 / 16 / kWideThreads;  // 16-byte pieces per thread per chunk
 
   const int tid = threadIdx.x;
@@ -219,13 +233,17 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide1_kernel(Problem pb,
   const int64_t stride = gridDim.x;
 
   u32x4_t xr[D][XR];
-  // chunk j of this workgroup: slice blockIdx.x + (j / 8) * gridDim.x, rows 32 * (j % 8)
+  // chunk j of this workgroup: slice blockIdx.x + (j / 8) * gridDim.x, rows 32 * (j % 8).
+  // Bounded buffer loads (zeros past K, no memory access): unconditional, so the
+  // compiler's memory-counter waits cover exactly the chunk being consumed.
   auto load_chunk = [&](int64_t j, u32x4_t* r) {
     const int64_t slice = blockIdx.x + (j >> 3) * stride;
-    if (slice >= pb.K) return;
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(b.x + slice * (kW * kW) + (j & 7) * (kChunk * kW));
+    const bool in = slice < pb.K;
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(b.x + (in ? slice : 0) * (kW * kW) + (j & 7) * (kChunk * kW)),
+        static_cast<int16_t>(0), in ? kChunk * kW * 2 : 0, kBufferWord3);
 #pragma unroll
-    for (int h = 0; h < XR; ++h) r[h] = src[tid + h * kWideThreads];
+    for (int h = 0; h < XR; ++h) r[h] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, tid * 16, h * kWideThreads * 16, 0);
   };
   auto store_chunk = [&](const u32x4_t* r, u32x4_t* dst) {
 #pragma unroll
@@ -240,75 +258,141 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide1_kernel(Problem pb,
 
   int64_t s = blockIdx.x;
   if (s >= pb.K) return;
-  // prologue: chunk 0 in LDS, chunks 1 .. D in registers (chunk k in xr[k % D])
+  // prologue: chunk 0 in LDS, chunks 1 .. D in registers (chunk k in xr[k % D]), issued
+  // in chunk order, so that waiting for one chunk never waits for a later one.
   load_chunk(0, xr[0]);
   store_chunk(xr[0], xs[0]);
 #pragma unroll
-  for (int k = 1; k <= D; ++k) load_chunk(k, xr[k % D]);
-
+  for (int k = 1; k <= D; ++k) {
+    __builtin_amdgcn_sched_barrier(0);
+    load_chunk(k, xr[k % D]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  lds_barrier();  // chunk 0 and P1 are in LDS
   const float dinv = pb.dmax_inv;
   int64_t j0 = 0;  // chunk index of this slice's chunk 0
-  for (; s < pb.K; s += stride, j0 += kNChunk) {
-    f32x4_t y[kIT / 2][8];
-#pragma unroll
-    for (int it = 0; it < kIT / 2; ++it)
-#pragma unroll
-      for (int u = 0; u < 8; ++u) y[it][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t y[kIT / 2][8];
 
+  // The lane's raw B rows of a chunk in LDS: rows 8g .. 8g+7, columns 128sc + 8c .. +7.
+  u32x4_t rows[8];
+  auto read_rows = [&](const u32x4_t* buf) {
 #pragma unroll
-    for (int ch = 0; ch < kNChunk; ++ch) {
-      // chunk ch is in xs[ch & 1]; every wave is done with the other buffer
-      __syncthreads();
-      // chunk ch + 1: registers -> the free buffer; then request chunk ch + 1 + D into
-      // the registers it frees
-      store_chunk(xr[(ch + 1) % D], xs[(ch + 1) & 1]);
-      load_chunk(j0 + ch + 1 + D, xr[(ch + 1) % D]);
+    for (int t = 0; t < 8; ++t) rows[t] = buf[(8 * g + t) * 32 + 16 * sc + c];
+  };
 
-      // B operands: rows 8g .. 8g+7 of the chunk, columns 128sc + 8c .. +7, transposed
-      u32x4_t rows[8];
+  // One chunk of the current slice: y[rows, cols] += P1[rows, chunk] . x[chunk, cols].
+  // On entry `rows` holds this chunk's B rows (read during the previous step).  The step
+  // publishes chunk ch + 1 to LDS, and once every wave has done so reads its rows for the
+  // next step while this chunk's products run.
+  auto chunk_step = [&](auto chv) {
+    constexpr int ch = decltype(chv)::value;
+    // this chunk's B operands, transposed (frees `rows`)
+    u32x4_t bx[8];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) rows[t] = xs[ch & 1][(8 * g + t) * 32 + 16 * sc + c];
-      u32x4_t bx[8];
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t sel = (u & 1) ? 0x07060302u : 0x05040100u;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const uint32_t sel = (u & 1) ? 0x07060302u : 0x05040100u;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          bx[u][q] = __builtin_amdgcn_perm(rows[2 * q + 1][u >> 1], rows[2 * q][u >> 1], sel);
-      }
-#pragma unroll
-      for (int it = 0; it < kIT / 2; ++it) {
-        const u32x4_t a = frag1[((8 * rh + it) * kNChunk + ch) * 64 + lane];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) y[it][u] = mfma16x16x32<DT>(a, bx[u], y[it][u]);
-      }
+      for (int q = 0; q < 4; ++q) bx[u][q] = __builtin_amdgcn_perm(rows[2 * q + 1][u >> 1], rows[2 * q][u >> 1], sel);
     }
-
-    // [FQV2] 第3步 pergroup / 第4步: 32-groups of 4 neighbouring lanes
-    uint8_t* codes = b.codes + s * (kW * kW / 2);
-    uint8_t* e8 = static_cast<uint8_t*>(b.scale) + s * e8m0_bytes_per_slice(kW * kW);
+    // chunk ch + 1: registers -> LDS buffer (ch + 1) & 1, whose previous chunk (ch - 1)
+    // every wave read before the last barrier; then request chunk ch + 1 + D into the
+    // registers it frees
+    store_chunk(xr[(ch + 1) % D], xs[(ch + 1) & 1]);
+    load_chunk(j0 + ch + 1 + D, xr[(ch + 1) % D]);
+    lds_barrier();  // chunk ch + 1 is in LDS; chunk ch's buffer is no longer read
+    // (the next slice's first rows are read after the epilogue, so that they are not
+    // held in registers across it)
+    if constexpr (ch + 1 < kNChunk) read_rows(xs[(ch + 1) & 1]);
+    // products, with each P1 fragment fetched one row tile ahead
+    u32x4_t a = frag1[((8 * rh) * kNChunk + ch) * 64 + lane];
 #pragma unroll
-    for (int it = 0; it < kIT / 2; ++it)
+    for (int it = 0; it < kIT / 2; ++it) {
+      const u32x4_t an = frag1[((8 * rh + (it + 1 < kIT / 2 ? it + 1 : it)) * kNChunk + ch) * 64 + lane];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) y[it][u] = mfma16x16x32<DT>(a, bx[u], y[it][u]);
+      a = an;
+    }
+  };
+
+  // [FQV2] 第3步 pergroup / 第4步 for the current slice: 32-groups of 4 neighbouring
+  // lanes (a quad).  Stores through buffer resources of the slice: a per-lane offset
+  // (opaque per slice, so no per-row address is hoisted and held in registers) plus the
+  // row as a scalar offset.  A row's four e8m0 bytes (one per quad) are gathered into
+  // one dword, so each 16-row tile costs one e8m0 store instead of four.
+  auto epilogue = [&]() {
+    const auto rs_codes = __builtin_amdgcn_make_buffer_rsrc(b.codes + s * (kW * kW / 2), static_cast<int16_t>(0),
+                                                            kW * kW / 2, kBufferWord3);
+    const auto rs_e8 = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<uint8_t*>(b.scale) + s * e8m0_bytes_per_slice(kW * kW), static_cast<int16_t>(0),
+        static_cast<int>(e8m0_bytes_per_slice(kW * kW)), kBufferWord3);
+    const int j = c & 3, k = c >> 2;  // lane in its quad, quad (= group) in the row
+    int code_off = (128 * rh + 4 * g) * (kW / 2) + 64 * sc + 4 * c;
+    int e8_off = (128 * rh + 4 * g + j) * (kW / 32) + 4 * sc;  // the dword of row 4g + j
+    asm volatile("" : "+v"(code_off), "+v"(e8_off));
+#pragma unroll
+    for (int it = 0; it < kIT / 2; ++it) {
+      uint32_t codes4[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = 128 * rh + 16 * it + 4 * g + i;
+        const int r0 = 16 * it + i;  // row - 128rh - 4g
         float amax = 0.0f;
 #pragma unroll
         for (int u = 0; u < 8; ++u) amax = fmaxf(amax, __builtin_fabsf(y[it][u][i]));
         amax = group_max<4>(amax);
-        const uint32_t code = e8m0_code_fast(amax, pb.dmax, dinv);
+        const uint32_t code = e8m0_code_v<SV>(amax, pb.dmax, dinv);
+        codes4[i] = code;
         const float scf = e8m0_to_float(code);
         uint32_t packed = fp4x2<0>(0u, y[it][0][i], y[it][1][i], scf);
         packed = fp4x2<1>(packed, y[it][2][i], y[it][3][i], scf);
         packed = fp4x2<2>(packed, y[it][4][i], y[it][5][i], scf);
         packed = fp4x2<3>(packed, y[it][6][i], y[it][7][i], scf);
-        *reinterpret_cast<uint32_t*>(codes + row * (kW / 2) + 64 * sc + 4 * c) = packed;
-        if ((c & 3) == 0) e8[row * (kW / 32) + 4 * sc + (c >> 2)] = static_cast<uint8_t>(code);
+        __builtin_amdgcn_raw_buffer_store_b32(packed, rs_codes, code_off, r0 * (kW / 2), 0);
       }
+      // lane (k, j) takes row 4g + j's code of group k, places it at byte k, and ORs in
+      // the other three quads' bytes (rotations by 4, 8, 12 lanes reach all of them)
+      const uint32_t all4 = codes4[0] | (codes4[1] << 8) | (codes4[2] << 16) | (codes4[3] << 24);
+      const uint32_t mine = __builtin_amdgcn_ubfe(all4, 8 * j, 8) << (8 * k);
+      const uint32_t row4 = mine | dpp_u<kDppRowRor4>(mine) | dpp_u<kDppRowRor8>(mine) | dpp_u<kDppRowRor12>(mine);
+      // the four lanes of row 4g + j hold the same dword and all store it (no branch)
+      __builtin_amdgcn_raw_buffer_store_b32(row4, rs_e8, e8_off, 16 * it * (kW / 32), 0);
+    }
+  };
+
+  auto zero_y = [&]() {
+#pragma unroll
+    for (int it = 0; it < kIT / 2; ++it)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) y[it][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  };
+
+  // The slice loop is rotated to start at chunk 4: the loop head's waits see the same
+  // loads in flight on entry and on every later pass, while the waits right after the
+  // epilogue's stores sit inside the body where they are counted exactly.
+  zero_y();
+  read_rows(xs[0]);
+  chunk_step(std::integral_constant<int, 0>{});
+  chunk_step(std::integral_constant<int, 1>{});
+  chunk_step(std::integral_constant<int, 2>{});
+  chunk_step(std::integral_constant<int, 3>{});
+  while (true) {
+    chunk_step(std::integral_constant<int, 4>{});
+    chunk_step(std::integral_constant<int, 5>{});
+    chunk_step(std::integral_constant<int, 6>{});
+    chunk_step(std::integral_constant<int, 7>{});
+    epilogue();
+    s += stride;
+    j0 += kNChunk;
+    if (s >= pb.K) break;
+    zero_y();
+    read_rows(xs[0]);
+    chunk_step(std::integral_constant<int, 0>{});
+    chunk_step(std::integral_constant<int, 1>{});
+    chunk_step(std::integral_constant<int, 2>{});
+    chunk_step(std::integral_constant<int, 3>{});
   }
 }
 
-template <int DT>
+template <int DT, int SV>
 hipError_t launch_w1(const Problem& pb, const Buffers& b, hipStream_t s) {
   static int cus = 0;
   if (cus == 0) {
@@ -318,11 +402,11 @@ hipError_t launch_w1(const Problem& pb, const Buffers& b, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   const int grid = static_cast<int>(pb.K < cus ? pb.K : cus);
-  mfma_wide1_kernel<DT><<<grid, kWideThreads, 0, s>>>(pb, b);
+  mfma_wide1_kernel<DT, SV><<<grid, kWideThreads, 0, s>>>(pb, b);
   return hipGetLastError();
 }
 
-template <int DT, bool PG, bool CLAMP>
+template <int DT, bool PG, bool CLAMP, int SV>
 hipError_t launch_w2(const Problem& pb, const Buffers& b, hipStream_t s) {
   static int cus = 0;
   if (cus == 0) {
@@ -332,15 +416,30 @@ hipError_t launch_w2(const Problem& pb, const Buffers& b, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   const int grid = static_cast<int>(pb.K < cus ? pb.K : cus);
-  mfma_wide2_kernel<DT, PG, CLAMP><<<grid, kWideThreads, 0, s>>>(pb, b);
+  mfma_wide2_kernel<DT, PG, CLAMP, SV><<<grid, kWideThreads, 0, s>>>(pb, b);
   return hipGetLastError();
 }
 
 template <int DT>
 hipError_t dispatch_w2(const Problem& pb, const Buffers& b, hipStream_t s) {
-  if (pb.mode == kPerGroupFp4) return launch_w2<DT, true, false>(pb, b, s);
-  if (pb.d >= 7.4999f) return launch_w2<DT, false, true>(pb, b, s);
-  return launch_w2<DT, false, false>(pb, b, s);
+  if (pb.mode == kPerGroupFp4) {
+    switch (e8m0_variant(pb)) {
+      case kE8V1: return launch_w2<DT, true, false, kE8V1>(pb, b, s);
+      case kE8V2Pow2: return launch_w2<DT, true, false, kE8V2Pow2>(pb, b, s);
+      default: return launch_w2<DT, true, false, kE8V2Div>(pb, b, s);
+    }
+  }
+  if (pb.d >= 7.4999f) return launch_w2<DT, false, true, kE8V1>(pb, b, s);
+  return launch_w2<DT, false, false, kE8V1>(pb, b, s);
+}
+
+template <int DT>
+hipError_t dispatch_w1(const Problem& pb, const Buffers& b, hipStream_t s) {
+  switch (e8m0_variant(pb)) {
+    case kE8V1: return launch_w1<DT, kE8V1>(pb, b, s);
+    case kE8V2Pow2: return launch_w1<DT, kE8V2Pow2>(pb, b, s);
+    default: return launch_w1<DT, kE8V2Div>(pb, b, s);
+  }
 }
 
 }  // namespace
@@ -351,7 +450,7 @@ bool mfma_wide_supports(const Problem& pb) {
 
 hipError_t launch_mfma_wide(const Problem& pb, const Buffers& b, hipStream_t s) {
   if (!mfma_wide_supports(pb)) return hipErrorNotSupported;
-  if (!pb.two_sided) return pb.dtype == kBF16 ? launch_w1<kBF16>(pb, b, s) : launch_w1<kF16>(pb, b, s);
+  if (!pb.two_sided) return pb.dtype == kBF16 ? dispatch_w1<kBF16>(pb, b, s) : dispatch_w1<kF16>(pb, b, s);
   return pb.dtype == kBF16 ? dispatch_w2<kBF16>(pb, b, s) : dispatch_w2<kF16>(pb, b, s);
 }
 
