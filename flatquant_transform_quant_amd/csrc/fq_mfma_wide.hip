@@ -208,34 +208,47 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb,
 
 // ---------------------------------------------------------------------------------------
 // Left-only 256 x 256 slices (P2 = [0, 0], per-group mode): y = P1 . x.
-//   * x moves HBM -> registers -> LDS in chunks of 32 rows (16 KB): four chunks (64 KB per
-//     CU) are in flight in registers while one is in LDS being used and the next is
-//     written to the other LDS buffer, so the HBM stream never waits on the products;
+//   * 8 waves per workgroup, two per SIMD, one workgroup per CU; wave w computes rows
+//     64*(w&3) .. +63 of columns 128*(w>>2) .. +127, so its part of y is 128 fp32 per lane
+//     and stays in ordinary registers (the epilogue reads it without moving it out of
+//     accumulation registers), and each SIMD has a second wave to run while one waits;
 //   * P1 is staged once in LDS as A fragments in natural k order (128 KB);
-//   * wave w computes rows 128*(w&1) .. +127 of columns 128*(w>>1) .. +127.  x is the B
-//     operand with the contraction over rows, so each lane reads 8 rows x 16 bytes
-//     (8 neighbouring columns) and transposes them in registers (v_perm_b32); MFMA u of a
-//     k-step then takes column 8c + u of the lane's block, so after the 8 MFMAs a lane
-//     holds 8 neighbouring columns of 4 rows: one 4-byte E2M1 run per row, and a 32-group
-//     spans 4 neighbouring lanes (a quad).
+//   * x streams HBM -> registers -> LDS in chunks of 32 rows (16 KB), two chunks ahead in
+//     registers.  x is the B operand with the contraction over rows, so a lane needs 8
+//     rows of one column: the transpose is done once per chunk, as it is written to LDS.
+//     Thread (r, j) loads rows 2r and 2r+1, columns 8j .. 8j+7, pairs the two rows of each
+//     column in one dword (v_perm_b32), and writes the 8 dwords to the places of the B
+//     fragments (u, lane, q) they belong to; every wave then reads its operands with plain
+//     16-byte reads.  MFMA u of a k-step takes column 8c + u of the lane's block, so after
+//     the 8 MFMAs a lane holds 8 neighbouring columns of 4 rows: one 4-byte E2M1 run per
+//     row, and a 32-group spans 4 neighbouring lanes (a quad).
+constexpr int kLeftWaves = 8;
+constexpr int kLeftThreads = 64 * kLeftWaves;
+
 template <int DT, int SV>
-__global__ __launch_bounds__(kWideThreads, 1) void mfma_wide1_kernel(Problem pb, Buffers b) {
+__global__ __launch_bounds__(kLeftThreads, 1) void mfma_wide1_kernel(Problem pb, Buffers b) {
   __shared__ u32x4_t frag1[kIT * kNChunk * 64];  // 128 KB: P1 A fragments (natural k order)
-  __shared__ u32x4_t xs[2][kChunk * 32];         // 2 x 16 KB, row-major 16-byte slots
-  constexpr int D = 2;                    // chunks in flight in registers (divides 8)
-  constexpr int XR = kChunk * kW * 2 / 16 / kWideThreads;  // 16-byte pieces per thread per chunk
+  // 2 x 16 KB: one chunk as B fragments, xs[buf][(sc*8 + u)*64 + 16g + c] element q = rows
+  // 8g + 2q, 8g + 2q + 1 of column 128sc + 8c + u
+  __shared__ u32x4_t xs[2][kChunk * 32];
+  constexpr int D = 2;                           // chunks in flight in registers (divides 8)
+  constexpr int XR = kChunk * kW * 2 / 16 / kLeftThreads;  // 16-byte pieces per thread per chunk
+  constexpr int RT = 4;                          // 16-row tiles per wave
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, g = lane >> 4;
-  const int rh = w & 1, sc = w >> 1;  // row half, column half
+  const int rq = w & 3, sc = w >> 2;  // row quarter, column half
   const int64_t stride = gridDim.x;
 
   u32x4_t xr[D][XR];
-  // chunk j of this workgroup: slice blockIdx.x + (j / 8) * gridDim.x, rows 32 * (j % 8).
-  // Bounded buffer loads (zeros past K, no memory access): unconditional, so the
-  // compiler's memory-counter waits cover exactly the chunk being consumed.
+  // This thread's pieces of chunk j of the workgroup (slice blockIdx.x + (j / 8) *
+  // gridDim.x, x rows 32 * (j % 8) + 2r and 2r + 1, columns 8jj .. 8jj+7, where
+  // r = tid / 32, jj = tid % 32).  Bounded buffer loads (zeros past K, no memory access):
+  // unconditional, so the compiler's memory-counter waits cover exactly the chunk
+  // being consumed.
+  const int pr = tid >> 5, pj = tid & 31;
   auto load_chunk = [&](int64_t j, u32x4_t* r) {
     const int64_t slice = blockIdx.x + (j >> 3) * stride;
     const bool in = slice < pb.K;
@@ -243,14 +256,22 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide1_kernel(Problem pb,
         const_cast<uint16_t*>(b.x + (in ? slice : 0) * (kW * kW) + (j & 7) * (kChunk * kW)),
         static_cast<int16_t>(0), in ? kChunk * kW * 2 : 0, kBufferWord3);
 #pragma unroll
-    for (int h = 0; h < XR; ++h) r[h] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, tid * 16, h * kWideThreads * 16, 0);
+    for (int h = 0; h < XR; ++h)
+      r[h] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, ((2 * pr) * kW + 8 * pj) * 2, h * kW * 2, 0);
   };
+  // pair rows 2r, 2r+1 per column and write each dword to its fragment place:
+  // column n = 8jj + e -> sc = jj / 16, c = jj % 16, u = e; row pair 2r -> g = r / 4, q = r % 4
+  const int st_base = ((pj >> 4) * 8 * 64 + (pr >> 2) * 16 + (pj & 15)) * 4 + (pr & 3);
   auto store_chunk = [&](const u32x4_t* r, u32x4_t* dst) {
+    uint32_t* d32 = reinterpret_cast<uint32_t*>(dst);
 #pragma unroll
-    for (int h = 0; h < XR; ++h) dst[tid + h * kWideThreads] = r[h];
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      d32[st_base + e * 64 * 4] = __builtin_amdgcn_perm(r[1][e >> 1], r[0][e >> 1], sel);
+    }
   };
   // P1[i, 32ch + 8gg .. +7] -> frag1[(it*8 + ch)*64 + 16*gg + i%16]
-  for (int q = tid; q < kW * kW / 8; q += kWideThreads) {
+  for (int q = tid; q < kW * kW / 8; q += kLeftThreads) {
     const int i = q >> 5, m0 = (q & 31) * 8;
     const int it = i >> 4, ch = m0 >> 5, gg = (m0 & 31) >> 3;
     frag1[(it * kNChunk + ch) * 64 + 16 * gg + (i & 15)] = reinterpret_cast<const u32x4_t*>(b.p1)[q];
@@ -268,49 +289,33 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide1_kernel(Problem pb,
     load_chunk(k, xr[k % D]);
   }
   __builtin_amdgcn_sched_barrier(0);
-  lds_barrier();  // chunk 0 and P1 are in LDS
+
   const float dinv = pb.dmax_inv;
   int64_t j0 = 0;  // chunk index of this slice's chunk 0
-  f32x4_t y[kIT / 2][8];
-
-  // The lane's raw B rows of a chunk in LDS: rows 8g .. 8g+7, columns 128sc + 8c .. +7.
-  u32x4_t rows[8];
-  auto read_rows = [&](const u32x4_t* buf) {
-#pragma unroll
-    for (int t = 0; t < 8; ++t) rows[t] = buf[(8 * g + t) * 32 + 16 * sc + c];
-  };
+  f32x4_t y[RT][8];
 
   // One chunk of the current slice: y[rows, cols] += P1[rows, chunk] . x[chunk, cols].
-  // On entry `rows` holds this chunk's B rows (read during the previous step).  The step
-  // publishes chunk ch + 1 to LDS, and once every wave has done so reads its rows for the
-  // next step while this chunk's products run.
   auto chunk_step = [&](auto chv) {
     constexpr int ch = decltype(chv)::value;
-    // this chunk's B operands, transposed (frees `rows`)
-    u32x4_t bx[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const uint32_t sel = (u & 1) ? 0x07060302u : 0x05040100u;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) bx[u][q] = __builtin_amdgcn_perm(rows[2 * q + 1][u >> 1], rows[2 * q][u >> 1], sel);
-    }
-    // chunk ch + 1: registers -> LDS buffer (ch + 1) & 1, whose previous chunk (ch - 1)
-    // every wave read before the last barrier; then request chunk ch + 1 + D into the
-    // registers it frees
+    // chunk ch is in xs[ch & 1]; every wave is done with the other buffer
+    lds_barrier();
+    // chunk ch + 1: registers -> the free buffer; then request chunk ch + 1 + D into
+    // the registers it frees
     store_chunk(xr[(ch + 1) % D], xs[(ch + 1) & 1]);
     load_chunk(j0 + ch + 1 + D, xr[(ch + 1) % D]);
-    lds_barrier();  // chunk ch + 1 is in LDS; chunk ch's buffer is no longer read
-    // (the next slice's first rows are read after the epilogue, so that they are not
-    // held in registers across it)
-    if constexpr (ch + 1 < kNChunk) read_rows(xs[(ch + 1) & 1]);
-    // products, with each P1 fragment fetched one row tile ahead
-    u32x4_t a = frag1[((8 * rh) * kNChunk + ch) * 64 + lane];
+
+    u32x4_t a[RT];
 #pragma unroll
-    for (int it = 0; it < kIT / 2; ++it) {
-      const u32x4_t an = frag1[((8 * rh + (it + 1 < kIT / 2 ? it + 1 : it)) * kNChunk + ch) * 64 + lane];
+    for (int it = 0; it < RT; ++it) a[it] = frag1[((RT * rq + it) * kNChunk + ch) * 64 + lane];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) y[it][u] = mfma16x16x32<DT>(a, bx[u], y[it][u]);
-      a = an;
+    for (int half = 0; half < 2; ++half) {
+      u32x4_t bx[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) bx[u] = xs[ch & 1][(sc * 8 + 4 * half + u) * 64 + lane];
+#pragma unroll
+      for (int it = 0; it < RT; ++it)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) y[it][4 * half + u] = mfma16x16x32<DT>(a[it], bx[u], y[it][4 * half + u]);
     }
   };
 
@@ -326,15 +331,15 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide1_kernel(Problem pb,
         static_cast<uint8_t*>(b.scale) + s * e8m0_bytes_per_slice(kW * kW), static_cast<int16_t>(0),
         static_cast<int>(e8m0_bytes_per_slice(kW * kW)), kBufferWord3);
     const int j = c & 3, k = c >> 2;  // lane in its quad, quad (= group) in the row
-    int code_off = (128 * rh + 4 * g) * (kW / 2) + 64 * sc + 4 * c;
-    int e8_off = (128 * rh + 4 * g + j) * (kW / 32) + 4 * sc;  // the dword of row 4g + j
+    int code_off = (64 * rq + 4 * g) * (kW / 2) + 64 * sc + 4 * c;
+    int e8_off = (64 * rq + 4 * g + j) * (kW / 32) + 4 * sc;  // the dword of row 4g + j
     asm volatile("" : "+v"(code_off), "+v"(e8_off));
 #pragma unroll
-    for (int it = 0; it < kIT / 2; ++it) {
+    for (int it = 0; it < RT; ++it) {
       uint32_t codes4[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r0 = 16 * it + i;  // row - 128rh - 4g
+        const int r0 = 16 * it + i;  // row - 64rq - 4g
         float amax = 0.0f;
 #pragma unroll
         for (int u = 0; u < 8; ++u) amax = fmaxf(amax, __builtin_fabsf(y[it][u][i]));
@@ -360,7 +365,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide1_kernel(Problem pb,
 
   auto zero_y = [&]() {
 #pragma unroll
-    for (int it = 0; it < kIT / 2; ++it)
+    for (int it = 0; it < RT; ++it)
 #pragma unroll
       for (int u = 0; u < 8; ++u) y[it][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   };
@@ -369,7 +374,6 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide1_kernel(Problem pb,
   // loads in flight on entry and on every later pass, while the waits right after the
   // epilogue's stores sit inside the body where they are counted exactly.
   zero_y();
-  read_rows(xs[0]);
   chunk_step(std::integral_constant<int, 0>{});
   chunk_step(std::integral_constant<int, 1>{});
   chunk_step(std::integral_constant<int, 2>{});
@@ -384,7 +388,6 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide1_kernel(Problem pb,
     j0 += kNChunk;
     if (s >= pb.K) break;
     zero_y();
-    read_rows(xs[0]);
     chunk_step(std::integral_constant<int, 0>{});
     chunk_step(std::integral_constant<int, 1>{});
     chunk_step(std::integral_constant<int, 2>{});
@@ -402,7 +405,7 @@ hipError_t launch_w1(const Problem& pb, const Buffers& b, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   const int grid = static_cast<int>(pb.K < cus ? pb.K : cus);
-  mfma_wide1_kernel<DT, SV><<<grid, kWideThreads, 0, s>>>(pb, b);
+  mfma_wide1_kernel<DT, SV><<<grid, kLeftThreads, 0, s>>>(pb, b);
   return hipGetLastError();
 }
 
