@@ -21,6 +21,7 @@
 #include <hip/hip_runtime.h>
 
 #include "fq_mfma_common.h"
+#include "fq_mfma_pstage.h"
 
 namespace fq {
 namespace {
@@ -86,30 +87,12 @@ __global__ __launch_bounds__(kSmallThreads, 2) void mfma_small_kernel(Problem pb
                                                                 16 * mt * N * 2, 0);
   };
   // ---- stage P2 / P1 fragments (once per workgroup) ----
-  // All coalesced 16-byte loads of P1 and P2 are issued first (one memory latency), then
-  // each 2-byte value is written to its fragment slot:
-  //   P2[j, n]  -> frag2[(ks*NT + nt)*64 + 16*g + c], element t   (j = 32ks + 8g + t, n = R*c + nt)
-  //   P1[i, m]  -> frag1[(it*KS2 + ks2)*64 + 16*g + i%16], element t, where m = 32ks2 + w and
-  //                w = 4g + t (t < 4) or 16 + 4g + (t - 4) (t >= 4)
   // The P loads go first and the x loads of the first slices right after them, so the
-  // staging below waits for P alone (the memory counter completes in issue order) while
-  // x is still arriving.  Chunks past the end of P1/P2 (or all of P2 when it is empty)
-  // read zeros through bounded buffer resources, so no load is conditional.
+  // staging waits for P alone (the memory counter completes in issue order) while x is
+  // still arriving.
   {
-    constexpr int C2 = N * N / 8, C1 = M * M / 8;  // 16-byte chunks of P2 and P1
-    constexpr int L2 = (C2 + kSmallThreads - 1) / kSmallThreads;
-    constexpr int L1 = (C1 + kSmallThreads - 1) / kSmallThreads;
-    u32x4_t r2[L2], r1[L1];
-    const bool two = pb.two_sided != 0;
-    const auto rs2 = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(two ? b.p2 : b.p1),
-                                                      static_cast<int16_t>(0), two ? N * N * 2 : 0,
-                                                      kBufferWord3);
-    const auto rs1 = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(b.p1), static_cast<int16_t>(0),
-                                                      M * M * 2, kBufferWord3);
-#pragma unroll
-    for (int q = 0; q < L2; ++q) r2[q] = __builtin_amdgcn_raw_buffer_load_b128(rs2, (tid + q * kSmallThreads) * 16, 0, 0);
-#pragma unroll
-    for (int q = 0; q < L1; ++q) r1[q] = __builtin_amdgcn_raw_buffer_load_b128(rs1, (tid + q * kSmallThreads) * 16, 0, 0);
+    PStage<DT, M, N, kSmallThreads> ps;
+    ps.issue(pb, b, tid);
     __builtin_amdgcn_sched_barrier(0);  // keep the issue order: P, then x
     // With two slices in flight their loads are issued now, overlapping the staging; with
     // one (large slices) registers are too short and the load waits for the slice loop.
@@ -121,56 +104,7 @@ __global__ __launch_bounds__(kSmallThreads, 2) void mfma_small_kernel(Problem pb
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    uint16_t* f2 = reinterpret_cast<uint16_t*>(frag2);
-    uint16_t* f1 = reinterpret_cast<uint16_t*>(frag1);
-    if (two) {
-#pragma unroll
-      for (int q = 0; q < L2; ++q) {
-        const int ch = tid + q * kSmallThreads;
-        if (ch < C2) {
-          const int j = ch / (N / 8), n0 = (ch % (N / 8)) * 8;
-          const int ks = j >> 5, gg = (j >> 3) & 3, t = j & 7;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int n = n0 + e, cc = n / R, nt = n % R;
-            f2[((ks * NT + nt) * 64 + 16 * gg + cc) * 8 + t] =
-                static_cast<uint16_t>(r2[q][e >> 1] >> (16 * (e & 1)));
-          }
-        }
-      }
-    } else {
-      // an empty P2 is run as the identity
-      const uint16_t one = DT == kBF16 ? uint16_t(0x3F80) : uint16_t(0x3C00);
-      for (int idx = tid; idx < KS1 * NT * 64; idx += kSmallThreads) {
-        const int l = idx & 63, f = idx >> 6, ks = f / NT, nt = f % NT;
-        const int n = R * (l & 15) + nt, j0 = 32 * ks + 8 * (l >> 4);
-        uint32_t w[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p)
-          w[p] = uint32_t(j0 + 2 * p == n ? one : 0) | (uint32_t(j0 + 2 * p + 1 == n ? one : 0) << 16);
-        frag2[idx] = u32x4_t{w[0], w[1], w[2], w[3]};
-      }
-    }
-    // P1 columns beyond M (M = 16: the second half of the k-step) hold zeros
-    if (M < 32)
-      for (int idx = tid; idx < MT * KS2 * 64; idx += kSmallThreads) frag1[idx] = u32x4_t{0u, 0u, 0u, 0u};
-    if (M < 32) lds_barrier();
-#pragma unroll
-    for (int q = 0; q < L1; ++q) {
-      const int ch = tid + q * kSmallThreads;
-      if (ch < C1) {
-        const int i = ch / (M / 8), m0 = (ch % (M / 8)) * 8;
-        const int it = i >> 4, r = i & 15;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int m = m0 + e, ks2 = m >> 5, w = m & 31;
-          const int gg = w < 16 ? (w >> 2) : ((w - 16) >> 2);
-          const int t = w < 16 ? (w & 3) : 4 + ((w - 16) & 3);
-          f1[((it * KS2 + ks2) * 64 + 16 * gg + r) * 8 + t] =
-              static_cast<uint16_t>(r1[q][e >> 1] >> (16 * (e & 1)));
-        }
-      }
-    }
+    ps.scatter(pb, frag2, frag1, tid);
   }
   lds_barrier();
   if (s >= pb.K) return;

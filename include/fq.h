@@ -130,8 +130,8 @@ void fq_executor_destroy(fq_executor* executor);
 fq_status fq_executor_set_repeatable(fq_executor* executor, int32_t repeat);
 
 /* Kernel variant the executor will launch: 0 = the automatic choice, 1 = the generic
- * kernel (any shape), 2 = the small-slice MFMA kernel, 3 = the whole-workgroup MFMA
- * kernel for 256-class slices.  Selecting a variant that does not support the planned
+ * kernel (any shape), 2 = the small-slice MFMA kernel (one wave per slice), 3 = the
+ * whole-workgroup MFMA kernel for 256-class slices.  Selecting a variant that does not support the planned
  * problem returns FQ_ERR_PARAM_INVALID and leaves the executor unchanged.  Meant for
  * tests and benchmarks. */
 fq_status fq_executor_set_kernel(fq_executor* executor, int32_t variant);
