@@ -93,9 +93,18 @@ def cpu_baseline(w, x_host, p1, p2, budget_s: float = 10.0):
         dt = time.perf_counter() - t
     else:
         n, dt = n0, dt0
-    elems = n * w.M * w.N
+    # the whole workload takes less than the budget: repeat passes over it
+    reps = 1
+    if n == w.K and dt < 0.5 * budget_s:
+        reps = max(1, min(200, int(budget_s / max(dt, 1e-6))))
+        t = time.perf_counter()
+        for _ in range(reps):
+            oracle.run_codes_only(x_host, p1, p2, w.dtype, w.mode, w.clip_ratio, w.dst_type_max, threads)
+        dt = time.perf_counter() - t
+    elems = reps * n * w.M * w.N
+    what = f"{reps} passes over all {w.K} slices" if reps > 1 else f"first {n} of {w.K} slices"
     return {"value": elems / dt / 1e9, "unit": "Gelem/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n} of {w.K} slices ({elems} elements), {dt:.2f} s wall on {threads} threads"}
+            "sample": f"{what} ({elems} elements), {dt:.2f} s wall on {threads} threads"}
 
 
 def main() -> int:
