@@ -2,7 +2,7 @@
 //
 //   P2[j, n]  -> frag2[(ks*NT + nt)*64 + 16*g + c], element t   (j = 32ks + 8g + t, n = R*c + nt)
 //   P1[i, m]  -> frag1[(it*KS2 + ks2)*64 + 16*g + i%16], element t, where m = 32ks2 + w and
-//                w = 4g + t (t < 4) or 16 + 4g + (t - 4) (t >= 4)
+//                w = 4g + t (t < 4) or 16 + 4g + (t - 4) (t >= 4); columns past M are zero
 //
 // P2's layout makes it GEMM1's B operand with output column R*c + nt in lane c of n-tile
 // nt; P1's relabels the contraction index m so that GEMM1's accumulator registers are
@@ -17,42 +17,85 @@ namespace fq {
 template <int DT, int M, int N, int THREADS>
 struct PStage {
   static constexpr int MT = M / 16, NT = N / 16, R = N / 16, KS1 = N / 32, KS2 = (M + 31) / 32;
-  static constexpr int C2 = N * N / 8, C1 = M * M / 8;  // 16-byte chunks of P2 and P1
-  static constexpr int L2 = (C2 + THREADS - 1) / THREADS;
-  static constexpr int L1 = (C1 + THREADS - 1) / THREADS;
   static constexpr int FRAG2 = KS1 * NT * 64, FRAG1 = MT * KS2 * 64;  // u32x4 slots
-  u32x4_t r2[L2], r1[L1];
+  // P2 goes by 8x8 blocks (rows 32ks + 8g .. +7, columns 8cb .. 8cb+7): one thread loads
+  // the block's 8 rows (16 bytes each), pairs the rows of each column with v_perm_b32 and
+  // writes the 8 columns as 8 whole fragments.
+  static constexpr int B2 = (N / 8) * (N / 8);          // blocks of P2
+  static constexpr int L2 = (B2 + THREADS - 1) / THREADS;
+  // A P1 fragment is two 8-byte pieces of one row of P1 (its 8 relabelled k-slots are
+  // columns 32ks2 + 4g .. +3 and 32ks2 + 16 + 4g .. +3).
+  static constexpr int L1 = (FRAG1 + THREADS - 1) / THREADS;
+  u32x4_t r2[L2][8];
+  uint32_t r1[L1][4];
 
-  // All coalesced 16-byte loads of P1 and P2 (one memory latency).  Chunks past the end
-  // (or all of P2 when it is empty) read zeros through bounded buffer resources, so no
-  // load is conditional.
+  // The loads (one memory latency each for P2 and P1).  Loads past the end of P1/P2 (or
+  // all of P2 when it is empty) read zeros through bounded buffer resources, so no load
+  // is conditional.
   __device__ __forceinline__ void issue(const Problem& pb, const Buffers& b, int tid) {
+    issue_p2(pb, b, tid);
+    issue_p1(b, tid);
+  }
+  __device__ __forceinline__ void issue_p2(const Problem& pb, const Buffers& b, int tid) {
+    // the staging's own copy of the thread index: its lane arithmetic is not shared with
+    // (and kept live for) the kernel's slice loop
+    asm volatile("" : "+v"(tid));
     const bool two = pb.two_sided != 0;
     const auto rs2 = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(two ? b.p2 : b.p1),
                                                       static_cast<int16_t>(0), two ? N * N * 2 : 0, kBufferWord3);
+#pragma unroll
+    for (int q = 0; q < L2; ++q) {
+      const int blk = tid + q * THREADS;
+      const int rb = blk / (N / 8), cb = blk % (N / 8);  // rows 8rb .. +7, columns 8cb .. +7
+      const int off = blk < B2 ? ((8 * rb) * N + 8 * cb) * 2 : N * N * 2;  // past the end: zeros
+#pragma unroll
+      for (int t = 0; t < 8; ++t) r2[q][t] = __builtin_amdgcn_raw_buffer_load_b128(rs2, off + t * N * 2, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void issue_p1(const Buffers& b, int tid) {
+    asm volatile("" : "+v"(tid));
     const auto rs1 = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(b.p1), static_cast<int16_t>(0),
                                                       M * M * 2, kBufferWord3);
 #pragma unroll
-    for (int q = 0; q < L2; ++q) r2[q] = __builtin_amdgcn_raw_buffer_load_b128(rs2, (tid + q * THREADS) * 16, 0, 0);
-#pragma unroll
-    for (int q = 0; q < L1; ++q) r1[q] = __builtin_amdgcn_raw_buffer_load_b128(rs1, (tid + q * THREADS) * 16, 0, 0);
+    for (int q = 0; q < L1; ++q) {
+      const int slot = tid + q * THREADS;
+      const int l = slot & 63, f = slot >> 6, it = f / KS2, ks2 = f % KS2;
+      const int i = 16 * it + (l & 15), gg = l >> 4;
+      const int m0 = 32 * ks2 + 4 * gg, m1 = m0 + 16;
+      const bool in = slot < FRAG1;
+      const int o0 = in ? (i * M + m0) * 2 : M * M * 2;
+      const int o1 = (in && m1 < M) ? (i * M + m1) * 2 : M * M * 2;  // columns past M are zero
+      const auto v0 = __builtin_amdgcn_raw_buffer_load_b64(rs1, o0, 0, 0);
+      const auto v1 = __builtin_amdgcn_raw_buffer_load_b64(rs1, o1, 0, 0);
+      r1[q][0] = v0[0];
+      r1[q][1] = v0[1];
+      r1[q][2] = v1[0];
+      r1[q][3] = v1[1];
+    }
   }
 
-  // Each 2-byte value to its fragment slot; the caller puts a barrier after this.
+  // Fragments to LDS; the caller puts a barrier after this.
   __device__ __forceinline__ void scatter(const Problem& pb, u32x4_t* frag2, u32x4_t* frag1, int tid) {
-    uint16_t* f2 = reinterpret_cast<uint16_t*>(frag2);
-    uint16_t* f1 = reinterpret_cast<uint16_t*>(frag1);
+    scatter_p2(pb, frag2, tid);
+    scatter_p1(frag1, tid);
+  }
+  __device__ __forceinline__ void scatter_p2(const Problem& pb, u32x4_t* frag2, int tid) {
+    asm volatile("" : "+v"(tid));
     if (pb.two_sided != 0) {
 #pragma unroll
       for (int q = 0; q < L2; ++q) {
-        const int ch = tid + q * THREADS;
-        if (ch < C2) {
-          const int j = ch / (N / 8), n0 = (ch % (N / 8)) * 8;
-          const int ks = j >> 5, gg = (j >> 3) & 3, t = j & 7;
+        const int blk = tid + q * THREADS;
+        if (blk < B2) {
+          const int rb = blk / (N / 8), cb = blk % (N / 8);
+          const int ks = rb >> 2, gg = rb & 3;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const int n = n0 + e, cc = n / R, nt = n % R;
-            f2[((ks * NT + nt) * 64 + 16 * gg + cc) * 8 + t] = static_cast<uint16_t>(r2[q][e >> 1] >> (16 * (e & 1)));
+            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+            u32x4_t v;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) v[p] = __builtin_amdgcn_perm(r2[q][2 * p + 1][e >> 1], r2[q][2 * p][e >> 1], sel);
+            const int n = 8 * cb + e, cc = n / R, nt = n % R;
+            frag2[(ks * NT + nt) * 64 + 16 * gg + cc] = v;
           }
         }
       }
@@ -69,25 +112,13 @@ struct PStage {
         frag2[idx] = u32x4_t{w[0], w[1], w[2], w[3]};
       }
     }
-    // P1 columns beyond M (M = 16: the second half of the k-step) hold zeros
-    if (M < 32) {
-      for (int idx = tid; idx < FRAG1; idx += THREADS) frag1[idx] = u32x4_t{0u, 0u, 0u, 0u};
-      lds_barrier();
-    }
+  }
+  __device__ __forceinline__ void scatter_p1(u32x4_t* frag1, int tid) {
+    asm volatile("" : "+v"(tid));
 #pragma unroll
     for (int q = 0; q < L1; ++q) {
-      const int ch = tid + q * THREADS;
-      if (ch < C1) {
-        const int i = ch / (M / 8), m0 = (ch % (M / 8)) * 8;
-        const int it = i >> 4, r = i & 15;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int m = m0 + e, ks2 = m >> 5, w = m & 31;
-          const int gg = w < 16 ? (w >> 2) : ((w - 16) >> 2);
-          const int t = w < 16 ? (w & 3) : 4 + ((w - 16) & 3);
-          f1[((it * KS2 + ks2) * 64 + 16 * gg + r) * 8 + t] = static_cast<uint16_t>(r1[q][e >> 1] >> (16 * (e & 1)));
-        }
-      }
+      const int slot = tid + q * THREADS;
+      if (slot < FRAG1) frag1[slot] = u32x4_t{r1[q][0], r1[q][1], r1[q][2], r1[q][3]};
     }
   }
 };

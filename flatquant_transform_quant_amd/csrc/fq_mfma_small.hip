@@ -92,19 +92,25 @@ __global__ __launch_bounds__(kSmallThreads, 2) void mfma_small_kernel(Problem pb
   // still arriving.
   {
     PStage<DT, M, N, kSmallThreads> ps;
-    ps.issue(pb, b, tid);
-    __builtin_amdgcn_sched_barrier(0);  // keep the issue order: P, then x
-    // With two slices in flight their loads are issued now, overlapping the staging; with
-    // one (large slices) registers are too short and the load waits for the slice loop.
     if constexpr (PF > 1) {
-      // in slice order (the loop's first wait is for the first slice)
+      ps.issue(pb, b, tid);
+      __builtin_amdgcn_sched_barrier(0);  // keep the issue order: P, then x
+      // With two slices in flight their loads are issued now, overlapping the staging,
+      // in slice order (the loop's first wait is for the first slice).
 #pragma unroll
       for (int q = 0; q < PF; ++q) {
         load_x(q, s + q * waves);
         __builtin_amdgcn_sched_barrier(0);
       }
+      ps.scatter(pb, frag2, frag1, tid);
+    } else {
+      // Large slices: registers are short, so P2 and P1 are staged one after the other
+      // and the first x load waits for the slice loop.
+      ps.issue_p2(pb, b, tid);
+      ps.scatter_p2(pb, frag2, tid);
+      ps.issue_p1(b, tid);
+      ps.scatter_p1(frag1, tid);
     }
-    ps.scatter(pb, frag2, frag1, tid);
   }
   lds_barrier();
   if (s >= pb.K) return;
