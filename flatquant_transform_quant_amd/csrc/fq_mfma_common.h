@@ -49,6 +49,90 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4_t c)
   }
 }
 
+// The same product with its accumulator kept in ordinary VGPRs.  A kernel that keeps a
+// large accumulator block in the accumulation registers (all 256 of them) needs a second,
+// short-lived accumulator elsewhere; the compiler picks one register form for every MFMA
+// of a function, so these are written out.  The compiler does not see these as MFMAs, so
+// they carry their own hazard handling:
+//   * a chain on one accumulator uses the same registers as destination and C operand,
+//     which the hardware forwards without wait states;
+//   * the operands come from LDS/memory loads (ordered by the compiler's s_waitcnt) or
+//     from long-lived registers; mfma_v_begin() adds the wait states a VALU-written
+//     operand needs;
+//   * mfma_v_drain() must follow the last product before anything reads an accumulator:
+//     it holds every accumulator as an operand, so no consumer can be scheduled ahead of
+//     its wait states (16, twice what a 4-pass product needs before a VALU read).
+// None of the statements is volatile: data dependences alone order them, so the compiler
+// stays free to issue LDS reads and other work ahead of and between the products.
+template <int DT>
+__device__ __forceinline__ f32x4_t mfma_v_first(u32x4_t a, u32x4_t b) {
+  f32x4_t d;
+  if constexpr (DT == kBF16)
+    asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  else
+    asm("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  return d;
+}
+
+template <int DT>
+__device__ __forceinline__ void mfma_v_acc(f32x4_t& d, u32x4_t a, u32x4_t b) {
+  if constexpr (DT == kBF16)
+    asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+  else
+    asm("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+
+// Accumulation in the accumulation registers, destination tied to the C operand.  For the
+// 16x16 shapes the compiler has no tied form and, with every accumulation register live,
+// rotates tiles through spare registers instead of accumulating in place; the tie rules
+// that out.  Hazards as above: C is written by other products of the same chain or by
+// fenced VALU writes (agpr_fence after zeroing), and every read of the results must
+// follow an agpr_fence<16>.
+template <int DT>
+__device__ __forceinline__ void mfma_a_acc(f32x4_t& d, u32x4_t a, u32x4_t b) {
+  if constexpr (DT == kBF16)
+    asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+  else
+    asm("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+}
+
+// Wait states on 4 ordinary registers (a VALU result about to feed an inline-asm product).
+__device__ __forceinline__ void vgpr_fence2(u32x4_t (&v)[4]) {
+  asm("s_nop 1" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]));
+}
+
+#define FQ_A4(y, i) "+a"(y[i][0]), "+a"(y[i][1]), "+a"(y[i][2]), "+a"(y[i][3])
+// Wait states held on a 16 x 4 block of accumulation-register tiles: WS = 2 after VALU
+// writes that products will read, WS = 16 after products whose results VALU will read.
+// WS = 0 only pins the block in its registers: copies read before it are dead after it,
+// so a second pass over the block reads the registers again instead of keeping copies.
+template <int WS>
+__device__ __forceinline__ void agpr_fence(f32x4_t (&y)[16][4]) {
+  if constexpr (WS == 0)
+    asm(""
+        : FQ_A4(y, 0), FQ_A4(y, 1), FQ_A4(y, 2), FQ_A4(y, 3), FQ_A4(y, 4), FQ_A4(y, 5), FQ_A4(y, 6), FQ_A4(y, 7),
+          FQ_A4(y, 8), FQ_A4(y, 9), FQ_A4(y, 10), FQ_A4(y, 11), FQ_A4(y, 12), FQ_A4(y, 13), FQ_A4(y, 14), FQ_A4(y, 15));
+  else if constexpr (WS == 2)
+    asm("s_nop 1"
+        : FQ_A4(y, 0), FQ_A4(y, 1), FQ_A4(y, 2), FQ_A4(y, 3), FQ_A4(y, 4), FQ_A4(y, 5), FQ_A4(y, 6), FQ_A4(y, 7),
+          FQ_A4(y, 8), FQ_A4(y, 9), FQ_A4(y, 10), FQ_A4(y, 11), FQ_A4(y, 12), FQ_A4(y, 13), FQ_A4(y, 14), FQ_A4(y, 15));
+  else
+    asm("s_nop 7\n\ts_nop 7"
+        : FQ_A4(y, 0), FQ_A4(y, 1), FQ_A4(y, 2), FQ_A4(y, 3), FQ_A4(y, 4), FQ_A4(y, 5), FQ_A4(y, 6), FQ_A4(y, 7),
+          FQ_A4(y, 8), FQ_A4(y, 9), FQ_A4(y, 10), FQ_A4(y, 11), FQ_A4(y, 12), FQ_A4(y, 13), FQ_A4(y, 14), FQ_A4(y, 15));
+}
+#undef FQ_A4
+
+template <int N>
+__device__ __forceinline__ void mfma_v_drain(f32x4_t (&d)[N]) {
+  static_assert(N == 4 || N == 8, "drain of 4 or 8 accumulators");
+  if constexpr (N == 4)
+    asm("s_nop 7\n\ts_nop 7" : "+v"(d[0]), "+v"(d[1]), "+v"(d[2]), "+v"(d[3]));
+  else
+    asm("s_nop 7\n\ts_nop 7"
+        : "+v"(d[0]), "+v"(d[1]), "+v"(d[2]), "+v"(d[3]), "+v"(d[4]), "+v"(d[5]), "+v"(d[6]), "+v"(d[7]));
+}
+
 // DPP lane moves inside 16-lane rows.
 enum : int {
   kDppQuadXor1 = 0xB1,    // quad_perm [1,0,3,2]

@@ -106,6 +106,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb,
     for (int it = 0; it < kIT; ++it)
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt) y[it][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    agpr_fence<2>(y);
 
     for (int ch = 0; ch < kNChunk; ++ch) {
       lds_barrier();  // every wave is done with the previous chunk (and with `red`)
@@ -116,33 +117,41 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb,
       else if (s + gridDim.x < pb.K)
         load_chunk(s + gridDim.x, 0);
 
-      // GEMM1: T rows 32ch + 16h + (4g .. 4g+3), h = 0, 1, of the wave's columns
-      f32x4_t acc[2][kNT];
+      // GEMM1: T rows 32ch + 16h + (4g .. 4g+3), h = 0, 1, of the wave's columns.  y fills
+      // the accumulation registers, so these accumulators are kept in ordinary VGPRs.
+      f32x4_t acc[2 * kNT];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-#pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) acc[h][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         const int row = 16 * h + c;
 #pragma unroll
         for (int ks = 0; ks < kW / 32; ++ks) {
           const u32x4_t a = xs[row * 32 + ((4 * ks + g) ^ row)];
 #pragma unroll
-          for (int nt = 0; nt < kNT; ++nt) acc[h][nt] = mfma16x16x32<DT>(a, p2f[ks][nt], acc[h][nt]);
+          for (int nt = 0; nt < kNT; ++nt) {
+            if (ks == 0)
+              acc[h * kNT + nt] = mfma_v_first<DT>(a, p2f[ks][nt]);
+            else
+              mfma_v_acc<DT>(acc[h * kNT + nt], a, p2f[ks][nt]);
+          }
         }
       }
+      mfma_v_drain(acc);
       u32x4_t tb[kNT];
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt)
-        tb[nt] = u32x4_t{round16x2<DT>(acc[0][nt][0], acc[0][nt][1]), round16x2<DT>(acc[0][nt][2], acc[0][nt][3]),
-                         round16x2<DT>(acc[1][nt][0], acc[1][nt][1]), round16x2<DT>(acc[1][nt][2], acc[1][nt][3])};
-      // GEMM2: y += P1[:, chunk] . T_chunk
+        tb[nt] = u32x4_t{round16x2<DT>(acc[nt][0], acc[nt][1]), round16x2<DT>(acc[nt][2], acc[nt][3]),
+                         round16x2<DT>(acc[kNT + nt][0], acc[kNT + nt][1]),
+                         round16x2<DT>(acc[kNT + nt][2], acc[kNT + nt][3])};
+      vgpr_fence2(tb);
+      // GEMM2: y += P1[:, chunk] . T_chunk, accumulated in place in the accumulation registers
 #pragma unroll
       for (int it = 0; it < kIT; ++it) {
         const u32x4_t a = frag1[(it * kNChunk + ch) * 64 + lane];
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) y[it][nt] = mfma16x16x32<DT>(a, tb[nt], y[it][nt]);
+        for (int nt = 0; nt < kNT; ++nt) mfma_a_acc<DT>(y[it][nt], a, tb[nt]);
       }
     }
+    agpr_fence<16>(y);
 
     // Output stores go through buffer resources for this slice: a per-lane offset (made
     // opaque per slice, so no per-row address is hoisted out of the slice loop and held in
