@@ -13,6 +13,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "fq_codec.h"
 #include "fq_internal.h"
@@ -36,6 +37,15 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// f(std::integral_constant<int, I>{}) for I = B .. E-1, in order (compile-time indices).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 
 template <int DT>
@@ -104,15 +114,9 @@ __device__ __forceinline__ void vgpr_fence2(u32x4_t (&v)[4]) {
 #define FQ_A4(y, i) "+a"(y[i][0]), "+a"(y[i][1]), "+a"(y[i][2]), "+a"(y[i][3])
 // Wait states held on a 16 x 4 block of accumulation-register tiles: WS = 2 after VALU
 // writes that products will read, WS = 16 after products whose results VALU will read.
-// WS = 0 only pins the block in its registers: copies read before it are dead after it,
-// so a second pass over the block reads the registers again instead of keeping copies.
 template <int WS>
 __device__ __forceinline__ void agpr_fence(f32x4_t (&y)[16][4]) {
-  if constexpr (WS == 0)
-    asm(""
-        : FQ_A4(y, 0), FQ_A4(y, 1), FQ_A4(y, 2), FQ_A4(y, 3), FQ_A4(y, 4), FQ_A4(y, 5), FQ_A4(y, 6), FQ_A4(y, 7),
-          FQ_A4(y, 8), FQ_A4(y, 9), FQ_A4(y, 10), FQ_A4(y, 11), FQ_A4(y, 12), FQ_A4(y, 13), FQ_A4(y, 14), FQ_A4(y, 15));
-  else if constexpr (WS == 2)
+  if constexpr (WS == 2)
     asm("s_nop 1"
         : FQ_A4(y, 0), FQ_A4(y, 1), FQ_A4(y, 2), FQ_A4(y, 3), FQ_A4(y, 4), FQ_A4(y, 5), FQ_A4(y, 6), FQ_A4(y, 7),
           FQ_A4(y, 8), FQ_A4(y, 9), FQ_A4(y, 10), FQ_A4(y, 11), FQ_A4(y, 12), FQ_A4(y, 13), FQ_A4(y, 14), FQ_A4(y, 15));
@@ -120,6 +124,15 @@ __device__ __forceinline__ void agpr_fence(f32x4_t (&y)[16][4]) {
     asm("s_nop 7\n\ts_nop 7"
         : FQ_A4(y, 0), FQ_A4(y, 1), FQ_A4(y, 2), FQ_A4(y, 3), FQ_A4(y, 4), FQ_A4(y, 5), FQ_A4(y, 6), FQ_A4(y, 7),
           FQ_A4(y, 8), FQ_A4(y, 9), FQ_A4(y, 10), FQ_A4(y, 11), FQ_A4(y, 12), FQ_A4(y, 13), FQ_A4(y, 14), FQ_A4(y, 15));
+}
+// Ends a pass over the block that produced `r`: every read of that pass happens before
+// this point (r passes through it), and copies read before it are dead after it (the block
+// is redefined), so a second pass reads the registers again instead of keeping 256 copies.
+__device__ __forceinline__ void agpr_pass_end(f32x4_t (&y)[16][4], float& r) {
+  asm(""
+      : FQ_A4(y, 0), FQ_A4(y, 1), FQ_A4(y, 2), FQ_A4(y, 3), FQ_A4(y, 4), FQ_A4(y, 5), FQ_A4(y, 6), FQ_A4(y, 7),
+        FQ_A4(y, 8), FQ_A4(y, 9), FQ_A4(y, 10), FQ_A4(y, 11), FQ_A4(y, 12), FQ_A4(y, 13), FQ_A4(y, 14), FQ_A4(y, 15),
+        "+v"(r));
 }
 #undef FQ_A4
 

@@ -36,13 +36,19 @@ constexpr int kIT = kW / 16;  // 16-row tiles of y
 template <int DT, bool PG, bool CLAMP, int SV>
 __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb, Buffers b) {
   __shared__ u32x4_t frag1[kIT * kNChunk * 64];   // 128 KB: P1 A fragments
-  __shared__ u32x4_t xs[kChunk * 32];             // 16 KB: one x chunk, 32 slots of 16 B per row
-  __shared__ float red[kWideWaves];
+  // 2 x 16 KB: x chunks in GEMM1 A-fragment order.  The 16-byte slot q = 4ks + g of chunk
+  // row r = 16h + c (x columns 8q .. 8q+7) sits at (2ks + h)*64 + 16g + (c ^ 4g): a lane's
+  // reads are one base address plus immediate offsets, and both the reads and the stores
+  // below touch 16 distinct bank groups per 16 lanes.
+  __shared__ u32x4_t xs[2][kChunk * 32];
+  constexpr int D = 2;                            // chunks in flight in registers (divides 8)
+  constexpr int XR = kChunk * kW * 2 / 16 / kWideThreads;  // 16-byte pieces per thread per chunk
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, g = lane >> 4;
+  const int64_t stride = gridDim.x;
 
   // ---- P1 -> LDS fragments: P1[i, m] -> frag1[(it*8 + ch)*64 + 16*gg + i%16] element t,
   // m = 32ch + (t < 4 ? 4gg + t : 16 + 4gg + t - 4) ----
@@ -82,102 +88,169 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb,
       p2f[ks][nt] = u32x4_t{v[0], v[1], v[2], v[3]};
     }
 
-  // x chunk prefetch: thread t moves 16-byte slots t + 256h, h = 0..3, of the chunk
-  constexpr int XR = kChunk * kW * 2 / 16 / kWideThreads;
-  u32x4_t xr[XR];
-  auto load_chunk = [&](int64_t slice, int ch) {
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(b.x + slice * (kW * kW) + ch * (kChunk * kW));
+  // Chunk j of the workgroup: slice blockIdx.x + (j / 8) * gridDim.x, x rows 32 * (j % 8) ..
+  // Load h of wave w covers chunk rows 8h + 4(w/2) .. +3, slots 16(w%2) .. +15: lane l takes
+  // row + (l % 4), slot + l / 4 (whole 256-byte row halves per instruction).  Bounded buffer
+  // loads (zeros past K, no memory access): unconditional, so the compiler's memory-counter
+  // waits cover exactly the chunk being consumed.
+  u32x4_t xr[D][XR];
+  const int ld_off = ((4 * (w >> 1) + (lane & 3)) * 32 + 16 * (w & 1) + (lane >> 2)) * 16;
+  auto load_chunk = [&](int64_t j, u32x4_t* r) {
+    const int64_t slice = blockIdx.x + (j >> 3) * stride;
+    const bool in = slice < pb.K;
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(b.x + (in ? slice : 0) * (kW * kW) + (j & 7) * (kChunk * kW)),
+        static_cast<int16_t>(0), in ? kChunk * kW * 2 : 0, kBufferWord3);
 #pragma unroll
-    for (int h = 0; h < XR; ++h) xr[h] = src[tid + h * kWideThreads];
+    for (int h = 0; h < XR; ++h) r[h] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, ld_off, h * 8 * kW * 2, 0);
   };
-  auto store_chunk = [&]() {
+  // the slot of load h: row 8h + 4(w/2) + l%4 (c = 8(h%2) + 4(w/2) + l%4, h_row = h/2),
+  // slot 16(w%2) + l/4 (ks = 4(w%2) + l/16, g = (l/4)%4)
+  const int sg = (lane >> 2) & 3;
+  const int st_even = (4 * (w & 1) + (lane >> 4)) * 2 * 64 + 16 * sg + ((4 * (w >> 1) + (lane & 3)) ^ (4 * sg));
+  const int st_odd = st_even ^ 8;
+  auto store_chunk = [&](const u32x4_t* r, u32x4_t* dst) {
 #pragma unroll
-    for (int h = 0; h < XR; ++h) {
-      const int gi = tid + h * kWideThreads, row = gi >> 5, q = gi & 31;
-      xs[row * 32 + (q ^ row)] = xr[h];
-    }
+    for (int h = 0; h < XR; ++h) dst[((h & 1) ? st_odd : st_even) + (h >> 1) * 64] = r[h];
   };
+  // LDS read bases (opaque, so every fragment read is one of three bases plus an immediate
+  // offset below 64 KB instead of an address register of its own hoisted out of the loop):
+  // the lane's x-chunk slot, and its P1 fragment slot in the low and high 64 KB of frag1.
+  int rd_base = 16 * g + (c ^ (4 * g));
+  int f1_lo = lane, f1_hi = lane + kIT / 2 * kNChunk * 64;
+  asm volatile("" : "+v"(rd_base), "+v"(f1_lo), "+v"(f1_hi));
 
   int64_t s = blockIdx.x;
-  if (s < pb.K) load_chunk(s, 0);
-  for (; s < pb.K; s += gridDim.x) {
-    f32x4_t y[kIT][kNT];
+  if (s >= pb.K) return;
+  // prologue: chunk 0 in LDS, chunks 1 .. D in registers (chunk k in xr[k % D]), issued in
+  // chunk order, so that waiting for one chunk never waits for a later one.
+  load_chunk(0, xr[0]);
+  store_chunk(xr[0], xs[0]);
 #pragma unroll
-    for (int it = 0; it < kIT; ++it)
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) y[it][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    agpr_fence<2>(y);
+  for (int k = 1; k <= D; ++k) {
+    __builtin_amdgcn_sched_barrier(0);
+    load_chunk(k, xr[k % D]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  lds_barrier();  // chunk 0 is in LDS
 
-    for (int ch = 0; ch < kNChunk; ++ch) {
-      lds_barrier();  // every wave is done with the previous chunk (and with `red`)
-      store_chunk();
-      lds_barrier();  // the chunk is in LDS
-      if (ch + 1 < kNChunk)
-        load_chunk(s, ch + 1);
-      else if (s + gridDim.x < pb.K)
-        load_chunk(s + gridDim.x, 0);
+  int64_t j0 = 0;  // chunk index of this slice's chunk 0
+  f32x4_t y[kIT][kNT];
 
-      // GEMM1: T rows 32ch + 16h + (4g .. 4g+3), h = 0, 1, of the wave's columns.  y fills
-      // the accumulation registers, so these accumulators are kept in ordinary VGPRs.
-      f32x4_t acc[2 * kNT];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int row = 16 * h + c;
-#pragma unroll
-        for (int ks = 0; ks < kW / 32; ++ks) {
-          const u32x4_t a = xs[row * 32 + ((4 * ks + g) ^ row)];
-#pragma unroll
-          for (int nt = 0; nt < kNT; ++nt) {
-            if (ks == 0)
-              acc[h * kNT + nt] = mfma_v_first<DT>(a, p2f[ks][nt]);
-            else
-              mfma_v_acc<DT>(acc[h * kNT + nt], a, p2f[ks][nt]);
-          }
-        }
-      }
-      mfma_v_drain(acc);
-      u32x4_t tb[kNT];
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt)
-        tb[nt] = u32x4_t{round16x2<DT>(acc[nt][0], acc[nt][1]), round16x2<DT>(acc[nt][2], acc[nt][3]),
-                         round16x2<DT>(acc[kNT + nt][0], acc[kNT + nt][1]),
-                         round16x2<DT>(acc[kNT + nt][2], acc[kNT + nt][3])};
-      vgpr_fence2(tb);
-      // GEMM2: y += P1[:, chunk] . T_chunk, accumulated in place in the accumulation registers
-#pragma unroll
-      for (int it = 0; it < kIT; ++it) {
-        const u32x4_t a = frag1[(it * kNChunk + ch) * 64 + lane];
-#pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) mfma_a_acc<DT>(y[it][nt], a, tb[nt]);
-      }
+  // A chunk is 32 stages of 4 products sharing one A fragment: stages 0..15 are GEMM1
+  // (k-step k/2 of row half k%2, A from the x chunk), stages 16..31 GEMM2 (row tile k-16,
+  // A from P1).  The A fragment of stage k is read P stages ahead into ring[k % 4]; the
+  // scheduling barriers keep that order (the compiler cannot see the products' latency).
+  constexpr int P = 3;
+  u32x4_t ring[P + 1];
+  auto read_a = [&](auto chv, auto kv) {
+    constexpr int ch = decltype(chv)::value, k = decltype(kv)::value;
+    if constexpr (k < 16)
+      ring[k % (P + 1)] = xs[ch & 1][rd_base + (2 * (k >> 1) + (k & 1)) * 64];
+    else
+      ring[k % (P + 1)] = k < 16 + kIT / 2 ? frag1[f1_lo + ((k - 16) * kNChunk + ch) * 64]
+                                           : frag1[f1_hi + ((k - 16 - kIT / 2) * kNChunk + ch) * 64];
+  };
+
+  // One chunk: T_ch = x[32ch .. 32ch+31, :] . P2[:, strip] (GEMM1), rounded to the dtype in
+  // registers, then y[:, strip] += P1[:, 32ch .. 32ch+31] . T_ch (GEMM2).  The barrier sits
+  // between the two: before it every wave has stored chunk ch+1 and finished reading chunk
+  // ch, so after it the next chunk's first fragments can be read and, in the next step,
+  // chunk ch+2 can be stored over chunk ch.  CARRY: stages 0..P-1 of this chunk were read
+  // by the previous step.
+  auto chunk_step = [&](auto chv, auto carryv) {
+    constexpr int ch = decltype(chv)::value;
+    constexpr bool carry_in = decltype(carryv)::value;
+    constexpr bool carry_out = ch != kNChunk - 1;  // the next slice's chunk 0 starts afresh
+    if constexpr (!carry_in) {
+      read_a(chv, std::integral_constant<int, 0>{});
+      read_a(chv, std::integral_constant<int, 1>{});
+      read_a(chv, std::integral_constant<int, 2>{});
     }
-    agpr_fence<16>(y);
+    store_chunk(xr[(ch + 1) % D], xs[(ch + 1) & 1]);
+    load_chunk(j0 + ch + 1 + D, xr[(ch + 1) % D]);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // Output stores go through buffer resources for this slice: a per-lane offset (made
-    // opaque per slice, so no per-row address is hoisted out of the slice loop and held in
-    // registers) plus the row as a scalar offset.
+    f32x4_t acc[2 * kNT];
+    u32x4_t tb[kNT];
+    static_for<0, 32>([&](auto kv) {
+      constexpr int k = decltype(kv)::value;
+      if constexpr (k + P < 32)
+        read_a(chv, std::integral_constant<int, k + P>{});
+      else if constexpr (carry_out)
+        read_a(std::integral_constant<int, ch + 1>{}, std::integral_constant<int, k + P - 32>{});
+      __builtin_amdgcn_sched_barrier(0);
+      const u32x4_t a = ring[k % (P + 1)];
+      if constexpr (k < 16) {
+        constexpr int h = k & 1, ks = k >> 1;
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+          if constexpr (ks == 0)
+            acc[h * kNT + nt] = mfma_v_first<DT>(a, p2f[ks][nt]);
+          else
+            mfma_v_acc<DT>(acc[h * kNT + nt], a, p2f[ks][nt]);
+        }
+      } else {
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) mfma_a_acc<DT>(y[k - 16][nt], a, tb[nt]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (k == 15) {
+        mfma_v_drain(acc);
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt)
+          tb[nt] = u32x4_t{round16x2<DT>(acc[nt][0], acc[nt][1]), round16x2<DT>(acc[nt][2], acc[nt][3]),
+                           round16x2<DT>(acc[kNT + nt][0], acc[kNT + nt][1]),
+                           round16x2<DT>(acc[kNT + nt][2], acc[kNT + nt][3])};
+        vgpr_fence2(tb);
+        lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    });
+  };
+
+  // Output stores go through buffer resources for this slice: a per-lane offset (made
+  // opaque per slice, so no per-row address is hoisted out of the slice loop and held in
+  // registers) plus the row as a scalar offset.
+  auto epilogue = [&]() {
+    agpr_fence<16>(y);
     const auto rs_codes = __builtin_amdgcn_make_buffer_rsrc(b.codes + s * (kW * kW / 2), static_cast<int16_t>(0),
                                                             kW * kW / 2, kBufferWord3);
     int code_off = 4 * g * (kW / 2) + 32 * w + 2 * c;
     asm volatile("" : "+v"(code_off));
     if constexpr (!PG) {
-      // [FQV2] 第3步 pertoken: max|y| over the slice (4 waves), scale, codes
+      // [FQV2] 第3步 pertoken: max|y| over the slice (4 waves), scale, codes.  The partial
+      // maxima pass through xs[1], which held the slice's last chunk (every wave finished
+      // reading it before the last chunk's barrier) and is written next by the next slice's
+      // first chunk step.
+      // (the scheduling barriers keep each pass to one 16-row tile of y at a time)
       float amax = 0.0f;
 #pragma unroll
-      for (int it = 0; it < kIT; ++it)
+      for (int it = 0; it < kIT; ++it) {
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) amax = fmaxf(amax, __builtin_fabsf(y[it][nt][i]));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      agpr_pass_end(y, amax);  // the codes pass reads y from its registers again
       amax = wave_max(amax);
-      if (lane == 0) red[w] = amax;
+      float* red = reinterpret_cast<float*>(xs[1]);
+      // (no lane-dependent branches in this epilogue: with every accumulation register
+      // live, a divergent branch costs the register allocator hundreds of spills)
+      red[w] = amax;  // every lane writes the same value
       lds_barrier();
-      amax = red[0];
-#pragma unroll
-      for (int q = 1; q < kWideWaves; ++q) amax = fmaxf(amax, red[q]);
+      amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+      lds_barrier();  // every wave has read `red` before the next chunk is stored over it
       const float scale = amax / pb.d;
-      const float inv = scale > 0.0f ? 1.0f / scale : 0.0f;
-      if (tid == 0) static_cast<float*>(b.scale)[s] = scale;
+      float inv = scale > 0.0f ? 1.0f / scale : 0.0f;
+      agpr_pass_end(y, inv);  // the codes pass reads y only once inv is known
+      {
+        // every lane stores the same 4 bytes
+        const auto rs_scale = __builtin_amdgcn_make_buffer_rsrc(static_cast<float*>(b.scale) + s, static_cast<int16_t>(0),
+                                                                4, kBufferWord3);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(scale), rs_scale, 0, 0, 0);
+      }
 #pragma unroll
       for (int it = 0; it < kIT; ++it)
 #pragma unroll
@@ -185,8 +258,9 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb,
           const int r0 = 16 * it + i;  // row - 4g
           const uint32_t b0 = pair_byte(int4_biased<CLAMP>(y[it][0][i], inv), int4_biased<CLAMP>(y[it][1][i], inv));
           const uint32_t b1 = pair_byte(int4_biased<CLAMP>(y[it][2][i], inv), int4_biased<CLAMP>(y[it][3][i], inv));
-          *reinterpret_cast<uint16_t*>(b.codes + s * (kW * kW / 2) + (r0 + 4 * g) * (kW / 2) + 32 * w + 2 * c) =
-              static_cast<uint16_t>(unbias(__builtin_amdgcn_perm(b1, b0, 0x0C0C0400u)));
+          __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(unbias(__builtin_amdgcn_perm(b1, b0, 0x0C0C0400u))),
+                                                rs_codes, code_off, r0 * (kW / 2), 0);
+          if (i == 3) __builtin_amdgcn_sched_barrier(0);
         }
     } else {
       // [FQV2] 第3步 pergroup / 第4步: a 32-group is 8 neighbouring lanes of one row
@@ -212,6 +286,39 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb,
           __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(code), rs_e8, e8_off, r0 * (kW / 32), 0);
         }
     }
+  };
+
+  auto zero_y = [&]() {
+#pragma unroll
+    for (int it = 0; it < kIT; ++it)
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) y[it][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    agpr_fence<2>(y);
+  };
+
+  // The slice loop is rotated to start at chunk 4: the loop head's waits see the same
+  // loads in flight on entry and on every later pass.
+  using F = std::false_type;
+  using T = std::true_type;
+  zero_y();
+  chunk_step(std::integral_constant<int, 0>{}, F{});
+  chunk_step(std::integral_constant<int, 1>{}, T{});
+  chunk_step(std::integral_constant<int, 2>{}, T{});
+  chunk_step(std::integral_constant<int, 3>{}, T{});
+  while (true) {
+    chunk_step(std::integral_constant<int, 4>{}, T{});
+    chunk_step(std::integral_constant<int, 5>{}, T{});
+    chunk_step(std::integral_constant<int, 6>{}, T{});
+    chunk_step(std::integral_constant<int, 7>{}, T{});
+    epilogue();
+    s += stride;
+    j0 += kNChunk;
+    if (s >= pb.K) break;
+    zero_y();
+    chunk_step(std::integral_constant<int, 0>{}, F{});
+    chunk_step(std::integral_constant<int, 1>{}, T{});
+    chunk_step(std::integral_constant<int, 2>{}, T{});
+    chunk_step(std::integral_constant<int, 3>{}, T{});
   }
 }
 
