@@ -106,6 +106,23 @@ __device__ __forceinline__ void mfma_a_acc(f32x4_t& d, u32x4_t a, u32x4_t b) {
     asm("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
 }
 
+// The first product of such a chain: C = 0, so the block needs no zeroing.
+template <int DT>
+__device__ __forceinline__ void mfma_a_first(f32x4_t& d, u32x4_t a, u32x4_t b) {
+  if constexpr (DT == kBF16)
+    asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(d) : "v"(a), "v"(b));
+  else
+    asm("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0" : "=a"(d) : "v"(a), "v"(b));
+}
+
+// Marks 4 accumulation-register tiles as read from here on.  Placed after at least four
+// further products have been issued behind the tiles' last product (the products run in
+// order, so by then it has written its results), this orders VALU reads of the tiles
+// without wait states of its own.
+__device__ __forceinline__ void agpr_tiles_done(f32x4_t (&t)[4]) {
+  asm("" : "+a"(t[0]), "+a"(t[1]), "+a"(t[2]), "+a"(t[3]));
+}
+
 // Wait states on 4 ordinary registers (a VALU result about to feed an inline-asm product).
 __device__ __forceinline__ void vgpr_fence2(u32x4_t (&v)[4]) {
   asm("s_nop 1" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]));

@@ -136,6 +136,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb,
 
   int64_t j0 = 0;  // chunk index of this slice's chunk 0
   f32x4_t y[kIT][kNT];
+  float amax_run = 0.0f;  // per token: max|y| of the slice's finished tiles
 
   // A chunk is 32 stages of 4 products sharing one A fragment: stages 0..15 are GEMM1
   // (k-step k/2 of row half k%2, A from the x chunk), stages 16..31 GEMM2 (row tile k-16,
@@ -162,6 +163,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb,
     constexpr int ch = decltype(chv)::value;
     constexpr bool carry_in = decltype(carryv)::value;
     constexpr bool carry_out = ch != kNChunk - 1;  // the next slice's chunk 0 starts afresh
+    if constexpr (!PG && ch == kNChunk - 1) amax_run = 0.0f;
     if constexpr (!carry_in) {
       read_a(chv, std::integral_constant<int, 0>{});
       read_a(chv, std::integral_constant<int, 1>{});
@@ -191,8 +193,25 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb,
             mfma_v_acc<DT>(acc[h * kNT + nt], a, p2f[ks][nt]);
         }
       } else {
+        // per token, last chunk: max|y| of the tile the previous stage finished, a quarter
+        // after each product (VALU work issued while the product runs; the last tile
+        // follows in the epilogue)
+        constexpr bool amax_here = !PG && ch == kNChunk - 1 && k >= 17;
+        constexpr int t = amax_here ? k - 17 : 0;
+        if constexpr (amax_here) agpr_tiles_done(y[t]);
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) mfma_a_acc<DT>(y[k - 16][nt], a, tb[nt]);
+        for (int nt = 0; nt < kNT; ++nt) {
+          if constexpr (ch == 0)
+            mfma_a_first<DT>(y[k - 16][nt], a, tb[nt]);
+          else
+            mfma_a_acc<DT>(y[k - 16][nt], a, tb[nt]);
+          if constexpr (amax_here) {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) amax_run = fmaxf(amax_run, __builtin_fabsf(y[t][nt][i]));
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (k == 15) {
@@ -224,16 +243,11 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb,
       // reading it before the last chunk's barrier) and is written next by the next slice's
       // first chunk step.
       // (the scheduling barriers keep each pass to one 16-row tile of y at a time)
-      float amax = 0.0f;
+      float amax = amax_run;
 #pragma unroll
-      for (int it = 0; it < kIT; ++it) {
+      for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) amax = fmaxf(amax, __builtin_fabsf(y[it][nt][i]));
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      agpr_pass_end(y, amax);  // the codes pass reads y from its registers again
+        for (int i = 0; i < 4; ++i) amax = fmaxf(amax, __builtin_fabsf(y[kIT - 1][nt][i]));
       amax = wave_max(amax);
       float* red = reinterpret_cast<float*>(xs[1]);
       // (no lane-dependent branches in this epilogue: with every accumulation register
@@ -288,19 +302,10 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb,
     }
   };
 
-  auto zero_y = [&]() {
-#pragma unroll
-    for (int it = 0; it < kIT; ++it)
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) y[it][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    agpr_fence<2>(y);
-  };
-
   // The slice loop is rotated to start at chunk 4: the loop head's waits see the same
   // loads in flight on entry and on every later pass.
   using F = std::false_type;
   using T = std::true_type;
-  zero_y();
   chunk_step(std::integral_constant<int, 0>{}, F{});
   chunk_step(std::integral_constant<int, 1>{}, T{});
   chunk_step(std::integral_constant<int, 2>{}, T{});
@@ -314,7 +319,6 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb,
     s += stride;
     j0 += kNChunk;
     if (s >= pb.K) break;
-    zero_y();
     chunk_step(std::integral_constant<int, 0>{}, F{});
     chunk_step(std::integral_constant<int, 1>{}, T{});
     chunk_step(std::integral_constant<int, 2>{}, T{});
