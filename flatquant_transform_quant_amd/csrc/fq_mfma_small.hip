@@ -14,7 +14,7 @@
 // bytes per row, and a 32-group spans 32/R neighbouring lanes.
 // An empty P2 ([0, 0]) is run as P2 = I: T = RNE(x * 1) = x exactly.
 //
-// Workgroups of 4 waves share P1/P2 fragments staged once in LDS in operand order (one
+// The waves of a workgroup share P1/P2 fragments staged once in LDS in operand order (one
 // 16-byte read per lane, conflict-free); the grid is persistent, each wave walking the
 // slices wave_id, wave_id + total_waves, ...  The next slice's x is requested while the
 // current slice's GEMM2 and epilogue run.
@@ -26,9 +26,6 @@
 namespace fq {
 namespace {
 
-constexpr int kSmallWaves = 4;
-constexpr int kSmallThreads = 64 * kSmallWaves;
-
 // Slices of x kept in flight per wave: two for small slices (the loads of the slice two
 // ahead are issued as soon as the current one's first product has consumed its
 // registers), one where registers are short.  (Three measured slower: the extra slice
@@ -38,9 +35,20 @@ constexpr int prefetch_depth() {
   return (M * N <= 4096) ? 2 : 1;
 }
 
+// Waves per workgroup: 8 for the large slices (one workgroup per CU, so the CU stages its
+// 40 KB or more of P fragments once: 6-9% faster at M=64, N=128), 4 for the small ones
+// (two workgroups per CU measured faster there).
+template <int M, int N, bool PG>
+constexpr int small_waves() {
+  return prefetch_depth<M, N, PG>() == 1 ? 8 : 4;
+}
+
 // CLAMP (per token): the int4 clamp is compiled in.  SV (per group): the e8m0 rule.
 template <int DT, int M, int N, bool PG, bool CLAMP, int SV>
-__global__ __launch_bounds__(kSmallThreads, 2) void mfma_small_kernel(Problem pb, Buffers b) {
+__global__ __launch_bounds__((64 * small_waves<M, N, PG>()), (8 / small_waves<M, N, PG>())) void mfma_small_kernel(
+    Problem pb, Buffers b) {
+  constexpr int kSmallWaves = small_waves<M, N, PG>();
+  constexpr int kSmallThreads = 64 * kSmallWaves;
   constexpr int MT = M / 16, NT = N / 16, R = N / 16;
   constexpr int KS1 = N / 32;              // GEMM1 k-steps over j
   constexpr int KS2 = (M + 31) / 32;       // GEMM2 k-steps over m
@@ -289,6 +297,7 @@ __global__ __launch_bounds__(kSmallThreads, 2) void mfma_small_kernel(Problem pb
 
 template <int DT, int M, int N, bool PG, bool CLAMP, int SV>
 hipError_t launch_one(const Problem& pb, const Buffers& b, hipStream_t s) {
+  constexpr int kWaves = small_waves<M, N, PG>(), kThreads = 64 * kWaves;
   static int grid_cap = 0;  // workgroups that fit the device at once (per instantiation)
   if (grid_cap == 0) {
     int dev = 0, cus = 0, per_cu = 0;
@@ -296,13 +305,13 @@ hipError_t launch_one(const Problem& pb, const Buffers& b, hipStream_t s) {
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e == hipSuccess)
       e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_small_kernel<DT, M, N, PG, CLAMP, SV>,
-                                                       kSmallThreads, 0);
+                                                       kThreads, 0);
     if (e != hipSuccess) return e;
     grid_cap = cus * (per_cu > 0 ? per_cu : 1);
   }
-  const int64_t need = (pb.K + kSmallWaves - 1) / kSmallWaves;
+  const int64_t need = (pb.K + kWaves - 1) / kWaves;
   const int grid = static_cast<int>(need < grid_cap ? need : grid_cap);
-  mfma_small_kernel<DT, M, N, PG, CLAMP, SV><<<grid, kSmallThreads, 0, s>>>(pb, b);
+  mfma_small_kernel<DT, M, N, PG, CLAMP, SV><<<grid, kThreads, 0, s>>>(pb, b);
   return hipGetLastError();
 }
 
