@@ -88,6 +88,18 @@ def test_k_not_a_multiple_of_the_grid():
         assert rep["ok"], rep["errors"]
 
 
+@pytest.mark.parametrize("key", ["c4", "c5"])
+def test_k_ragged_whole_workgroup_kernels(key):
+    """M = N = 256 with K leaving some CUs two or three slices and others one: the slice
+    loop's later passes, the chunk lookahead across slices and the loads past K."""
+    w = synth.WORKLOADS[key]
+    for K in (257, 515):
+        x, p1, p2 = synth.make_inputs(w, 0, K)
+        rep = check(x, p1, p2, w.dtype, w.mode, w.clip_ratio, w.dst_type_max, label=f"{key} ragged K={K}",
+                    slices=sorted({0, 1, 255, 256, 257 % K, K // 2, K - 2, K - 1}))
+        assert rep["ok"], rep["errors"]
+
+
 def test_zero_input_gives_zero_scale_and_codes():
     for mode, dmax in (("int32", 0.0), ("fp4", 0.0), ("fp4", 8.0)):
         x = np.zeros((4, 64, 64), np.uint16)
@@ -114,7 +126,7 @@ def test_full_size_sampled(key):
     assert rep["ok"], rep["errors"]
 
 
-@pytest.mark.parametrize("key", ["c2", "c3", "c5"])
+@pytest.mark.parametrize("key", ["c2", "c3", "c4", "c5"])
 def test_deterministic_across_runs_and_streams(key):
     w = synth.WORKLOADS[key]
     K = 512 if w.M * w.N <= 8192 else 32
