@@ -36,16 +36,27 @@ constexpr int prefetch_depth() {
 }
 
 // Waves per workgroup: 8 for the large slices (one workgroup per CU, so the CU stages its
-// 40 KB or more of P fragments once: 6-9% faster at M=64, N=128), 4 for the small ones
-// (two workgroups per CU measured faster there).
+// 40 KB or more of P fragments once: 6-9% faster at M=64, N=128), 4 for the small ones.
 template <int M, int N, bool PG>
 constexpr int small_waves() {
   return prefetch_depth<M, N, PG>() == 1 ? 8 : 4;
 }
 
+// Workgroups per CU: for 4096-element slices with two in flight, one (a wave per SIMD, 8
+// slices each at K = 8192) -- 4-6% faster than the two that fit, which double the x
+// requested at the start and the P staging; smaller slices fill the CU (more waves hide
+// their shorter latency chains).  0 = as many as fit.
+template <int M, int N, bool PG>
+constexpr int small_workgroups_per_cu() {
+  return (M * N >= 4096 && prefetch_depth<M, N, PG>() == 2) ? 1 : 0;
+}
+
 // CLAMP (per token): the int4 clamp is compiled in.  SV (per group): the e8m0 rule.
 template <int DT, int M, int N, bool PG, bool CLAMP, int SV>
-__global__ __launch_bounds__((64 * small_waves<M, N, PG>()), (8 / small_waves<M, N, PG>())) void mfma_small_kernel(
+// (The second launch bound is HIP's minimum of waves per SIMD: 2 keeps the 4-wave variants
+// to 256 registers, the budget they were written for, also where one wave per SIMD is
+// launched; an 8-wave workgroup already puts two on each SIMD.)
+__global__ __launch_bounds__((64 * small_waves<M, N, PG>()), (small_waves<M, N, PG>() == 8 ? 1 : 2)) void mfma_small_kernel(
     Problem pb, Buffers b) {
   constexpr int kSmallWaves = small_waves<M, N, PG>();
   constexpr int kSmallThreads = 64 * kSmallWaves;
@@ -307,7 +318,8 @@ hipError_t launch_one(const Problem& pb, const Buffers& b, hipStream_t s) {
       e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_small_kernel<DT, M, N, PG, CLAMP, SV>,
                                                        kThreads, 0);
     if (e != hipSuccess) return e;
-    grid_cap = cus * (per_cu > 0 ? per_cu : 1);
+    constexpr int wg = small_workgroups_per_cu<M, N, PG>();
+    grid_cap = cus * (wg > 0 ? wg : (per_cu > 0 ? per_cu : 1));
   }
   const int64_t need = (pb.K + kWaves - 1) / kWaves;
   const int grid = static_cast<int>(need < grid_cap ? need : grid_cap);
