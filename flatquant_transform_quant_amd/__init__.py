@@ -75,12 +75,14 @@ def _load():
     L.fq_status_string.restype = ctypes.c_char_p
     L.fq_last_error.argtypes = []
     L.fq_last_error.restype = ctypes.c_char_p
+    L.fq_dequant.argtypes = [P, P, P, vp]
+    L.fq_dequant.restype = ctypes.c_int32
     return L
 
 
 lib = _load()
 EXPORTS = ("fq_get_workspace_size", "fq_run", "fq_executor_destroy", "fq_executor_set_repeatable",
-           "fq_executor_set_kernel", "fq_executor_kernel", "fq_status_string", "fq_last_error")
+           "fq_executor_set_kernel", "fq_executor_kernel", "fq_status_string", "fq_last_error", "fq_dequant")
 
 
 def status_string(status: int) -> str:
@@ -143,6 +145,11 @@ def fq_status_string(status: int) -> str:
 
 def fq_last_error() -> str:
     return lib.fq_last_error().decode()
+
+
+def fq_dequant(codes: FqTensor, scale: FqTensor, out: FqTensor, stream_ptr: int) -> int:
+    ref = lambda t: ctypes.byref(t) if t is not None else None  # noqa: E731
+    return lib.fq_dequant(ref(codes), ref(scale), ref(out), stream_ptr or None)
 
 
 # ---- torch marshalling ---------------------------------------------------------------
@@ -254,3 +261,19 @@ def quantize(x, p1, p2, out, quant_scale, mode: str, clip_ratio: float = 1.0,
     ex = Executor(x, p1, p2, out, quant_scale, mode, clip_ratio, dst_type_max, kernel=kernel,
                   repeatable=False)
     ex.run(stream)
+
+
+def dequantize(codes, quant_scale, mode: str, M: int, N: int, dtype, out=None, stream=None):
+    """Values of quantizer outputs (as stored by ``empty_outputs``) in ``dtype``
+    (torch.bfloat16 or torch.float16): a [K, M, N] tensor, ``out`` when given."""
+    torch = _torch()
+    K = codes.shape[0]
+    if out is None:
+        out = torch.empty((K, M, N), dtype=dtype, device=codes.device)
+    dt = {torch.float16: DT_FLOAT16, torch.bfloat16: DT_BFLOAT16}.get(out.dtype, -1)
+    st = fq_dequant(describe_out(codes, mode, K, M, N), describe_scale(quant_scale, mode),
+                    make_tensor(out.data_ptr(), dt, out.shape, out.stride()),
+                    (stream if stream is not None else torch.cuda.current_stream(codes.device)).cuda_stream)
+    if st != FQ_SUCCESS:
+        raise FqError(st, "fq_dequant")
+    return out

@@ -1,0 +1,134 @@
+// Dequantization of the quantizer's outputs: codes + scales -> values in x's dtype, the
+// second half of a quantize -> dequantize ("fake-quant") round trip.
+//
+//   per token:  value = q * quantScale[k]                   (APT-LLM page, section 2.1:
+//               q the two's-complement int4 code              the symmetric integer format
+//                                                             dequantizes as q * scale)
+//   per group:  value = E2M1(code) * 2^(e8m0 - 127)          ([FQV2] 第3步 pergroup: the
+//               E2M1 magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6     scale is a power of two;
+//               with the sign bit on top                       ModelOpt page, section 6.1)
+//
+// The product is formed in IEEE fp32 (per group it is exact or overflows to inf; an e8m0
+// byte 0xFF, NaN in the MX encoding, makes its group NaN) and rounded once, to nearest
+// even, to the output dtype.  Codes are read in the packed layouts the quantizer writes:
+// K * M*N/2 bytes, low nibble = lower flattened index; e8m0 [K, 2*ceil(M*N/64)] bytes.
+//
+// HBM-bound streaming (0.5 byte in, 2 bytes out per element).  Slices whose element
+// count is a multiple of 32 take the fast path: a thread turns 32 consecutive codes (one
+// 16-byte load; per group exactly one group) into 64 output bytes (four 16-byte stores),
+// so a wave reads 1 KB and writes 4 KB contiguously.  Other shapes take a thread per code
+// byte.
+#include <hip/hip_runtime.h>
+
+#include "fq_codec.h"
+#include "fq_internal.h"
+
+namespace fq {
+namespace {
+
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+
+constexpr int kDqThreads = 256;
+
+// fp32 value of an E2M1 code (bit 3 the sign, bits 0-2 the magnitude index)
+__device__ __forceinline__ float e2m1_float(uint32_t code) {
+  const uint32_t c = code & 7u;
+  const uint32_t mag = c < 2u ? (c ? 0x3F000000u : 0u)                       // 0, 0.5
+                               : (((126u + (c >> 1)) << 23) | ((c & 1u) << 22));  // 1 .. 6
+  return __uint_as_float(mag | ((code & 8u) << 28));
+}
+
+// value of a code: per token with the slice's fp32 scale, per group with the group's e8m0 byte
+template <bool PG>
+__device__ __forceinline__ float dq_value(uint32_t code, float scale, uint32_t e8) {
+  if constexpr (!PG) {
+    const int q = static_cast<int>(code << 28) >> 28;  // sign-extend the nibble
+    return static_cast<float>(q) * scale;
+  } else {
+    const float v = __builtin_amdgcn_ldexpf(e2m1_float(code), static_cast<int>(e8) - 127);
+    return e8 == 255u ? __uint_as_float(0x7FC00000u) : v;
+  }
+}
+
+// Fast path: unit u covers elements 32u .. 32u+31 of the flattened [K, M*N] tensor, all in
+// slice u / (MN/32).
+template <int DT, bool PG>
+__global__ __launch_bounds__(kDqThreads) void dequant32_kernel(const uint8_t* __restrict__ codes,
+                                                                const void* __restrict__ scale,
+                                                                uint16_t* __restrict__ out, uint32_t units,
+                                                                uint32_t units_per_slice, uint32_t e8_per_slice) {
+  const uint32_t u = blockIdx.x * kDqThreads + threadIdx.x;
+  if (u >= units) return;
+  const uint32_t k = u / units_per_slice;
+  const u32x4_t c = reinterpret_cast<const u32x4_t*>(codes)[u];
+  float sc = 0.0f;
+  uint32_t e8 = 0;
+  if constexpr (!PG)
+    sc = static_cast<const float*>(scale)[k];
+  else
+    e8 = static_cast<const uint8_t*>(scale)[static_cast<uint64_t>(k) * e8_per_slice + (u - k * units_per_slice)];
+  u32x4_t* dst = reinterpret_cast<u32x4_t*>(out) + static_cast<uint64_t>(u) * 4;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {  // word w of the codes: elements 8w .. 8w+7
+    u32x4_t o;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t lo = (c[w] >> (8 * p)) & 15u, hi = (c[w] >> (8 * p + 4)) & 15u;
+      o[p] = round16x2<DT>(dq_value<PG>(lo, sc, e8), dq_value<PG>(hi, sc, e8));
+    }
+    dst[w] = o;
+  }
+}
+
+// Any shape: a thread per code byte (elements 2b and 2b+1; M*N is even, so a byte never
+// spans two slices).
+template <int DT, bool PG>
+__global__ __launch_bounds__(kDqThreads) void dequant_bytes_kernel(const uint8_t* __restrict__ codes,
+                                                                    const void* __restrict__ scale,
+                                                                    uint16_t* __restrict__ out, uint64_t bytes,
+                                                                    uint64_t mn, uint32_t e8_per_slice) {
+  const uint64_t bi = static_cast<uint64_t>(blockIdx.x) * kDqThreads + threadIdx.x;
+  if (bi >= bytes) return;
+  const uint64_t e = 2 * bi, k = e / mn, f = e - k * mn;
+  const uint32_t byte = codes[bi];
+  float sc = 0.0f;
+  uint32_t e8 = 0;
+  if constexpr (!PG)
+    sc = static_cast<const float*>(scale)[k];
+  else
+    e8 = static_cast<const uint8_t*>(scale)[k * e8_per_slice + f / 32];
+  reinterpret_cast<uint32_t*>(out)[bi] = round16x2<DT>(dq_value<PG>(byte & 15u, sc, e8), dq_value<PG>(byte >> 4, sc, e8));
+}
+
+template <int DT, bool PG>
+hipError_t launch_dq(int64_t K, int64_t MN, const uint8_t* codes, const void* scale, uint16_t* out,
+                     hipStream_t s) {
+  const uint32_t e8_per_slice = static_cast<uint32_t>(e8m0_bytes_per_slice(MN));
+  const bool aligned = (reinterpret_cast<uintptr_t>(codes) % 16 == 0) && (reinterpret_cast<uintptr_t>(out) % 16 == 0);
+  if (MN % 32 == 0 && aligned) {
+    const uint64_t units = static_cast<uint64_t>(K) * (MN / 32);  // <= 2^29
+    const uint32_t grid = static_cast<uint32_t>((units + kDqThreads - 1) / kDqThreads);
+    dequant32_kernel<DT, PG><<<grid, kDqThreads, 0, s>>>(codes, scale, out, static_cast<uint32_t>(units),
+                                                          static_cast<uint32_t>(MN / 32), e8_per_slice);
+  } else {
+    const uint64_t bytes = static_cast<uint64_t>(K) * (MN / 2);
+    const uint64_t grid = (bytes + kDqThreads - 1) / kDqThreads;
+    dequant_bytes_kernel<DT, PG><<<static_cast<uint32_t>(grid), kDqThreads, 0, s>>>(
+        codes, scale, out, bytes, static_cast<uint64_t>(MN), e8_per_slice);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_dequant(int32_t dtype, bool per_group, int64_t K, int64_t M, int64_t N, const uint8_t* codes,
+                          const void* scale, uint16_t* out, hipStream_t s) {
+  const int64_t MN = M * N;
+  if (dtype == kBF16)
+    return per_group ? launch_dq<kBF16, true>(K, MN, codes, scale, out, s)
+                     : launch_dq<kBF16, false>(K, MN, codes, scale, out, s);
+  return per_group ? launch_dq<kF16, true>(K, MN, codes, scale, out, s)
+                   : launch_dq<kF16, false>(K, MN, codes, scale, out, s);
+}
+
+}  // namespace fq

@@ -342,6 +342,52 @@ void fq_executor_destroy(fq_executor* executor) {
   if (live(executor)) release(executor);
 }
 
+fq_status fq_dequant(const fq_tensor* codes, const fq_tensor* scale, const fq_tensor* out, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (!codes || !scale || !out || !codes->data || !scale->data || !out->data) return FQ_ERR_PARAM_NULLPTR;
+  // out: the values, [K, M, N] in x's dtype (its sizes fix K, M and N)
+  if (out->ndim != 3 || !strides_ok(*out)) return FQ_ERR_PARAM_INVALID;
+  const int64_t K = out->shape[0], M = out->shape[1], N = out->shape[2];
+  if (K < 1 || K > kMaxK || M < 1 || M > kMaxMN || N < 1 || N > kMaxMN) return FQ_ERR_PARAM_INVALID;
+  if (out->dtype != FQ_DT_FLOAT16 && out->dtype != FQ_DT_BFLOAT16) return FQ_ERR_PARAM_INVALID;
+  const int64_t MN = M * N;
+  // codes and scales as the quantizer writes them ([FQV2] 参数速查)
+  bool per_group;
+  switch (codes->dtype) {
+    case FQ_DT_INT32:
+      if (N % 8 != 0 || !shape_is(*codes, 3, K, M, N / 8)) return FQ_ERR_PARAM_INVALID;
+      per_group = false;
+      break;
+    case FQ_DT_INT4:
+      if (N % 2 != 0 || !shape_is(*codes, 3, K, M, N)) return FQ_ERR_PARAM_INVALID;
+      per_group = false;
+      break;
+    case FQ_DT_FLOAT4_E2M1:
+      if (N % 2 != 0 || !shape_is(*codes, 2, K, MN)) return FQ_ERR_PARAM_INVALID;
+      per_group = true;
+      break;
+    default:
+      return FQ_ERR_PARAM_INVALID;
+  }
+  if (per_group) {
+    if (scale->dtype != FQ_DT_FLOAT8_E8M0 || !shape_is(*scale, 3, K, ceil_div(MN, 64), 2)) return FQ_ERR_PARAM_INVALID;
+  } else {
+    if (scale->dtype != FQ_DT_FLOAT32 || !shape_is(*scale, 1, K)) return FQ_ERR_PARAM_INVALID;
+  }
+  // contiguous tensors only; the output is written 4 bytes at a time
+  if (!strides_ok(*codes) || !strides_ok(*scale) || !is_contiguous(*codes) || !is_contiguous(*scale) ||
+      !is_contiguous(*out))
+    return FQ_ERR_PARAM_INVALID;
+  if (reinterpret_cast<uintptr_t>(out->data) % 4 != 0 || (!per_group && reinterpret_cast<uintptr_t>(scale->data) % 4 != 0))
+    return FQ_ERR_PARAM_INVALID;
+  if (!device_is_gfx950()) return fail_runtime("the current device is not gfx950", hipSuccess);
+  const hipError_t err =
+      fq::launch_dequant(out->dtype == FQ_DT_FLOAT16 ? fq::kF16 : fq::kBF16, per_group, K, M, N,
+                         static_cast<const uint8_t*>(codes->data), scale->data, static_cast<uint16_t*>(out->data), stream);
+  if (err != hipSuccess) return fail_runtime("dequant kernel launch", err);
+  return FQ_SUCCESS;
+}
+
 fq_status fq_executor_set_repeatable(fq_executor* executor, int32_t repeat) {
   if (!executor) return FQ_ERR_PARAM_NULLPTR;
   if (!live(executor)) return FQ_ERR_PARAM_INVALID;

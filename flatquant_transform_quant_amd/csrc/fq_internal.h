@@ -48,6 +48,10 @@ hipError_t launch_mfma_small(const Problem& pb, const Buffers& b, hipStream_t s)
 bool mfma_wide_supports(const Problem& pb);
 hipError_t launch_mfma_wide(const Problem& pb, const Buffers& b, hipStream_t s);
 
+// Dequantization of contiguous codes/scales into a contiguous [K, M, N] 16-bit output.
+hipError_t launch_dequant(int32_t dtype, bool per_group, int64_t K, int64_t M, int64_t N, const uint8_t* codes,
+                          const void* scale, uint16_t* out, hipStream_t s);
+
 // Strided 16-bit gather into a contiguous buffer: dst[i0, i1, i2] = src[i0*s0 + i1*s1 + i2*s2].
 hipError_t launch_gather16(const uint16_t* src, uint16_t* dst, const int64_t shape[3],
                            const int64_t strides[3], hipStream_t s);

@@ -121,6 +121,28 @@ fq_status fq_get_workspace_size(const fq_tensor* x, const fq_tensor* kroneckerP1
  * Calls with distinct executors may come from different host threads. */
 fq_status fq_run(void* workspace, uint64_t workspaceSize, fq_executor* executor, hipStream_t stream);
 
+/* ---- dequantization ------------------------------------------------------------------
+ * The values of the codes fq_run writes, in a 16-bit float dtype: the second half of a
+ * quantize -> dequantize ("fake-quant") round trip, e.g. to measure the RMS error
+ * (the APT-LLM page, section 5.2, checks |dequantize(quantize(x)) - x| this way; the
+ * ModelOpt page, section 6.4, uses such a round trip as a reference).
+ *   per token (codes INT32 [K, M, N/8] or INT4 [K, M, N], scale FLOAT32 [K]):
+ *       value = q * scale[k], q the two's-complement int4 code (the APT-LLM page, section
+ *       2.1: the symmetric integer format dequantizes as q * scale)
+ *   per group (codes FLOAT4_E2M1 [K, M*N], scale FLOAT8_E8M0 [K, ceilDiv(M*N, 64), 2]):
+ *       value = E2M1(code) * 2^(e8m0 - 127), E2M1 magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 with
+ *       the sign bit on top (the ModelOpt page, section 6.1; [FQV2] 第3步 pergroup)
+ * The product is formed in IEEE fp32 (per group it is exact, or overflows to infinity; an
+ * e8m0 byte 0xFF, NaN in the MX encoding, makes its group NaN) and rounded once, to
+ * nearest even, to out's dtype.
+ *   out   FLOAT16 | BFLOAT16 [K, M, N]; K, M, N in the ranges of x above; 4-byte aligned.
+ * All three tensors must be contiguous device memory owned by the caller (valid until the
+ * work completes on the stream).  The work is enqueued on `stream` without synchronizing;
+ * no workspace.  Errors: a NULL tensor or data pointer -> FQ_ERR_PARAM_NULLPTR; any shape,
+ * dtype, stride or alignment mismatch -> FQ_ERR_PARAM_INVALID (these checks make no HIP
+ * call); not a gfx950 device, or a launch failure -> FQ_ERR_RUNTIME. */
+fq_status fq_dequant(const fq_tensor* codes, const fq_tensor* scale, const fq_tensor* out, hipStream_t stream);
+
 /* Releases an executor that will not be run (or a repeatable one).  NULL is a no-op. */
 void fq_executor_destroy(fq_executor* executor);
 

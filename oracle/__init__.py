@@ -75,6 +75,9 @@ def lib():
         for fn in ("fqo_round_f32", "fqo_round_bf16", "fqo_round_f16"):
             getattr(L, fn).argtypes = [ctypes.c_double]
             getattr(L, fn).restype = ctypes.c_double
+        L.fqo_dequant.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                  p, p, p]
+        L.fqo_dequant.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -206,3 +209,34 @@ def run_codes_only(x, p1, p2, dtype, mode, clip_ratio=1.0, dst_type_max=0.0, nth
     if rc != 0:
         raise ValueError(f"fqo_run failed ({rc})")
     return packed, sc
+
+
+def dequant(packed: np.ndarray, scale: np.ndarray, M: int, N: int, dtype: str, mode: str) -> np.ndarray:
+    """Values of the codes (uint16 bits of the output dtype, [S, M, N]): q * scale per
+    token, E2M1 value * 2^(e8m0 - 127) per group (see fqo_dequant in fq_oracle.c).
+
+    packed: [S, M*N/2] bytes as the quantizer writes them (low nibble first); scale: fp32
+    [S] per token ("int32" / "int4"), e8m0 bytes [S, 2*ceil(M*N/64)] per group ("fp4")."""
+    S = packed.shape[0]
+    packed = np.ascontiguousarray(packed, dtype=np.uint8).reshape(S, M * N // 2)
+    if mode in ("int32", "int4"):
+        scale = np.ascontiguousarray(scale, dtype=np.float32).reshape(S)
+        m = PER_TOKEN
+    elif mode == "fp4":
+        scale = np.ascontiguousarray(scale, dtype=np.uint8).reshape(S, -1)
+        m = PER_GROUP
+    else:
+        raise ValueError(f"unknown mode {mode!r}")
+    out = np.empty((S, M, N), np.uint16)
+    st = lib().fqo_dequant(_DT[dtype], m, S, M, N, packed.ctypes.data, scale.ctypes.data, out.ctypes.data)
+    if st != 0:
+        raise ValueError(f"fqo_dequant rejected the arguments ({st})")
+    return out
+
+
+def dt_to_float(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """float64 values of 16-bit dtype bits (exact)."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    if _DT[dtype] == BF16:
+        return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return bits.view(np.float16).astype(np.float64)

@@ -567,3 +567,69 @@ int fqo_run(const fqo_params* p, const uint16_t* x, const uint16_t* p1, const ui
   }
   return status;
 }
+
+/* ---- dequantization (the second half of a fake-quant round trip) ---------
+ * The APT-LLM page, section 2.1: the symmetric integer format dequantizes as
+ * q * scale.  Per group, an element is the value of its E2M1 code ([MOCONV]
+ * 6.1's magnitudes, sign bit on top) times the group's e8m0 power of two
+ * 2^(e - 127) ([FQV2] 第3步 pergroup).  The ModelOpt page, section 6.4, uses
+ * such a quantize -> dequantize round trip as a reference, and the APT-LLM
+ * page, section 5.2, checks the RMS of dequantize(quantize(x)) - x.
+ * Readings: the product is formed in IEEE fp32 (per token a C float
+ * multiply; per group the exact product rounded once to fp32, so 6 * 2^127
+ * overflows to inf) and rounded once, to nearest even, to the output dtype
+ * (overflow to inf).  An e8m0 byte 0xFF is NaN (the OCP MX encoding), and so
+ * is every element of its group.  Codes are read from the packed layouts the
+ * quantizer writes: [S, M*N/2] bytes, low nibble = lower flattened index
+ * (INT32 and INT4 outputs are byte-identical); e8m0 [S, 2*ceil(M*N/64)].
+ */
+
+/* bits of a value already representable in the format (after round_dt) */
+static uint16_t bf16_bits(double v) {
+  float f = (float)v; /* exact: v is a bf16 value, and bf16 values are fp32 values */
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if (isnan(v)) return 0x7FC0;
+  return (uint16_t)(u >> 16);
+}
+
+static uint16_t f16_bits(double v) {
+  if (isnan(v)) return 0x7E00;
+  uint16_t s = signbit(v) ? 0x8000 : 0;
+  double a = fabs(v);
+  if (isinf(a)) return s | 0x7C00;
+  if (a == 0.0) return s;
+  if (a < ldexp(1.0, -14)) return s | (uint16_t)ldexp(a, 24); /* subnormal: multiple of 2^-24 */
+  int ex;
+  double m = frexp(a, &ex);  /* a = m 2^ex, m in [0.5, 1) */
+  int e = ex - 1;            /* a = (2m) 2^e, 2m in [1, 2) */
+  uint16_t mant = (uint16_t)ldexp(2.0 * m - 1.0, 10);
+  return s | (uint16_t)((e + 15) << 10) | mant;
+}
+
+int fqo_dequant(int dtype, int mode, int64_t S, int64_t M, int64_t N, const uint8_t* packed,
+                const void* scale, uint16_t* out) {
+  if (dtype != FQO_F16 && dtype != FQO_BF16) return -1;
+  if (mode != FQO_PER_TOKEN && mode != FQO_PER_GROUP) return -1;
+  const int64_t MN = M * N;
+  if (M < 1 || N < 1 || MN % 2 != 0) return -1;
+  const int64_t gs = 2 * ceil_div(MN, 64); /* e8m0 bytes per slice */
+  for (int64_t k = 0; k < S; ++k) {
+    const uint8_t* pk = packed + k * (MN / 2);
+    for (int64_t f = 0; f < MN; ++f) {
+      const int nib = (pk[f >> 1] >> (4 * (f & 1))) & 15;
+      double v;
+      if (mode == FQO_PER_TOKEN) {
+        const int q = nib >= 8 ? nib - 16 : nib;          /* two's complement nibble */
+        const float prod = (float)q * ((const float*)scale)[k]; /* IEEE fp32 product */
+        v = (double)prod;
+      } else {
+        const int e = ((const uint8_t*)scale)[k * gs + f / 32];
+        v = e == 255 ? NAN : fqo_round_f32(ldexp(fqo_e2m1_value(nib), e - 127));
+      }
+      const double r = round_dt(v, dtype);
+      out[k * MN + f] = dtype == FQO_BF16 ? bf16_bits(r) : f16_bits(r);
+    }
+  }
+  return 0;
+}

@@ -34,6 +34,11 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(fq.EXPORTS)
 
 
+def _no_gpu():
+    import torch
+    return torch.cuda.device_count() == 0
+
+
 def tens(dtype, shape, strides=None, data=DUMMY):
     return fq.make_tensor(data, dtype, shape, strides)
 
@@ -238,11 +243,15 @@ def test_run_argument_checks_without_device():
     assert fq.fq_run(DUMMY, ws2 - 1, ex2, 0) == INVAL  # too small
     fq.fq_executor_destroy(ex2)
     assert fq.fq_executor_set_repeatable(ex2, True) == INVAL  # released
-    # single-use executor: released by fq_run even when it fails (here: no device)
-    st = fq.fq_run(0, 0, ex, 0)
-    assert st in (fq.FQ_ERR_RUNTIME, OK)
-    assert fq.fq_run(0, 0, ex, 0) == INVAL
-    assert fq.fq_executor_kernel(ex) < 0
+    # single-use executor: released by fq_run even when it fails (here: no device).  The
+    # dummy pointers must never reach a kernel, so this part runs only without a GPU.
+    if _no_gpu():
+        st = fq.fq_run(0, 0, ex, 0)
+        assert st == fq.FQ_ERR_RUNTIME
+        assert fq.fq_run(0, 0, ex, 0) == INVAL
+        assert fq.fq_executor_kernel(ex) < 0
+    else:
+        fq.fq_executor_destroy(ex)
 
 
 def test_kernel_selection_api():
@@ -272,3 +281,59 @@ def test_one_hip_runtime_per_process():
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr
     assert r.stdout.strip().splitlines()[-1] == "1"
+
+
+# ---------------------------------------------------------------- fq_dequant arguments
+# (every case is rejected before any HIP call, so no pointer is ever dereferenced)
+
+def dq_args(mode="int32", K=4, M=16, N=16, dt=fq.DT_BFLOAT16):
+    out = tens(dt, (K, M, N))
+    if mode == "int32":
+        return tens(fq.DT_INT32, (K, M, N // 8)), tens(fq.DT_FLOAT32, (K,)), out
+    if mode == "int4":
+        return tens(fq.DT_INT4, (K, M, N)), tens(fq.DT_FLOAT32, (K,)), out
+    return tens(fq.DT_FLOAT4_E2M1, (K, M * N)), tens(fq.DT_FLOAT8_E8M0, (K, -(-(M * N) // 64), 2)), out
+
+
+def test_dequant_null_is_161001():
+    c, s, o = dq_args()
+    assert fq.fq_dequant(None, s, o, 0) == NULLP
+    assert fq.fq_dequant(c, None, o, 0) == NULLP
+    assert fq.fq_dequant(c, s, None, 0) == NULLP
+    assert fq.fq_dequant(c, s, tens(fq.DT_BFLOAT16, (4, 16, 16), data=0), 0) == NULLP
+
+
+@pytest.mark.parametrize("case", ["out_dtype", "out_rank", "K0", "M257", "codes_shape", "codes_dtype",
+                                  "scale_dtype", "scale_shape", "e8m0_shape", "strided_out",
+                                  "strided_codes", "misaligned_out", "int32_N", "mixed_mode"])
+def test_dequant_invalid_is_161002(case):
+    c, s, o = dq_args("fp4" if case in ("e8m0_shape", "mixed_mode") else "int32")
+    if case == "out_dtype":
+        o = tens(fq.DT_FLOAT32, (4, 16, 16))
+    elif case == "out_rank":
+        o = tens(fq.DT_BFLOAT16, (4, 256))
+    elif case == "K0":
+        c, s, o = tens(fq.DT_INT32, (0, 16, 2)), tens(fq.DT_FLOAT32, (0,)), tens(fq.DT_BFLOAT16, (0, 16, 16))
+    elif case == "M257":
+        c, s, o = dq_args("int32", M=257)
+    elif case == "codes_shape":
+        c = tens(fq.DT_INT32, (4, 16, 4))
+    elif case == "codes_dtype":
+        c = tens(fq.DT_FLOAT32, (4, 16, 2))
+    elif case == "scale_dtype":
+        s = tens(fq.DT_FLOAT8_E8M0, (4,))
+    elif case == "scale_shape":
+        s = tens(fq.DT_FLOAT32, (5,))
+    elif case == "e8m0_shape":
+        s = tens(fq.DT_FLOAT8_E8M0, (4, 3, 2))
+    elif case == "strided_out":
+        o = tens(fq.DT_BFLOAT16, (4, 16, 16), (512, 32, 1))
+    elif case == "strided_codes":
+        c = tens(fq.DT_INT32, (4, 16, 2), (64, 4, 1))
+    elif case == "misaligned_out":
+        o = tens(fq.DT_BFLOAT16, (4, 16, 16), data=DUMMY + 2)
+    elif case == "int32_N":
+        c, s, o = tens(fq.DT_INT32, (4, 16, 1)), tens(fq.DT_FLOAT32, (4,)), tens(fq.DT_BFLOAT16, (4, 16, 12))
+    elif case == "mixed_mode":
+        s = tens(fq.DT_FLOAT32, (4,))
+    assert fq.fq_dequant(c, s, o, 0) == INVAL

@@ -409,3 +409,87 @@ def test_example_shapes_from_page():
         nib = ((words.astype(np.int64) >> (4 * i)) & 0xF)
         assert np.array_equal(np.where(nib >= 8, nib - 16, nib), lv[:, :, i::8])
     assert r["scale"].shape == (K,)
+
+
+# ---------------------------------------------------------------- dequantization
+# Pins of oracle.dequant against independent routines: numpy's IEEE fp32 arithmetic and
+# ldexp, numpy's fp32 -> fp16 cast and torch's fp32 -> bf16 cast (both round to nearest
+# even), and the E2M1 magnitudes the ModelOpt page prints (section 6.1, tests/golden).
+
+
+def _to_dt_bits(v32, dtype):
+    v32 = np.asarray(v32, dtype=np.float32)
+    if dtype == "bf16":
+        return torch.from_numpy(v32.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return v32.astype(np.float16).view(np.uint16)
+
+
+def _same_bits(got, want, dtype):
+    """Equal bits, NaN for NaN (any payload)."""
+    g = oracle.dt_to_float(got, dtype)
+    w = oracle.dt_to_float(want, dtype)
+    nan = np.isnan(w)
+    assert np.array_equal(np.isnan(g), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_dequant_per_group_every_code_and_e8m0(dtype):
+    # one slice of 32 * 256 elements: group g = e8m0 byte g, element j of a group = code j % 16
+    M, N = 256, 32
+    codes = np.tile(np.arange(16, dtype=np.uint8), 2 * 256)            # [256 * 32]
+    packed = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)[None, :]
+    e8 = np.zeros((1, 2 * (-(-M * N // 64))), np.uint8)
+    e8[0, :256] = np.arange(256, dtype=np.uint8)
+    got = oracle.dequant(packed, e8, M, N, dtype, "fp4").reshape(-1)
+    page = np.array([float(v) for v in keyed("e2m1_table.txt")["magnitudes"]])
+    mag = page[codes & 7] * np.where(codes & 8, -1.0, 1.0)
+    e = np.repeat(np.arange(256), 32)
+    with np.errstate(over="ignore"):
+        v32 = np.ldexp(mag, e - 127).astype(np.float32)              # exact, or inf
+    v32[e == 255] = np.nan
+    _same_bits(got, _to_dt_bits(v32, dtype), dtype)
+    assert (got[(codes == 8) & (e < 255)] == 0x8000).all()  # -0 keeps its sign
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_dequant_per_token_every_code_against_fp32_product(dtype):
+    rng = np.random.default_rng(7)
+    scales = np.concatenate([
+        np.array([0.0, 1e-45, 1.2e-38, 2.0 ** -20, 0.125, 1.0, 7.0 / 3.0, 1e4, 9362.0, 3e37, 3.3e38],
+                 np.float32),
+        (rng.standard_normal(53) * np.exp(rng.uniform(-30, 30, 53))).astype(np.float32).__abs__()])
+    S, M, N = scales.size, 2, 8
+    codes = np.tile(np.arange(16, dtype=np.uint8), S).reshape(S, 16)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    got = oracle.dequant(packed, scales, M, N, dtype, "int4").reshape(S, 16)
+    q = np.where(codes >= 8, codes.astype(np.int32) - 16, codes.astype(np.int32)).astype(np.float32)
+    with np.errstate(over="ignore"):
+        v32 = q * scales[:, None]                                     # IEEE fp32 product
+    _same_bits(got.reshape(-1), _to_dt_bits(v32, dtype).reshape(-1), dtype)
+
+
+@pytest.mark.parametrize("mode", ["int4", "fp4"])
+def test_dequant_round_trip_error_bound(mode):
+    # |value - y| is at most half the quantization step (the codes are nearest), plus the
+    # output dtype's half unit in the last place
+    w = synth.WORKLOADS["c2"]
+    x, p1, p2 = synth.make_inputs(w, 0, 6)
+    r = oracle.run(x, p1, p2, w.dtype, mode, clip_ratio=1.0, dst_type_max=0.0, ranges=False, want_y=True)
+    M, N = w.M, w.N
+    scale = r["scale"] if mode == "int4" else r["e8m0"]
+    v = oracle.dt_to_float(oracle.dequant(r["packed"], scale, M, N, "bf16", mode), "bf16").reshape(6, -1)
+    y = r["y"].reshape(6, -1).astype(np.float64)
+    half_ulp = np.abs(v) * 2.0 ** -8
+    if mode == "int4":
+        step = r["scale"].astype(np.float64)[:, None]
+        assert (np.abs(v - y) <= 0.5 * step * (1 + 1e-6) + half_ulp).all()
+    else:
+        # E2M1 spacing at |y|'s level: 0.5 below 2, 1 in [2, 4), 2 at and above 4 (x 2^(e-127));
+        # values beyond 6 * 2^(e-127) saturate (V1 makes the group max land in [4, 8))
+        e = np.repeat(r["e8m0"][:, : (M * N) // 32].astype(np.float64), 32, axis=1)
+        unit = np.ldexp(1.0, (e - 127).astype(int))
+        a = np.abs(y) / unit
+        spacing = np.where(a < 2, 0.5, np.where(a < 4, 1.0, 2.0)) * unit
+        sat = np.maximum(np.abs(y) - 6 * unit, 0)
+        assert (np.abs(v - y) <= 0.5 * spacing * (1 + 1e-6) + sat + half_ulp).all()
