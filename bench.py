@@ -39,6 +39,16 @@ def algorithmic_bytes(w, K=None) -> int:
     return b
 
 
+def dequant_bytes(w, K=None) -> int:
+    """Bytes one dequantization launch must move: read the codes (0.5 B/elem) and scales,
+    write the values (2 B/elem)."""
+    K = w.K if K is None else K
+    MN = w.M * w.N
+    b = K * MN // 2 + 2 * K * MN
+    b += K * 2 * (-(-MN // 64)) if w.mode == "fp4" else 4 * K
+    return b
+
+
 def algorithmic_flops(w, K=None) -> int:
     K = w.K if K is None else K
     f = 2 * w.M * w.M * w.N
@@ -60,13 +70,15 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def profiled_traffic(w):
+def profiled_traffic(w, op="quantize"):
     """HBM bytes per launch from the committed rocprofv3 counter summary of this workload
     (FETCH_SIZE and WRITE_SIZE, each scaled against a copy kernel of known size), or None
     when there is none or the kernels have changed since the counters were taken."""
     import glob
 
     for f in glob.glob(os.path.join(ROOT, "profiles", f"*_{w.name}.md")):
+        if os.path.basename(f).startswith("dequant_") != (op == "dequant"):
+            continue
         with open(f, encoding="utf-8") as fh:
             for line in fh:
                 if line.startswith("machine-readable:"):
@@ -107,6 +119,24 @@ def cpu_baseline(w, x_host, p1, p2, budget_s: float = 10.0):
             "sample": f"{what} ({elems} elements), {dt:.2f} s wall on {threads} threads"}
 
 
+def cpu_baseline_dequant(w, packed, scale, budget_s: float = 10.0):
+    """The oracle's dequantization (single thread) on the host, over as many passes of the
+    workload's codes as fit the budget, scaled to Gelem/s."""
+    import oracle
+
+    t = time.perf_counter()
+    oracle.dequant(packed, scale, w.M, w.N, w.dtype, w.mode)
+    dt0 = time.perf_counter() - t
+    reps = max(1, min(50, int(budget_s / max(dt0, 1e-6))))
+    t = time.perf_counter()
+    for _ in range(reps):
+        oracle.dequant(packed, scale, w.M, w.N, w.dtype, w.mode)
+    dt = time.perf_counter() - t
+    elems = reps * w.K * w.M * w.N
+    return {"value": elems / dt / 1e9, "unit": "Gelem/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} passes over all {w.K} slices ({elems} elements), {dt:.2f} s wall on 1 thread"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,6 +146,8 @@ def main() -> int:
     ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 generic, 2 mfma-small, 3 mfma-wide")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--op", default="quantize", choices=["quantize", "dequant"],
+                    help="quantize (the fused operator, default) or dequant (codes + scales -> values)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this operator shards over K with no communication, and "
@@ -137,6 +169,8 @@ def main() -> int:
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(tdt).to(dev)
 
     x_host, p1, p2 = synth.make_inputs(w)
+    if args.op == "dequant":
+        return bench_dequant(args, w, x_host, p1, p2, to_dev, dev, tdt)
     # rotate input/output sets so one lap touches > 2x the 256 MB last-level cache
     per_set = algorithmic_bytes(w)
     nsets = int(max(1, min(8, -(-(600 * 2 ** 20) // per_set))))
@@ -214,6 +248,78 @@ def main() -> int:
         "config": {"workload": w.name, "K": w.K, "M": w.M, "N": w.N, "mode": w.mode,
                    "clip_ratio": w.clip_ratio, "dst_type_max": w.dst_type_max,
                    "two_sided": w.two_sided, "buffer_sets": nsets, "parallelism": "none"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def bench_dequant(args, w, x_host, p1, p2, to_dev, dev, tdt):
+    """Times fq_dequant on the codes and scales the quantizer makes for the workload."""
+    import torch
+
+    import flatquant_transform_quant_amd as fq
+
+    per_set = dequant_bytes(w)
+    nsets = int(max(1, min(8, -(-(600 * 2 ** 20) // per_set))))
+    x = to_dev(x_host)
+    p1d = to_dev(p1)
+    p2d = to_dev(p2) if p2 is not None else None
+    codes = [fq.empty_outputs(w.K, w.M, w.N, w.mode, dev) for _ in range(nsets)]
+    for out, sc in codes:
+        fq.quantize(x, p1d, p2d, out, sc, w.mode, w.clip_ratio, w.dst_type_max)
+    del x
+    vals = [torch.empty((w.K, w.M, w.N), dtype=tdt, device=dev) for _ in range(nsets)]
+    stream = torch.cuda.Stream(dev)
+    torch.cuda.synchronize()
+
+    def step(i):
+        out, sc = codes[i % nsets]
+        fq.dequantize(out, sc, w.mode, w.M, w.N, tdt, out=vals[i % nsets], stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms = total_ms / args.steps  # one launch per step, back to back on `stream`
+    elems = w.K * w.M * w.N
+    bytes_ = dequant_bytes(w)
+    gbs = bytes_ / (ms / 1e3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": profiled_traffic(w, "dequant"),
+            "kernel": "dequant32_kernel" if (w.M * w.N) % 32 == 0 else "dequant_bytes_kernel",
+            "avg_launch_us": round(ms * 1e3, 3), "algorithmic_bytes": bytes_}
+    cpu = None
+    if not args.no_cpu:
+        import numpy as np
+
+        out, sc = codes[0]
+        packed = out.contiguous().view(torch.uint8).reshape(w.K, -1).cpu().numpy()
+        scale = (sc.contiguous().view(torch.uint8).reshape(w.K, -1) if w.mode == "fp4" else sc).cpu().numpy()
+        cpu = cpu_baseline_dequant(w, np.ascontiguousarray(packed), np.ascontiguousarray(scale), args.cpu_budget)
+    line = {
+        "metric": "Gelem/s dequantized (codes of x[K,M,N] -> values) + % of HBM roofline, 1 MI355X",
+        "value": round(elems * args.steps / (total_ms / 1e3) / 1e9, 2),
+        "unit": "Gelem/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "op": "dequant", "K": w.K, "M": w.M, "N": w.N, "mode": w.mode,
+                   "buffer_sets": nsets, "parallelism": "none"},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -14,10 +14,8 @@
 // K * M*N/2 bytes, low nibble = lower flattened index; e8m0 [K, 2*ceil(M*N/64)] bytes.
 //
 // HBM-bound streaming (0.5 byte in, 2 bytes out per element).  Slices whose element
-// count is a multiple of 32 take the fast path: a thread turns 32 consecutive codes (one
-// 16-byte load; per group exactly one group) into 64 output bytes (four 16-byte stores),
-// so a wave reads 1 KB and writes 4 KB contiguously.  Other shapes take a thread per code
-// byte.
+// count is a multiple of 32 take the fast path (8 codes -> 16 bytes per lane and step, each
+// instruction of a wave one contiguous run); other shapes take a thread per code byte.
 #include <hip/hip_runtime.h>
 
 #include "fq_codec.h"
@@ -50,33 +48,35 @@ __device__ __forceinline__ float dq_value(uint32_t code, float scale, uint32_t e
   }
 }
 
-// Fast path: unit u covers elements 32u .. 32u+31 of the flattened [K, M*N] tensor, all in
-// slice u / (MN/32).
+// Fast path: a wave covers 2048 consecutive elements of the flattened [K, M*N] tensor in
+// four steps; at step w lane l turns the 8 codes of elements base + 512w + 8l .. +7 (one
+// dword) into 16 output bytes, so every load and store instruction of the wave touches one
+// contiguous run (256 B of codes, 1 KB of values).  An 8-element run never leaves its slice
+// or its 32-group (M*N is a multiple of 32).
 template <int DT, bool PG>
 __global__ __launch_bounds__(kDqThreads) void dequant32_kernel(const uint8_t* __restrict__ codes,
                                                                 const void* __restrict__ scale,
-                                                                uint16_t* __restrict__ out, uint32_t units,
-                                                                uint32_t units_per_slice, uint32_t e8_per_slice) {
-  const uint32_t u = blockIdx.x * kDqThreads + threadIdx.x;
-  if (u >= units) return;
-  const uint32_t k = u / units_per_slice;
-  const u32x4_t c = reinterpret_cast<const u32x4_t*>(codes)[u];
-  float sc = 0.0f;
-  uint32_t e8 = 0;
-  if constexpr (!PG)
-    sc = static_cast<const float*>(scale)[k];
-  else
-    e8 = static_cast<const uint8_t*>(scale)[static_cast<uint64_t>(k) * e8_per_slice + (u - k * units_per_slice)];
-  u32x4_t* dst = reinterpret_cast<u32x4_t*>(out) + static_cast<uint64_t>(u) * 4;
+                                                                uint16_t* __restrict__ out, uint32_t runs,
+                                                                uint32_t runs_per_slice, uint32_t e8_per_slice) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t wave_run = (blockIdx.x * kDqThreads + (threadIdx.x & ~63u)) * 4;  // first 8-element run
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {  // word w of the codes: elements 8w .. 8w+7
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t r = wave_run + 64 * w + lane;  // this lane's run: elements 8r .. 8r+7
+    if (r >= runs) break;
+    const uint32_t c = reinterpret_cast<const uint32_t*>(codes)[r];
+    const uint32_t k = r / runs_per_slice;
+    float sc = 0.0f;
+    uint32_t e8 = 0;
+    if constexpr (!PG)
+      sc = static_cast<const float*>(scale)[k];
+    else
+      e8 = static_cast<const uint8_t*>(scale)[static_cast<uint64_t>(k) * e8_per_slice + (r - k * runs_per_slice) / 4];
     u32x4_t o;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t lo = (c[w] >> (8 * p)) & 15u, hi = (c[w] >> (8 * p + 4)) & 15u;
-      o[p] = round16x2<DT>(dq_value<PG>(lo, sc, e8), dq_value<PG>(hi, sc, e8));
-    }
-    dst[w] = o;
+    for (int p = 0; p < 4; ++p)
+      o[p] = round16x2<DT>(dq_value<PG>((c >> (8 * p)) & 15u, sc, e8), dq_value<PG>((c >> (8 * p + 4)) & 15u, sc, e8));
+    reinterpret_cast<u32x4_t*>(out)[r] = o;
   }
 }
 
@@ -106,10 +106,11 @@ hipError_t launch_dq(int64_t K, int64_t MN, const uint8_t* codes, const void* sc
   const uint32_t e8_per_slice = static_cast<uint32_t>(e8m0_bytes_per_slice(MN));
   const bool aligned = (reinterpret_cast<uintptr_t>(codes) % 16 == 0) && (reinterpret_cast<uintptr_t>(out) % 16 == 0);
   if (MN % 32 == 0 && aligned) {
-    const uint64_t units = static_cast<uint64_t>(K) * (MN / 32);  // <= 2^29
-    const uint32_t grid = static_cast<uint32_t>((units + kDqThreads - 1) / kDqThreads);
-    dequant32_kernel<DT, PG><<<grid, kDqThreads, 0, s>>>(codes, scale, out, static_cast<uint32_t>(units),
-                                                          static_cast<uint32_t>(MN / 32), e8_per_slice);
+    const uint64_t runs = static_cast<uint64_t>(K) * (MN / 8);  // <= 2^31
+    const uint64_t per_block = 4 * kDqThreads;                   // runs a workgroup covers
+    const uint32_t grid = static_cast<uint32_t>((runs + per_block - 1) / per_block);
+    dequant32_kernel<DT, PG><<<grid, kDqThreads, 0, s>>>(codes, scale, out, static_cast<uint32_t>(runs),
+                                                          static_cast<uint32_t>(MN / 8), e8_per_slice);
   } else {
     const uint64_t bytes = static_cast<uint64_t>(K) * (MN / 2);
     const uint64_t grid = (bytes + kDqThreads - 1) / kDqThreads;
