@@ -75,6 +75,9 @@ def _load():
     L.fq_status_string.restype = ctypes.c_char_p
     L.fq_last_error.argtypes = []
     L.fq_last_error.restype = ctypes.c_char_p
+    L.fq_v1_get_workspace_size.argtypes = [P, P, P, ctypes.c_double, P, P,
+                                           ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(vp)]
+    L.fq_v1_get_workspace_size.restype = ctypes.c_int32
     L.fq_dequant.argtypes = [P, P, P, vp]
     L.fq_dequant.restype = ctypes.c_int32
     return L
@@ -82,7 +85,7 @@ def _load():
 
 lib = _load()
 EXPORTS = ("fq_get_workspace_size", "fq_run", "fq_executor_destroy", "fq_executor_set_repeatable",
-           "fq_executor_set_kernel", "fq_executor_kernel", "fq_status_string", "fq_last_error", "fq_dequant")
+           "fq_executor_set_kernel", "fq_executor_kernel", "fq_status_string", "fq_last_error", "fq_dequant", "fq_v1_get_workspace_size")
 
 
 def status_string(status: int) -> str:
@@ -116,6 +119,17 @@ def fq_get_workspace_size(x: FqTensor, p1: FqTensor, p2: FqTensor, clip_ratio: f
     ref = lambda t: ctypes.byref(t) if t is not None else None  # noqa: E731
     st = lib.fq_get_workspace_size(ref(x), ref(p1), ref(p2), float(clip_ratio), float(dst_type_max),
                                    ref(out), ref(quant_scale), ctypes.byref(ws), ctypes.byref(ex))
+    return st, ws.value, ex.value
+
+
+def fq_v1_get_workspace_size(x: FqTensor, p1: FqTensor, p2: FqTensor, clip_ratio: float,
+                             out: FqTensor, quant_scale: FqTensor):
+    """The V1 form (no dstTypeMax). Returns (status, workspace_size, executor_handle)."""
+    ws = ctypes.c_uint64(0)
+    ex = ctypes.c_void_p(None)
+    ref = lambda t: ctypes.byref(t) if t is not None else None  # noqa: E731
+    st = lib.fq_v1_get_workspace_size(ref(x), ref(p1), ref(p2), float(clip_ratio), ref(out), ref(quant_scale),
+                                      ctypes.byref(ws), ctypes.byref(ex))
     return st, ws.value, ex.value
 
 

@@ -342,6 +342,13 @@ void fq_executor_destroy(fq_executor* executor) {
   if (live(executor)) release(executor);
 }
 
+fq_status fq_v1_get_workspace_size(const fq_tensor* x, const fq_tensor* kroneckerP1,
+                                   const fq_tensor* kroneckerP2, double clipRatio, const fq_tensor* out,
+                                   const fq_tensor* quantScale, uint64_t* workspaceSize, fq_executor** executor) {
+  // [FQV2] V1 还是 V2: V2 with dstTypeMax 0.0 is V1
+  return fq_get_workspace_size(x, kroneckerP1, kroneckerP2, clipRatio, 0.0, out, quantScale, workspaceSize, executor);
+}
+
 fq_status fq_dequant(const fq_tensor* codes, const fq_tensor* scale, const fq_tensor* out, hipStream_t stream) {
   g_last_error[0] = '\0';
   if (!codes || !scale || !out || !codes->data || !scale->data || !out->data) return FQ_ERR_PARAM_NULLPTR;

@@ -108,6 +108,14 @@ fq_status fq_get_workspace_size(const fq_tensor* x, const fq_tensor* kroneckerP1
                                 const fq_tensor* out, const fq_tensor* quantScale,
                                 uint64_t* workspaceSize, fq_executor** executor);
 
+/* The first stage in the V1 form ([FQV2] V1 还是 V2): the same call without dstTypeMax.
+ * The page states that V2 with dstTypeMax = 0.0 behaves exactly as V1, so this plans the
+ * V2 call with dstTypeMax = 0.0 -- same checks, same statuses, same executor, run with
+ * fq_run. */
+fq_status fq_v1_get_workspace_size(const fq_tensor* x, const fq_tensor* kroneckerP1,
+                                   const fq_tensor* kroneckerP2, double clipRatio, const fq_tensor* out,
+                                   const fq_tensor* quantScale, uint64_t* workspaceSize, fq_executor** executor);
+
 /* ---- second stage ------------------------------------------------------------------
  * Enqueues the fused computation on `stream` (0 = the null stream) and returns without
  * synchronizing.  `workspace` is device memory of at least workspaceSize bytes (may be

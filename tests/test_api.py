@@ -23,7 +23,7 @@ NULLP, INVAL, OK = fq.FQ_ERR_PARAM_NULLPTR, fq.FQ_ERR_PARAM_INVALID, fq.FQ_SUCCE
 def header_functions():
     src = open(os.path.join(ROOT, "include", "fq.h"), encoding="utf-8").read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(fq_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(fq_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_library_exports_every_declared_function():
@@ -337,3 +337,32 @@ def test_dequant_invalid_is_161002(case):
     elif case == "mixed_mode":
         s = tens(fq.DT_FLOAT32, (4,))
     assert fq.fq_dequant(c, s, o, 0) == INVAL
+
+
+# ---------------------------------------------------------------- the V1 form
+# ([FQV2] V1 还是 V2: V2 with dstTypeMax 0.0 behaves as V1)
+
+@pytest.mark.parametrize("mode", ["int32", "int4", "fp4"])
+@pytest.mark.parametrize("bad", [None, "clip", "dims", "p1", "out", "scale", "null"])
+def test_v1_form_matches_v2_with_dst_type_max_zero(mode, bad):
+    p = problem(mode=mode)
+    clip = 1.0
+    if bad == "clip":
+        clip = 1.5
+    elif bad == "dims":
+        p["x"] = tens(fq.DT_BFLOAT16, (4, 300, 16))
+    elif bad == "p1":
+        p["p1"] = tens(fq.DT_FLOAT16, (16, 16))
+    elif bad == "out":
+        p["out"] = tens(fq.DT_INT32, (4, 16, 3))
+    elif bad == "scale":
+        p["sc"] = tens(fq.DT_FLOAT32, (5,))
+    elif bad == "null":
+        p["out"] = None
+    st1, ws1, ex1 = fq.fq_v1_get_workspace_size(p["x"], p["p1"], p["p2"], clip, p["out"], p["sc"])
+    st2, ws2, ex2 = fq.fq_get_workspace_size(p["x"], p["p1"], p["p2"], clip, 0.0, p["out"], p["sc"])
+    for ex in (ex1, ex2):
+        if ex:
+            fq.fq_executor_destroy(ex)
+    assert (st1, ws1) == (st2, ws2)
+    assert (st1 == OK) == (bad is None)

@@ -205,3 +205,23 @@ def test_int32_and_int4_layouts_are_byte_identical():
     a = fetch(*run_lib(xd, p1d, p2d, "int32", w.clip_ratio, 0.0), "int32", K)
     b = fetch(*run_lib(xd, p1d, p2d, "int4", w.clip_ratio, 0.0), "int4", K)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("key", ["c2", "c3", "c5"])
+def test_v1_form_runs_like_v2_with_dst_type_max_zero(key):
+    """[FQV2] V1 还是 V2: the V1 call (no dstTypeMax) gives what V2 gives with dstTypeMax 0.0."""
+    w = synth.WORKLOADS[key]
+    K = 16
+    x, p1, p2 = synth.make_inputs(w, 0, K)
+    xd, p1d = to_dev(x, w.dtype), to_dev(p1, w.dtype)
+    p2d = to_dev(p2, w.dtype) if p2 is not None else torch.empty((0, 0), dtype=xd.dtype, device=DEV)
+    ref = fetch(*run_lib(xd, p1d, p2d if p2 is not None else None, w.mode, w.clip_ratio, 0.0), w.mode, K)
+    out, sc = fq.empty_outputs(K, w.M, w.N, w.mode, DEV)
+    st, ws, ex = fq.fq_v1_get_workspace_size(fq.describe_input(xd), fq.describe_input(p1d), fq.describe_input(p2d),
+                                             w.clip_ratio, fq.describe_out(out, w.mode, K, w.M, w.N),
+                                             fq.describe_scale(sc, w.mode))
+    assert st == fq.FQ_SUCCESS and ws == 0
+    assert fq.fq_run(0, 0, ex, torch.cuda.current_stream().cuda_stream) == fq.FQ_SUCCESS
+    torch.cuda.synchronize()
+    got = fetch(out, sc, w.mode, K)
+    assert np.array_equal(ref[0], got[0]) and np.array_equal(ref[1], got[1])
