@@ -58,12 +58,14 @@ def algorithmic_flops(w, K=None) -> int:
 
 
 def kernel_source_hash() -> str:
-    """Hash of the HIP sources; the profile summaries record it beside their counters."""
+    """Hash of the device code (the HIP sources and the headers they include, not the host
+    code); the profile summaries record it beside their counters."""
     import glob
     import hashlib
 
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "flatquant_transform_quant_amd", "csrc", "*"))):
+    csrc = os.path.join(ROOT, "flatquant_transform_quant_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:
             h.update(fh.read())
