@@ -78,6 +78,8 @@ def lib():
         L.fqo_dequant.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                   p, p, p]
         L.fqo_dequant.restype = ctypes.c_int
+        L.fqo_mx_gemm.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, p, p, p, p, p, p]
+        L.fqo_mx_gemm.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -240,3 +242,21 @@ def dt_to_float(bits: np.ndarray, dtype: str) -> np.ndarray:
     if _DT[dtype] == BF16:
         return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     return bits.view(np.float16).astype(np.float64)
+
+
+def mx_gemm(a: np.ndarray, a_e8: np.ndarray, w: np.ndarray, w_e8: np.ndarray, H: int):
+    """C [T, O] = dequant(a) . dequant(w)^T in double, and sum|terms| [T, O] (see
+    fqo_mx_gemm).  a [T, H/2] and w [O, H/2] are E2M1 code bytes (low nibble first); a_e8
+    and w_e8 the e8m0 bytes [rows, 2*ceil(H/64)]."""
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    a_e8 = np.ascontiguousarray(a_e8, dtype=np.uint8).reshape(a.shape[0], -1)
+    w_e8 = np.ascontiguousarray(w_e8, dtype=np.uint8).reshape(w.shape[0], -1)
+    T, O = a.shape[0], w.shape[0]
+    c = np.empty((T, O), np.float64)
+    cabs = np.empty((T, O), np.float64)
+    st = lib().fqo_mx_gemm(T, O, H, a.ctypes.data, a_e8.ctypes.data, w.ctypes.data, w_e8.ctypes.data,
+                           c.ctypes.data, cabs.ctypes.data)
+    if st != 0:
+        raise ValueError(f"fqo_mx_gemm rejected the arguments ({st})")
+    return c, cabs

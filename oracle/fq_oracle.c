@@ -633,3 +633,45 @@ int fqo_dequant(int dtype, int mode, int64_t S, int64_t M, int64_t N, const uint
   }
   return 0;
 }
+
+/* ---- MXFP4 consumer GEMM (the product that follows the quantizer) ----------
+ * C[t, o] = sum_h value(a[t, h]) * value(w[o, h]), value() the dequantization above
+ * (E2M1 code times its 32-group's 2^(e8m0 - 127)), both operands in the quantizer's
+ * per-group layout: codes [rows, H/2] bytes (low nibble first), e8m0 [rows, 2*ceil(H/64)].
+ * The products are exact in double and the H-term sums are accumulated in double (error
+ * below H 2^-53 sum|terms|); `c` receives the sums, `cabs` (if non-NULL) sum|terms|, from
+ * which the comparison derives the bound any fp32 accumulation order can reach.  e8m0
+ * bytes 0xFF are outside this function's domain (the quantizer never writes them). */
+int fqo_mx_gemm(int64_t T, int64_t O, int64_t H, const uint8_t* a, const uint8_t* a_e8, const uint8_t* w,
+                const uint8_t* w_e8, double* c, double* cabs) {
+  if (T < 1 || O < 1 || H < 2 || H % 32 != 0) return -1;
+  const int64_t gs = 2 * ceil_div(H, 64);
+  double* av = (double*)malloc(sizeof(double) * (size_t)H);
+  double* wv = (double*)malloc(sizeof(double) * (size_t)(O * H));
+  if (!av || !wv) { free(av); free(wv); return -2; }
+  for (int64_t o = 0; o < O; ++o)
+    for (int64_t h = 0; h < H; ++h) {
+      const int nib = (w[o * (H / 2) + h / 2] >> (4 * (h & 1))) & 15;
+      wv[o * H + h] = ldexp(fqo_e2m1_value(nib), (int)w_e8[o * gs + h / 32] - 127);
+    }
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t h = 0; h < H; ++h) {
+      const int nib = (a[t * (H / 2) + h / 2] >> (4 * (h & 1))) & 15;
+      av[h] = ldexp(fqo_e2m1_value(nib), (int)a_e8[t * gs + h / 32] - 127);
+    }
+    for (int64_t o = 0; o < O; ++o) {
+      double s = 0.0, sa = 0.0;
+      const double* wr = wv + o * H;
+      for (int64_t h = 0; h < H; ++h) {
+        const double p = av[h] * wr[h];
+        s += p;
+        sa += fabs(p);
+      }
+      c[t * O + o] = s;
+      if (cabs) cabs[t * O + o] = sa;
+    }
+  }
+  free(av);
+  free(wv);
+  return 0;
+}

@@ -493,3 +493,53 @@ def test_dequant_round_trip_error_bound(mode):
         spacing = np.where(a < 2, 0.5, np.where(a < 4, 1.0, 2.0)) * unit
         sat = np.maximum(np.abs(y) - 6 * unit, 0)
         assert (np.abs(v - y) <= 0.5 * spacing * (1 + 1e-6) + sat + half_ulp).all()
+
+
+# ---------------------------------------------------------------- MXFP4 consumer GEMM
+
+def _mx_random(rows, H, rng, lo=100, hi=150):
+    codes = rng.integers(0, 256, (rows, H // 2), dtype=np.uint8)
+    e8 = rng.integers(lo, hi, (rows, 2 * (-(-H // 64))), dtype=np.uint8)
+    return codes, e8
+
+
+def _mx_decode(codes, e8, H):
+    page = np.array([float(v) for v in keyed("e2m1_table.txt")["magnitudes"]])
+    nib = np.stack([codes & 15, codes >> 4], axis=-1).reshape(codes.shape[0], H)
+    val = page[nib & 7] * np.where(nib & 8, -1.0, 1.0)
+    return np.ldexp(val, np.repeat(e8[:, : H // 32].astype(int) - 127, 32, axis=1))
+
+
+def test_mx_gemm_against_numpy_matmul():
+    rng = np.random.default_rng(3)
+    T, O, H = 5, 7, 256
+    a, ae = _mx_random(T, H, rng)
+    w, we = _mx_random(O, H, rng)
+    c, cabs = oracle.mx_gemm(a, ae, w, we, H)
+    A, W = _mx_decode(a, ae, H), _mx_decode(w, we, H)
+    assert np.allclose(c, A @ W.T, rtol=1e-12, atol=0)
+    assert np.allclose(cabs, np.abs(A) @ np.abs(W).T, rtol=1e-12, atol=0)
+
+
+def test_mx_gemm_one_hot_weights_select_activations():
+    rng = np.random.default_rng(4)
+    T, H = 6, 128
+    a, ae = _mx_random(T, H, rng)
+    O = 8
+    cols = rng.integers(0, H, O)
+    w = np.zeros((O, H // 2), np.uint8)
+    for o, j in enumerate(cols):
+        w[o, j // 2] |= np.uint8(0x2 << (4 * (j % 2)))     # E2M1 code 2 = 1.0
+    we = np.full((O, 2 * (-(-H // 64))), 127, np.uint8)     # 2^0
+    c, _ = oracle.mx_gemm(a, ae, w, we, H)
+    A = _mx_decode(a, ae, H)
+    assert np.array_equal(c, A[:, cols])
+
+
+def test_mx_gemm_weight_scale_step_doubles_exactly():
+    rng = np.random.default_rng(5)
+    a, ae = _mx_random(4, 512, rng)
+    w, we = _mx_random(3, 512, rng)
+    c1, _ = oracle.mx_gemm(a, ae, w, we, 512)
+    c2, _ = oracle.mx_gemm(a, ae, w, we + 1, 512)
+    assert np.array_equal(c2, 2 * c1)
