@@ -52,6 +52,10 @@ hipError_t launch_mfma_wide(const Problem& pb, const Buffers& b, hipStream_t s);
 hipError_t launch_dequant(int32_t dtype, bool per_group, int64_t K, int64_t M, int64_t N, const uint8_t* codes,
                           const void* scale, uint16_t* out, hipStream_t s);
 
+// MXFP4 consumer GEMM over contiguous operands: C[T, O] = A[T, H] . W[O, H]^T (bf16 or fp32 C).
+hipError_t launch_mx_gemm(int64_t T, int64_t O, int64_t H, const uint8_t* a, const uint8_t* a_e8, const uint8_t* w,
+                          const uint8_t* w_e8, void* c, bool f32_out, hipStream_t s);
+
 // Strided 16-bit gather into a contiguous buffer: dst[i0, i1, i2] = src[i0*s0 + i1*s1 + i2*s2].
 hipError_t launch_gather16(const uint16_t* src, uint16_t* dst, const int64_t shape[3],
                            const int64_t strides[3], hipStream_t s);

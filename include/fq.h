@@ -151,6 +151,30 @@ fq_status fq_run(void* workspace, uint64_t workspaceSize, fq_executor* executor,
  * call); not a gfx950 device, or a launch failure -> FQ_ERR_RUNTIME. */
 fq_status fq_dequant(const fq_tensor* codes, const fq_tensor* scale, const fq_tensor* out, hipStream_t stream);
 
+/* ---- MXFP4 consumer GEMM ----------------------------------------------------------------
+ * The product that follows the quantizer in a FlatQuant linear layer:
+ *     C[t, o] = sum_h value(a[t, h]) * value(w[o, h])
+ * with both operands in the per-group format fq_run writes ([FQV2] 第3步 pergroup / 第4步:
+ * E2M1 codes, one e8m0 power of two per 32 consecutive elements of a row; the E2M1 values
+ * from the ModelOpt page, section 6.1), so the quantizer's out / quantScale of a FLOAT4_E2M1
+ * call feed it directly as a / a_scale (T = K, H = M*N).
+ *   a        FLOAT4_E2M1  [T, H]                     H a multiple of 128
+ *   a_scale  FLOAT8_E8M0  [T, ceilDiv(H, 64), 2]
+ *   w        FLOAT4_E2M1  [O, H]
+ *   w_scale  FLOAT8_E8M0  [O, ceilDiv(H, 64), 2]
+ *   c        BFLOAT16 | FLOAT32 [T, O]
+ * The products are accumulated in fp32 (the order is unspecified: the result lies within
+ * gamma(H) * sum|terms| of the exact sum, gamma(n) = n u / (1 - n u), u = 2^-24) and rounded
+ * once to c's dtype (round to nearest even).  Scales whose products leave the fp32 normal
+ * range, and the e8m0 byte 0xFF (NaN), are outside the supported domain; the quantizer
+ * writes neither.  All tensors contiguous device memory owned by the caller; a and w 16-byte
+ * aligned; (T + 128) * H / 2 and (O + 128) * H / 2 below 2^31.  Enqueued on `stream` without
+ * synchronizing; no workspace.  Errors: a NULL tensor or data pointer -> FQ_ERR_PARAM_NULLPTR;
+ * any shape, dtype, stride, size or alignment mismatch -> FQ_ERR_PARAM_INVALID (no HIP call
+ * is made before these checks); not a gfx950 device, or a launch failure -> FQ_ERR_RUNTIME. */
+fq_status fq_mx_gemm(const fq_tensor* a, const fq_tensor* a_scale, const fq_tensor* w, const fq_tensor* w_scale,
+                     const fq_tensor* c, hipStream_t stream);
+
 /* Releases an executor that will not be run (or a repeatable one).  NULL is a no-op. */
 void fq_executor_destroy(fq_executor* executor);
 

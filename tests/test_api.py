@@ -366,3 +366,44 @@ def test_v1_form_matches_v2_with_dst_type_max_zero(mode, bad):
             fq.fq_executor_destroy(ex)
     assert (st1, ws1) == (st2, ws2)
     assert (st1 == OK) == (bad is None)
+
+
+# ---------------------------------------------------------------- fq_mx_gemm arguments
+# (rejected before any HIP call)
+
+def mx_args(T=4, O=8, H=256, cdt=fq.DT_BFLOAT16):
+    G = -(-H // 64)
+    return [tens(fq.DT_FLOAT4_E2M1, (T, H)), tens(fq.DT_FLOAT8_E8M0, (T, G, 2)), tens(fq.DT_FLOAT4_E2M1, (O, H)),
+            tens(fq.DT_FLOAT8_E8M0, (O, G, 2)), tens(cdt, (T, O))]
+
+
+@pytest.mark.parametrize("which", range(5))
+def test_mx_gemm_null_is_161001(which):
+    args = mx_args()
+    args[which] = None
+    assert fq.fq_mx_gemm(*args, 0) == NULLP
+
+
+@pytest.mark.parametrize("case", ["H_not_128", "H_mismatch", "a_dtype", "scale_shape", "c_shape", "c_dtype",
+                                  "strided_a", "misaligned_a", "too_big"])
+def test_mx_gemm_invalid_is_161002(case):
+    args = mx_args()
+    if case == "H_not_128":
+        args = mx_args(H=192)
+    elif case == "H_mismatch":
+        args[2] = tens(fq.DT_FLOAT4_E2M1, (8, 384))
+    elif case == "a_dtype":
+        args[0] = tens(fq.DT_INT4, (4, 256))
+    elif case == "scale_shape":
+        args[1] = tens(fq.DT_FLOAT8_E8M0, (4, 3, 2))
+    elif case == "c_shape":
+        args[4] = tens(fq.DT_BFLOAT16, (8, 4))
+    elif case == "c_dtype":
+        args[4] = tens(fq.DT_FLOAT16, (4, 8))
+    elif case == "strided_a":
+        args[0] = tens(fq.DT_FLOAT4_E2M1, (4, 256), (512, 1))
+    elif case == "misaligned_a":
+        args[0] = tens(fq.DT_FLOAT4_E2M1, (4, 256), data=DUMMY + 8)
+    elif case == "too_big":
+        args = mx_args(T=1 << 18, H=1 << 14)
+    assert fq.fq_mx_gemm(*args, 0) == INVAL
