@@ -25,6 +25,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16/fp16 MFMA, TFLOP/s
+MFMA_FP4_PEAK_TFS = 10100.0    # MI355X dense fp4 MFMA, TFLOP/s
 
 
 def algorithmic_bytes(w, K=None) -> int:
@@ -148,8 +149,10 @@ def main() -> int:
     ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 generic, 2 mfma-small, 3 mfma-wide")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
-    ap.add_argument("--op", default="quantize", choices=["quantize", "dequant"],
-                    help="quantize (the fused operator, default) or dequant (codes + scales -> values)")
+    ap.add_argument("--op", default="quantize", choices=["quantize", "dequant", "mxgemm"],
+                    help="quantize (the fused operator, default), dequant (codes + scales -> values) or "
+                         "mxgemm (the MXFP4 GEMM consuming a per-group workload's output)")
+    ap.add_argument("--gemm-out", type=int, default=8192, help="mxgemm: output features O")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this operator shards over K with no communication, and "
@@ -173,6 +176,8 @@ def main() -> int:
     x_host, p1, p2 = synth.make_inputs(w)
     if args.op == "dequant":
         return bench_dequant(args, w, x_host, p1, p2, to_dev, dev, tdt)
+    if args.op == "mxgemm":
+        return bench_mx_gemm(args, w, x_host, p1, p2, to_dev, dev)
     # rotate input/output sets so one lap touches > 2x the 256 MB last-level cache
     per_set = algorithmic_bytes(w)
     nsets = int(max(1, min(8, -(-(600 * 2 ** 20) // per_set))))
@@ -322,6 +327,80 @@ def bench_dequant(args, w, x_host, p1, p2, to_dev, dev, tdt):
         "data": "synthetic",
         "config": {"workload": w.name, "op": "dequant", "K": w.K, "M": w.M, "N": w.N, "mode": w.mode,
                    "buffer_sets": nsets, "parallelism": "none"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def bench_mx_gemm(args, w, x_host, p1, p2, to_dev, dev):
+    """Times fq_mx_gemm with A = the workload's per-group quantizer output (T = K tokens,
+    H = M*N) and synthetic MXFP4 weights W [O, H] (seeded random codes and e8m0 scales)."""
+    import numpy as np
+    import torch
+
+    import flatquant_transform_quant_amd as fq
+
+    if w.mode != "fp4":
+        print("--op mxgemm needs a per-group (fp4) workload", file=sys.stderr)
+        return 2
+    T, H, O = w.K, w.M * w.N, args.gemm_out
+    x = to_dev(x_host)
+    a, a_sc = fq.empty_outputs(T, w.M, w.N, "fp4", dev)
+    fq.quantize(x, to_dev(p1), to_dev(p2) if p2 is not None else None, a, a_sc, "fp4", w.clip_ratio, w.dst_type_max)
+    del x
+    rng = np.random.default_rng(1234)
+    wc = torch.from_numpy(rng.integers(0, 256, (O, H // 2), dtype=np.uint8)).to(dev)
+    ws = torch.from_numpy(rng.integers(118, 128, (O, -(-H // 64), 2), dtype=np.uint8)).to(dev)
+    c = torch.empty((T, O), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.Stream(dev)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        fq.mx_gemm(a, a_sc, wc, ws, H, out=c, stream=stream)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        fq.mx_gemm(a, a_sc, wc, ws, H, out=c, stream=stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms = total_ms / args.steps
+    flops = 2 * T * O * H
+    tfs = flops / (ms / 1e3) / 1e12
+    bytes_ = T * H // 2 + O * H // 2 + (T + O) * 2 * (-(-H // 64)) + 2 * T * O
+    roof = {"bound": "mfma", "achieved": round(tfs, 1), "peak": MFMA_FP4_PEAK_TFS, "unit": "TFLOP/s",
+            "frac": round(tfs / MFMA_FP4_PEAK_TFS, 4), "traffic": None, "kernel": "mx_gemm_kernel",
+            "avg_launch_us": round(ms * 1e3, 3), "algorithmic_flops": flops, "algorithmic_bytes": bytes_,
+            "other_frac": round(bytes_ / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+
+        rows = 4
+        a_h = a[:rows].cpu().numpy()
+        ae_h = a_sc[:rows].reshape(rows, -1).cpu().numpy()
+        t = time.perf_counter()
+        oracle.mx_gemm(a_h, ae_h, wc.cpu().numpy(), ws.reshape(O, -1).cpu().numpy(), H)
+        dt = time.perf_counter() - t
+        cpu = {"value": 2 * rows * O * H / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+               "sample": f"{rows} of {T} rows of C ({rows * O} outputs, H = {H}), {dt:.2f} s wall on 1 thread"}
+    line = {
+        "metric": "TFLOP/s of the MXFP4 GEMM consuming the quantizer output + % of the fp4 MFMA roofline, 1 MI355X",
+        "value": round(tfs, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp4",
+        "data": "synthetic",
+        "config": {"workload": w.name, "op": "mxgemm", "T": T, "H": H, "O": O, "c": "bf16", "parallelism": "none"},
         "roofline": roof,
         "cpu_baseline": cpu,
     }
