@@ -412,7 +412,7 @@ fq_status fq_mx_gemm(const fq_tensor* a, const fq_tensor* a_scale, const fq_tens
   if ((c->dtype != FQ_DT_BFLOAT16 && c->dtype != FQ_DT_FLOAT32) || !shape_is(*c, 2, T, O)) return FQ_ERR_PARAM_INVALID;
   // 32-bit buffer offsets, with a tile's worth of rows past the end
   const int64_t lim = int64_t(1) << 31;
-  if ((T + 128) * (H / 2) >= lim || (O + 128) * (H / 2) >= lim || (T + 128) * gs >= lim || (O + 128) * gs >= lim)
+  if ((T + 256) * (H / 2) >= lim || (O + 256) * (H / 2) >= lim || (T + 256) * gs >= lim || (O + 256) * gs >= lim)
     return FQ_ERR_PARAM_INVALID;
   auto al = [](const void* p, uintptr_t n) { return reinterpret_cast<uintptr_t>(p) % n == 0; };
   if (!al(a->data, 16) || !al(w->data, 16) || !al(c->data, c->dtype == FQ_DT_FLOAT32 ? 4 : 2))

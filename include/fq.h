@@ -168,7 +168,7 @@ fq_status fq_dequant(const fq_tensor* codes, const fq_tensor* scale, const fq_te
  * once to c's dtype (round to nearest even).  Scales whose products leave the fp32 normal
  * range, and the e8m0 byte 0xFF (NaN), are outside the supported domain; the quantizer
  * writes neither.  All tensors contiguous device memory owned by the caller; a and w 16-byte
- * aligned; (T + 128) * H / 2 and (O + 128) * H / 2 below 2^31.  Enqueued on `stream` without
+ * aligned; (T + 256) * H / 2 and (O + 256) * H / 2 below 2^31.  Enqueued on `stream` without
  * synchronizing; no workspace.  Errors: a NULL tensor or data pointer -> FQ_ERR_PARAM_NULLPTR;
  * any shape, dtype, stride, size or alignment mismatch -> FQ_ERR_PARAM_INVALID (no HIP call
  * is made before these checks); not a gfx950 device, or a launch failure -> FQ_ERR_RUNTIME. */

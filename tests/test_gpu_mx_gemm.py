@@ -45,7 +45,8 @@ def _check(C, a, ae, w, we, H, bf16, label):
 def test_mx_gemm_random_operands(out_dtype):
     rng = np.random.default_rng(21)
     for T, O, H in [(1, 1, 128), (16, 16, 128), (128, 128, 256), (130, 200, 384), (257, 129, 1024),
-                    (64, 300, 4096), (3, 2, 8192), (200, 64, 128)]:
+                    (64, 300, 4096), (3, 2, 8192), (200, 64, 128),
+                    (2048, 1030, 384), (768, 2048, 512)]:  # several 256 x 256 tiles, ragged / 8-XCD tile counts
         say(f"[gpu] mx_gemm T={T} O={O} H={H} {out_dtype}")
         a, ae = _rand(T, H, rng)
         w, we = _rand(O, H, rng)
