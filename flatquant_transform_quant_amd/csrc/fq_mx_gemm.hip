@@ -16,25 +16,22 @@
 // Tiling: a workgroup of 8 waves computes a 256 x 256 tile of C, each wave 128 (t) x 64 (o)
 // as 8 x 4 products per 128-deep half of a stage.  A stage is 256 elements of the contraction:
 // the workgroup's 256 rows of A and 256 rows of W (128 code bytes and 8 scale bytes a row,
-// 68 KB) are copied from memory into one of two LDS buffers while the other one feeds the
-// products, one barrier per stage.  In LDS a row's eight 16-byte chunks are stored XOR-
-// permuted (chunk c at position c ^ (r & 7) ^ (r >> 3 & 1)), so that the 16 rows a fragment
-// read touches at one chunk land in 16 distinct bank groups.  Operand rows past T or O read
-// zeros through buffer resources bounded to the operand.  Workgroups are numbered so that
-// the ones dispatched to one XCD (its own L2) cover a contiguous range of tiles, walked in
-// groups of four row bands so that concurrently running tiles share operand rows.
+// 68 KB) are copied from memory into one of two LDS buffers by LDS-DMA loads while the other
+// buffer feeds the products, one barrier per stage.  In LDS a row's eight 16-byte chunks are
+// stored XOR-permuted (chunk c at position c ^ (r & 7)), which the LDS bank-conflict counter
+// reads as zero for the fragment reads.  Operand rows past T or O read zeros through buffer
+// resources bounded to the operand.  Workgroups are numbered so that the ones dispatched to
+// one XCD (its own L2) cover a contiguous range of tiles, walked in groups of four row bands
+// so that concurrently running tiles share operand rows.
 #include <hip/hip_runtime.h>
 
-#include "fq_codec.h"
-#include "fq_internal.h"
+#include "fq_mfma_common.h"
 
 namespace fq {
 namespace {
 
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
-typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 typedef __attribute__((ext_vector_type(8))) int i32x8_t;
-typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
 constexpr int kThreads = 512;               // 8 waves: 2 (t) x 4 (o)
 constexpr int kBT = 256, kBO = 256;         // C tile of a workgroup
@@ -45,10 +42,9 @@ constexpr int kCodeB = kBT * kRowB;         // 32 KB of codes per operand and st
 constexpr int kScOff = 2 * kCodeB;          // scales: [256 rows of A][256 rows of W] x 8 bytes
 constexpr int kStageB = kScOff + (kBT + kBO) * kScB;  // 69632
 constexpr int kGroup = 4;                   // row bands walked together
-constexpr int32_t kBufWord3 = 0x00020000;
 
 // LDS position of 16-byte chunk c of tile row r is c ^ swz(r)
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz(int r) { return r & 7; }
 
 template <bool F32OUT>
 __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(const uint8_t* __restrict__ a,
@@ -57,7 +53,8 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(const uint8_t* __rest
                                                             const uint8_t* __restrict__ w_e8, void* __restrict__ c,
                                                             int32_t T, int32_t O, int32_t H, int32_t gs, int32_t nT,
                                                             int32_t nO, int32_t vec_out) {
-  __shared__ __align__(16) uint8_t lds[2 * kStageB];
+  __shared__ __align__(16) uint8_t lds0[kStageB];  // stages of even / odd index
+  __shared__ __align__(16) uint8_t lds1[kStageB];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
 
@@ -70,46 +67,42 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(const uint8_t* __rest
   const int t0 = (gfirst + rem % gsz) * kBT, o0 = (rem / gsz) * kBO;
 
   const int row_bytes = H >> 1;
-  const auto ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a), static_cast<int16_t>(0), T * row_bytes, kBufWord3);
-  const auto rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(w), static_cast<int16_t>(0), O * row_bytes, kBufWord3);
+  const auto ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a), static_cast<int16_t>(0), T * row_bytes, kBufferWord3);
+  const auto rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(w), static_cast<int16_t>(0), O * row_bytes, kBufferWord3);
   // waves 0-3 copy the scales of A's rows, waves 4-7 those of W's rows
   const bool sc_a = wv < 4;
-  const auto rs = sc_a ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a_e8), static_cast<int16_t>(0), T * gs, kBufWord3)
-                       : __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(w_e8), static_cast<int16_t>(0), O * gs, kBufWord3);
+  const auto rs = sc_a ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a_e8), static_cast<int16_t>(0), T * gs, kBufferWord3)
+                       : __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(w_e8), static_cast<int16_t>(0), O * gs, kBufferWord3);
 
-  // copy mapping: load j takes tile row 64 j + tid/8, LDS position tid%8 (so 8 threads move
-  // one row's 128 bytes); swz(64 j + r) == swz(r)
-  const int crow = tid >> 3, cpos = tid & 7, cchunk = cpos ^ swz(crow);
-  int aoff[4], woff[4];
+  // Copy into a stage with LDS-DMA loads (buffer_load ... lds): lane l of a wave writes the 16
+  // (or 4) bytes it loads to LDS at the wave's base + 16 l (4 l).  Codes: load j of wave wv
+  // fills tile rows 64 j + 8 wv .. +7, lane l row 64 j + tid/8 at position l%8, so it loads
+  // chunk (l%8) ^ swz(row) of that row (swz(64 j + r) == swz(r)).  Scales: the stage's 512
+  // rows x 8 bytes (A's rows, then W's) in 16 runs of 32 rows; wave wv fills runs 2 wv and
+  // 2 wv + 1, lane l row 32 q + l/2, dword l%2.
+  const int crow = tid >> 3, cchunk = (tid & 7) ^ swz(crow);
+  int aoff[4], woff[4], soff[2];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     aoff[j] = (t0 + 64 * j + crow) * row_bytes + 16 * cchunk;
     woff[j] = (o0 + 64 * j + crow) * row_bytes + 16 * cchunk;
   }
-  const int soff = ((sc_a ? t0 : o0) + (tid & 255)) * gs;
-
-  struct Pref {
-    u32x4_t a[4], w[4];
-    uint32_t s0, s1;
-  };
-  auto gload = [&](Pref& p, int kt) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) soff[q] = ((sc_a ? t0 : o0) + ((32 * (2 * wv + q) + (lane >> 1)) & 255)) * gs + 4 * (lane & 1);
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  auto dma = [&](uint8_t* st, int kt) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      p.a[j] = __builtin_amdgcn_raw_buffer_load_b128(ra, aoff[j] + kRowB * kt, 0, 0);
-      p.w[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, woff[j] + kRowB * kt, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr)(st + (64 * j + 8 * wv) * kRowB), 16, aoff[j] + kRowB * kt, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr)(st + kCodeB + (64 * j + 8 * wv) * kRowB), 16,
+                                               woff[j] + kRowB * kt, 0, 0, 0);
     }
-    p.s0 = __builtin_amdgcn_raw_buffer_load_b32(rs, soff + kScB * kt, 0, 0);
-    p.s1 = __builtin_amdgcn_raw_buffer_load_b32(rs, soff + kScB * kt + 4, 0, 0);
-  };
-  auto lstore = [&](const Pref& p, int s) {
-    uint8_t* st = lds + s * kStageB;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      *reinterpret_cast<u32x4_t*>(st + (64 * j + crow) * kRowB + 16 * cpos) = p.a[j];
-      *reinterpret_cast<u32x4_t*>(st + kCodeB + (64 * j + crow) * kRowB + 16 * cpos) = p.w[j];
-    }
-    *reinterpret_cast<u32x2_t*>(st + kScOff + kScB * tid) = u32x2_t{p.s0, p.s1};
+    for (int q = 0; q < 2; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(st + kScOff + 256 * (2 * wv + q)), 4, soff[q] + kScB * kt, 0, 0, 0);
   };
+  // every load of this wave has landed in LDS; the barrier after it publishes the stage
+  auto dma_wait = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
   // products: this wave's rows of A are 128 wm + 16 i + lane%16, of W 64 wn + 16 j + lane%16
   const int wm = wv >> 2, wn = wv & 3;
@@ -120,21 +113,48 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(const uint8_t* __rest
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto half_step = [&](const uint8_t* st, int h) {
-    const int pos = 16 * ((4 * h + kb) ^ sw);
-    u32x4_t wf[4];
-    int wsc[4];
+  // One stage's products: NH halves of 128, each 8 A fragments x 4 W fragments.  The reads
+  // run one fragment ahead of the products: A fragment i + 1 (or, after the last one, the
+  // next half's W fragments and first A fragment) is read while the products of fragment i run.
+  // Per-lane LDS offsets of this wave's fragments in a stage (half h: code chunk 4 h + kb, so
+  // the XOR-permuted position of half 1 is that of half 0 ^ 4); fragment i / j adds a
+  // constant (2048 i for codes, 128 i for scales).  Kept opaque so that the compiler holds
+  // these few offsets instead of one address per stage, half and fragment.
+  int oa[2], ow[2], osa, osw;
+  oa[0] = (128 * wm + r16) * kRowB + 16 * (kb ^ sw);
+  oa[1] = oa[0] ^ 64;
+  ow[0] = kCodeB + (64 * wn + r16) * kRowB + 16 * (kb ^ sw);
+  ow[1] = ow[0] ^ 64;
+  osa = kScOff + kScB * (128 * wm + r16) + kb;
+  osw = kScOff + kScB * (kBT + 64 * wn + r16) + kb;
+  asm volatile("" : "+v"(oa[0]), "+v"(oa[1]), "+v"(ow[0]), "+v"(ow[1]), "+v"(osa), "+v"(osw));
+  auto read_a = [&](const uint8_t* st, int h, int i, u32x4_t& f, int& sc) __attribute__((always_inline)) {
+    f = *reinterpret_cast<const u32x4_t*>(st + oa[h] + 16 * kRowB * i);
+    sc = st[osa + 16 * kScB * i + 4 * h];
+  };
+  auto read_w = [&](const uint8_t* st, int h, u32x4_t (&f)[4], int (&sc)[4]) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int r = 64 * wn + 16 * j + r16;
-      wf[j] = *reinterpret_cast<const u32x4_t*>(st + kCodeB + r * kRowB + pos);
-      wsc[j] = st[kScOff + kScB * (kBT + r) + 4 * h + kb];
+      f[j] = *reinterpret_cast<const u32x4_t*>(st + ow[h] + 16 * kRowB * j);
+      sc[j] = st[osw + 16 * kScB * j + 4 * h];
     }
+  };
+  // One stage's products: one or two halves of 128, each 8 A fragments x 4 W fragments.  The
+  // reads run one fragment ahead of the products: A fragment i + 1 (after the last one, the
+  // next half's W fragments and first A fragment) is read while the products of i run.
+  auto half = [&](const uint8_t* st, int h, u32x4_t (&wf)[4], int (&wsc)[4], u32x4_t& af, int& asc,
+                  u32x4_t (&wfn)[4], int (&wscn)[4], bool next) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int r = 128 * wm + 16 * i + r16;
-      const u32x4_t af = *reinterpret_cast<const u32x4_t*>(st + r * kRowB + pos);
-      const int asc = st[kScOff + kScB * r + 4 * h + kb];
+      u32x4_t afn;
+      int ascn = 0;
+      if (i < 7) {
+        read_a(st, h, i + 1, afn, ascn);
+      } else if (next) {
+        read_w(st, h + 1, wfn, wscn);
+        read_a(st, h + 1, 0, afn, ascn);
+      }
+      __builtin_amdgcn_sched_barrier(0);
       const i32x8_t bv = {static_cast<int>(af[0]), static_cast<int>(af[1]), static_cast<int>(af[2]),
                           static_cast<int>(af[3]), 0, 0, 0, 0};
 #pragma unroll
@@ -144,21 +164,37 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(const uint8_t* __rest
         // format 4 = fp4 (E2M1) for both operands; scale byte 0 of each lane's scale operand
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[i][j], 4, 4, 0, wsc[j], 0, asc);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      if (i < 7 || next) {
+        af = afn;
+        asc = ascn;
+      }
     }
+  };
+  auto stage_products = [&](const uint8_t* st, bool full) __attribute__((always_inline)) {
+    u32x4_t w0[4], w1[4], af;
+    int s0[4], s1[4], asc;
+    read_w(st, 0, w0, s0);
+    read_a(st, 0, 0, af, asc);
+    half(st, 0, w0, s0, af, asc, w1, s1, full);
+    if (full) half(st, 1, w1, s1, af, asc, w0, s0, false);
   };
 
   const int nkt = (H + kKT - 1) / kKT;  // H is a multiple of 128: the last stage may hold one half
-  Pref p;
-  gload(p, 0);
-  lstore(p, 0);
+  // stage kt lives in lds0 for even kt, lds1 for odd kt; the loads of stage kt + 1 run while
+  // stage kt feeds the products
+  dma(lds0, 0);
+  dma_wait();
   __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    const bool more = kt + 1 < nkt;
-    if (more) gload(p, kt + 1);
-    const uint8_t* st = lds + (kt & 1) * kStageB;
-    half_step(st, 0);
-    if ((kt + 1) * kKT <= H) half_step(st, 1);
-    if (more) lstore(p, (kt + 1) & 1);
+  for (int kt = 0; kt < nkt; kt += 2) {
+    if (kt + 1 < nkt) dma(lds1, kt + 1);
+    stage_products(lds0, (kt + 1) * kKT <= H);
+    dma_wait();
+    __syncthreads();
+    if (kt + 1 >= nkt) break;
+    if (kt + 2 < nkt) dma(lds0, kt + 2);
+    stage_products(lds1, (kt + 2) * kKT <= H);
+    dma_wait();
     __syncthreads();
   }
 
