@@ -18,12 +18,15 @@ LIB_PATH = os.path.join(_HERE, "libfqoracle.so")
 
 F16, BF16 = 1, 2
 PER_TOKEN, PER_GROUP = 0, 1
+# per-token code formats (one byte a code except int4)
+QFMT = {"int32": 0, "int4": 0, "int8": 1, "e4m3": 2, "e5m2": 3}
+PER_TOKEN_MODES = tuple(QFMT)
 _DT = {"f16": F16, "fp16": F16, "float16": F16, "bf16": BF16, "bfloat16": BF16}
 
 
 class Params(ctypes.Structure):
     _fields_ = [("dtype", ctypes.c_int32), ("mode", ctypes.c_int32), ("M", ctypes.c_int64),
-                ("N", ctypes.c_int64), ("two_sided", ctypes.c_int32), ("pad_", ctypes.c_int32),
+                ("N", ctypes.c_int64), ("two_sided", ctypes.c_int32), ("qfmt", ctypes.c_int32),
                 ("clip_ratio", ctypes.c_double), ("dst_type_max", ctypes.c_double)]
 
 
@@ -63,6 +66,14 @@ def lib():
         L.fqo_run.restype = ctypes.c_int
         L.fqo_int4_code.argtypes = [ctypes.c_float]
         L.fqo_int4_code.restype = ctypes.c_int
+        L.fqo_int8_code.argtypes = [ctypes.c_float]
+        L.fqo_int8_code.restype = ctypes.c_int
+        L.fqo_fp8_code.argtypes = [ctypes.c_double, ctypes.c_int]
+        L.fqo_fp8_code.restype = ctypes.c_int
+        L.fqo_fp8_value.argtypes = [ctypes.c_int, ctypes.c_int]
+        L.fqo_fp8_value.restype = ctypes.c_double
+        L.fqo_qmax.argtypes = [ctypes.c_int]
+        L.fqo_qmax.restype = ctypes.c_double
         L.fqo_e2m1_code.argtypes = [ctypes.c_double]
         L.fqo_e2m1_code.restype = ctypes.c_int
         L.fqo_e2m1_value.argtypes = [ctypes.c_int]
@@ -88,6 +99,29 @@ def lib():
 
 def int4_code(q: float) -> int:
     return lib().fqo_int4_code(q)
+
+
+def int8_code(q: float) -> int:
+    return lib().fqo_int8_code(q)
+
+
+def fp8_code(q: float, fmt: str) -> int:
+    """FP8 code (sign bit 7) of q, fmt "e4m3" or "e5m2"."""
+    return lib().fqo_fp8_code(q, QFMT[fmt])
+
+
+def fp8_value(code: int, fmt: str) -> float:
+    return lib().fqo_fp8_value(code, QFMT[fmt])
+
+
+def qmax(mode: str) -> float:
+    """max_val of a per-token mode: 7 (int4), 127, 448, 57344."""
+    return lib().fqo_qmax(QFMT[mode])
+
+
+def code_bytes(M: int, N: int, mode: str) -> int:
+    """Bytes of codes per slice: M*N/2 for the 4-bit modes, M*N for the 8-bit ones."""
+    return M * N if mode in ("int8", "e4m3", "e5m2") else M * N // 2
 
 
 def e2m1_code(v: float) -> int:
@@ -130,8 +164,9 @@ def run(x: np.ndarray, p1: np.ndarray, p2: np.ndarray | None, dtype: str, mode: 
         want_y: bool = False, want_t: bool = False, nthreads: int = 1) -> dict:
     """Oracle outputs for x [S, M, N] (uint16 dtype bits) and P1 [M, M], P2 [N, N] or None.
 
-    mode: "int32" / "int4" (per-token int4) or "fp4" (per-group-32 E2M1).  Returns a dict
-    of numpy arrays; "packed" is [S, M*N/2] bytes (low nibble first).  With ranges=True the
+    mode: "int32" / "int4" (per-token int4), "int8" / "e4m3" / "e5m2" (per-token 8-bit
+    codes) or "fp4" (per-group-32 E2M1).  Returns a dict of numpy arrays; "packed" is
+    [S, M*N/2] bytes (low nibble first) for the 4-bit modes, [S, M*N] for the 8-bit ones.  With ranges=True the
     per-element reachable-level data used by the comparator is included.
     """
     x = np.ascontiguousarray(x, dtype=np.uint16)
@@ -141,10 +176,10 @@ def run(x: np.ndarray, p1: np.ndarray, p2: np.ndarray | None, dtype: str, mode: 
     if p2 is not None:
         p2 = np.ascontiguousarray(p2, dtype=np.uint16)
         assert p2.shape == (N, N)
-    per_token = mode in ("int32", "int4")
+    per_token = mode in PER_TOKEN_MODES
     MN, G, GS = out_shapes(M, N, mode)
     prm = Params(_DT[dtype], PER_TOKEN if per_token else PER_GROUP, M, N, 1 if p2 is not None else 0,
-                 0, float(clip_ratio), float(dst_type_max))
+                 QFMT.get(mode, 0), float(clip_ratio), float(dst_type_max))
     res: dict = {}
 
     def alloc(name, shape, dt):
@@ -153,7 +188,7 @@ def run(x: np.ndarray, p1: np.ndarray, p2: np.ndarray | None, dtype: str, mode: 
         return a.ctypes.data
 
     o = Out()
-    o.packed = alloc("packed", (S, MN // 2), np.uint8)
+    o.packed = alloc("packed", (S, code_bytes(M, N, mode)), np.uint8)
     if per_token:
         o.scale = alloc("scale", (S,), np.float32)
     else:
@@ -192,11 +227,11 @@ def run_codes_only(x, p1, p2, dtype, mode, clip_ratio=1.0, dst_type_max=0.0, nth
     """Codes and scales only (what the operator outputs), for timing the oracle."""
     x = np.ascontiguousarray(x, dtype=np.uint16)
     S, M, N = x.shape
-    per_token = mode in ("int32", "int4")
+    per_token = mode in PER_TOKEN_MODES
     MN, G, GS = out_shapes(M, N, mode)
     prm = Params(_DT[dtype], PER_TOKEN if per_token else PER_GROUP, M, N, 1 if p2 is not None else 0,
-                 0, float(clip_ratio), float(dst_type_max))
-    packed = np.zeros((S, MN // 2), np.uint8)
+                 QFMT.get(mode, 0), float(clip_ratio), float(dst_type_max))
+    packed = np.zeros((S, code_bytes(M, N, mode)), np.uint8)
     sc = np.zeros((S,), np.float32) if per_token else np.zeros((S, GS), np.uint8)
     o = Out()
     o.packed = packed.ctypes.data

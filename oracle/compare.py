@@ -5,8 +5,8 @@ The rule (per element of x[K, M, N]):
     one code is reachable -- the value lies within 1e-6 relative of a rounding tie, or
     within the fp32-accumulation error bound of a rounding boundary (of the code itself
     or of the dtype-rounded intermediate).  There the code may differ by one step (one
-    int4 value, or one E2M1 magnitude of the same sign, or the sign of an E2M1 zero when
-    the value is within error of 0), and it must lie in the reachable range;
+    integer value, or one E2M1 / FP8 magnitude of the same sign, or the sign of an E2M1 /
+    FP8 zero when the value is within error of 0), and it must lie in the reachable range;
   * such differences may make up at most ceil(1e-4 * elements) of a result;
   * per-token fp32 scales agree within 1e-5 relative -- or, for a slice whose largest
     element is itself moved by a reachable rounding tie of the intermediate, lie inside the
@@ -40,6 +40,15 @@ def _int4_level(c: np.ndarray) -> np.ndarray:
     return np.where(c >= 8, c - 16, c)
 
 
+def _int8_level(c: np.ndarray) -> np.ndarray:
+    return np.asarray(c, dtype=np.uint8).view(np.int8).astype(np.int16)
+
+
+def _fp8_level(c: np.ndarray) -> np.ndarray:
+    c = c.astype(np.int16)
+    return np.where(c & 0x80, -(c & 0x7F), c & 0x7F)
+
+
 def _e2m1_level(c: np.ndarray) -> np.ndarray:
     c = c.astype(np.int16)
     return np.where(c & 8, -(c & 7), c & 7)
@@ -48,23 +57,32 @@ def _e2m1_level(c: np.ndarray) -> np.ndarray:
 def compare(orc: dict, gpu_packed: np.ndarray, gpu_scale: np.ndarray, max_report: int = 8) -> dict:
     """Compare library outputs for the slices the oracle ran.
 
-    gpu_packed: [S, M*N/2] uint8 (the library's codes, any of the packed layouts, which
-    are byte-identical); gpu_scale: float32 [S] (per token) or uint8 [S, GS] (e8m0).
+    gpu_packed: [S, M*N/2] uint8 (the library's 4-bit codes, any of the packed layouts,
+    which are byte-identical) or [S, M*N] (8-bit codes); gpu_scale: float32 [S] (per
+    token) or uint8 [S, GS] (e8m0).
     """
     mode, M, N, S = orc["mode"], orc["M"], orc["N"], orc["S"]
     MN = M * N
-    per_token = mode in ("int32", "int4")
-    g = unpack_nibbles(np.asarray(gpu_packed).reshape(S, -1), MN)
-    o = unpack_nibbles(orc["packed"], MN)
+    per_token = mode in ("int32", "int4", "int8", "e4m3", "e5m2")
+    byte_codes = mode in ("int8", "e4m3", "e5m2")
+    if byte_codes:
+        g = np.asarray(gpu_packed, dtype=np.uint8).reshape(S, MN)
+        o = np.asarray(orc["packed"], dtype=np.uint8).reshape(S, MN)
+    else:
+        g = unpack_nibbles(np.asarray(gpu_packed).reshape(S, -1), MN)
+        o = unpack_nibbles(orc["packed"], MN)
     rep = {"elements": S * MN, "mismatch": 0, "mismatch_in_stated_window": 0, "flagged": 0,
            "alt_groups": 0, "max_scale_rel": 0.0, "errors": []}
     errs = rep["errors"]
 
     if per_token:
-        gl, ol = _int4_level(g), _int4_level(o)
+        level = {"int8": _int8_level, "e4m3": _fp8_level, "e5m2": _fp8_level}.get(mode, _int4_level)
+        gl, ol = level(g), level(o)
         lo, hi = orc["lo"].astype(np.int16), orc["hi"].astype(np.int16)
-        zs_ok = np.zeros_like(gl, dtype=bool)
-        sign_diff = np.zeros_like(gl, dtype=bool)
+        zs_ok = orc["zsign"].astype(bool)
+        # sign of an FP8 zero (integer zeros have none)
+        sign_diff = (gl == 0) & (ol == 0) & ((g & 0x80) != (o & 0x80)) if mode in ("e4m3", "e5m2") \
+            else np.zeros_like(gl, dtype=bool)
         gs = np.asarray(gpu_scale, dtype=np.float32).reshape(S)
         os_ = orc["scale"]
         with np.errstate(divide="ignore", invalid="ignore"):

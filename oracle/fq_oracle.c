@@ -13,7 +13,11 @@
  *   [DSQ]    the dequant_swiglu_quant Triton-Ascend page, section 6.1
  *            (round-half-to-even, 2.5 -> 2 and 3.5 -> 4);
  *   [APT]    the APT-LLM page, section 2.1 (symmetric b-bit integer
- *            quantization clamped to [-2^(b-1), 2^(b-1)-1]).
+ *            quantization clamped to [-2^(b-1), 2^(b-1)-1]);
+ *   [DSQ 3.4] the same dequant_swiglu_quant page, section 3.4 (dynamic
+ *            per-row quantization: scale = max|out| / max_val, codes
+ *            clamp(round(out / scale), -max_val, max_val), max_val 127 for
+ *            INT8, 448 for FP8 E4M3FN, 57344 for FP8 E5M2).
  *
  * What is computed for one slice x_k [M, N] (readings of silent or garbled
  * points are marked "reading"):
@@ -24,6 +28,14 @@
  *                                    [0,0] P2 the first step is skipped.
  *   per token:  scale = fl32(max|y| / fl32(7/clipRatio)),
  *               code  = clamp(RNE(fl32(y / scale)), -8, 7)    [FQV2] 第3步 pertoken
+ *   per token, 8-bit codes ([DSQ 3.4] with this operator's per-token clip; reading:
+ *     the divisor is fl32(max_val / clipRatio), which is the page's max_val at
+ *     clipRatio 1):  scale = fl32(max|y| / fl32(max_val/clipRatio)),  q = fl32(y/scale);
+ *     INT8: code = clamp(RNE(q), -127, 127);  FP8: code = the representable value
+ *     nearest clamp(q, -max_val, max_val), a tie to the even code; the code keeps the
+ *     sign of q (reading: the OCP FP8 encodings, E4M3FN = 1.4.3 bias 7 without
+ *     infinities, E5M2 = 1.5.2 bias 15; their largest finite values are the page's
+ *     max_val 448 and 57344)
  *   per group of 32 over the flattened index f = m*N + n ([FQV2] 第3步 pergroup):
  *     V1 (dstTypeMax == 0): e8m0 = clamp(floor(log2 amax) - 2 + 127, 0, 254),
  *        reading: emax = 2, the exponent of E2M1's largest value 6 = 1.5 * 2^2;
@@ -54,6 +66,11 @@
 #define FQO_BF16 2
 #define FQO_PER_TOKEN 0
 #define FQO_PER_GROUP 1
+/* per-token code formats */
+#define FQO_Q_INT4 0
+#define FQO_Q_INT8 1
+#define FQO_Q_E4M3 2
+#define FQO_Q_E5M2 3
 
 #define TIE_REL 1e-6 /* the stated tie window, relative */
 
@@ -118,6 +135,85 @@ int fqo_int4_code(float q) {
   if (r < -8.0f) r = -8.0f;
   if (r > 7.0f) r = 7.0f;
   return (int)r;
+}
+
+/* ---- 8-bit per-token encoders ([DSQ 3.4]) ---------------------------------- */
+
+/* max_val of a per-token code format: int4 7 ([FQV2] 第3步 pertoken), the others [DSQ 3.4] */
+double fqo_qmax(int fmt) {
+  switch (fmt) {
+    case FQO_Q_INT8: return 127.0;
+    case FQO_Q_E4M3: return 448.0;
+    case FQO_Q_E5M2: return 57344.0;
+    default: return 7.0;
+  }
+}
+
+int fqo_int8_code(float q) {
+  float r = nearbyintf(q); /* round half to even ([DSQ] 6.1) */
+  if (r < -127.0f) r = -127.0f;
+  if (r > 127.0f) r = 127.0f;
+  return (int)r;
+}
+
+/* Value of a non-negative FP8 code (bit 7 clear): sign-less 1.4.3 (bias 7) or 1.5.2
+ * (bias 15); exponent field 0 is subnormal (no implicit one, exponent 1 - bias). */
+double fqo_fp8_value(int code, int fmt) {
+  const int mb = fmt == FQO_Q_E4M3 ? 3 : 2, bias = fmt == FQO_Q_E4M3 ? 7 : 15;
+  const int e = (code & 0x7F) >> mb, m = code & ((1 << mb) - 1);
+  const double v = e == 0 ? ldexp((double)m, 1 - bias - mb) : ldexp(1.0 + ldexp((double)m, -mb), e - bias);
+  return (code & 0x80) ? -v : v;
+}
+
+/* the largest finite code: E4M3FN 0x7E (0x7F is NaN), E5M2 0x7B (0x7C is infinity) */
+static int fp8_max_code(int fmt) { return fmt == FQO_Q_E4M3 ? 0x7E : 0x7B; }
+
+/* Index (= code) of the FP8 magnitude nearest a >= 0, a <= max; the values grow with the
+ * code, so the two candidates are the largest code whose value is <= a and the next one.
+ * tie: 0 = even code, 1 = lower, 2 = upper. */
+static int fp8_index(double a, int fmt, int tie) {
+  int lo = 0, hi = fp8_max_code(fmt);
+  if (a >= fqo_fp8_value(hi, fmt)) return hi;
+  while (hi - lo > 1) { /* value(lo) <= a < value(hi) */
+    const int mid = (lo + hi) / 2;
+    if (fqo_fp8_value(mid, fmt) <= a) lo = mid; else hi = mid;
+  }
+  const double dl = a - fqo_fp8_value(lo, fmt), dh = fqo_fp8_value(hi, fmt) - a;
+  if (dl < dh) return lo;
+  if (dh < dl) return hi;
+  return tie == 1 ? lo : tie == 2 ? hi : ((lo & 1) ? hi : lo);
+}
+
+int fqo_fp8_code(double q, int fmt) {
+  const double mx = fqo_fp8_value(fp8_max_code(fmt), fmt);
+  double a = fabs(q);
+  if (a > mx) a = mx; /* clamp to +-max_val ([DSQ 3.4]) */
+  return (signbit(q) ? 0x80 : 0) | fp8_index(a, fmt, 0);
+}
+
+static int fp8_level(int code) { return (code & 0x80) ? -(code & 0x7F) : (code & 0x7F); }
+static double fp8_clamp(double v, int fmt) {
+  const double mx = fqo_fp8_value(fp8_max_code(fmt), fmt);
+  return v > mx ? mx : (v < -mx ? -mx : v);
+}
+static int fp8_level_down(double v, int fmt) {
+  v = fp8_clamp(v, fmt);
+  return v >= 0 ? fp8_index(v, fmt, 1) : -fp8_index(-v, fmt, 2);
+}
+static int fp8_level_up(double v, int fmt) {
+  v = fp8_clamp(v, fmt);
+  return v >= 0 ? fp8_index(v, fmt, 2) : -fp8_index(-v, fmt, 1);
+}
+/* |q| within TIE_REL of a midpoint between two adjacent FP8 magnitudes */
+static int fp8_near_tie(double q, int fmt) {
+  const double a = fabs(q);
+  const int c = fp8_index(a, fmt, 1);
+  for (int k = c - 1; k <= c; ++k) {
+    if (k < 0 || k + 1 > fp8_max_code(fmt)) continue;
+    const double mid = 0.5 * (fqo_fp8_value(k, fmt) + fqo_fp8_value(k + 1, fmt));
+    if (fabs(a - mid) <= TIE_REL * mid) return 1;
+  }
+  return 0;
 }
 
 /* ---- E2M1 encoder ----------------------------------------------------------
@@ -211,7 +307,7 @@ typedef struct {
   int32_t mode;         /* FQO_PER_TOKEN | FQO_PER_GROUP */
   int64_t M, N;
   int32_t two_sided;    /* 0: the right transform is skipped ([0,0] P2) */
-  int32_t pad_;
+  int32_t qfmt;         /* per token: FQO_Q_INT4 | _INT8 | _E4M3 | _E5M2 */
   double clip_ratio;
   double dst_type_max;
 } fqo_params;
@@ -347,7 +443,9 @@ static int slice(const fqo_params* p, const uint16_t* xs, const double* P1, cons
   if (o->y)
     for (int64_t f = 0; f < MN; ++f) o->y[s * MN + f] = (float)Y[f];
 
-  uint8_t* packed = o->packed ? o->packed + s * (MN / 2) : NULL;
+  const int fmt = p->mode == FQO_PER_TOKEN ? p->qfmt : FQO_Q_INT4;
+  const int wide = fmt != FQO_Q_INT4; /* one byte per code */
+  uint8_t* packed = o->packed ? o->packed + s * (wide ? MN : MN / 2) : NULL;
 
   if (p->mode == FQO_PER_TOKEN) {
     /* [FQV2] 第3步 pertoken: one fp32 scale per slice k */
@@ -356,7 +454,7 @@ static int slice(const fqo_params* p, const uint16_t* xs, const double* P1, cons
       float a = fabsf((float)Y[f]);
       if (a > amax) amax = a;
     }
-    const float d = (float)(7.0 / p->clip_ratio);
+    const float d = (float)(fqo_qmax(fmt) / p->clip_ratio);
     const float scale = amax / d;
     if (o->scale) o->scale[s] = scale;
     double Alo = 0.0, Ahi = 0.0, slo = 0.0, shi = 0.0;
@@ -375,20 +473,41 @@ static int slice(const fqo_params* p, const uint16_t* xs, const double* P1, cons
       if (o->scale_lo) o->scale_lo[s] = (float)slo;
       if (o->scale_hi) o->scale_hi[s] = (float)shi;
     }
+    /* level range of the format: int4 [-8, 7] ([APT] 2.1), INT8 +-127 ([DSQ 3.4]), FP8
+     * +- the largest finite code; a level is the code's signed value (int) or signed
+     * magnitude index (FP8), which grows with the value it encodes */
+    const int lmin = fmt == FQO_Q_INT4 ? -8 : fmt == FQO_Q_INT8 ? -127 : -fp8_max_code(fmt);
+    const int lmax = fmt == FQO_Q_INT4 ? 7 : fmt == FQO_Q_INT8 ? 127 : fp8_max_code(fmt);
     for (int64_t f = 0; f < MN; ++f) {
-      int code = 0;
+      int code = 0, level = 0;
       float q = 0.0f;
-      if (scale > 0.0f) {
-        q = (float)Y[f] / scale;
-        code = fqo_int4_code(q);
+      if (scale > 0.0f) q = (float)Y[f] / scale;
+      if (fmt == FQO_Q_INT4) {
+        if (scale > 0.0f) code = fqo_int4_code(q);
+        level = code;
+        if (packed) put_nibble(packed, f, code);
+      } else if (fmt == FQO_Q_INT8) {
+        if (scale > 0.0f) code = fqo_int8_code(q);
+        level = code;
+        if (packed) packed[f] = (uint8_t)(code & 0xFF);
+      } else {
+        if (scale > 0.0f) code = fqo_fp8_code(q, fmt);
+        level = fp8_level(code);
+        if (packed) packed[f] = (uint8_t)code;
       }
-      if (packed) put_nibble(packed, f, code);
-      if (o->lvl) o->lvl[s * MN + f] = (int8_t)code;
-      if (o->zsign) o->zsign[s * MN + f] = 0; /* int4 zero is unsigned */
+      if (o->lvl) o->lvl[s * MN + f] = (int8_t)level;
+      /* an integer zero is unsigned; an FP8 zero carries the sign of y, either of which
+       * is reachable when y's reachable interval contains 0 */
+      if (o->zsign)
+        o->zsign[s * MN + f] = (fmt == FQO_Q_E4M3 || fmt == FQO_Q_E5M2) && want && Ylo[f] <= 0.0 && Yhi[f] >= 0.0;
       int tie = 0;
       if (scale > 0.0f) {
-        double t = floor((double)q) + 0.5;
-        if (t >= -7.5 && t <= 6.5 && fabs((double)q - t) <= TIE_REL * fabs(t)) tie = 1;
+        if (fmt == FQO_Q_E4M3 || fmt == FQO_Q_E5M2) {
+          tie = fp8_near_tie(q, fmt);
+        } else {
+          double t = floor((double)q) + 0.5;
+          if (t >= lmin + 0.5 && t <= lmax - 0.5 && fabs((double)q - t) <= TIE_REL * fabs(t)) tie = 1;
+        }
       }
       if (o->ns_tie) o->ns_tie[s * MN + f] = (uint8_t)tie;
       if (want && (o->lo || o->hi)) {
@@ -396,8 +515,8 @@ static int slice(const fqo_params* p, const uint16_t* xs, const double* P1, cons
         if (amax == 0.0f) {
           lo = hi = 0;
         } else if (!(slo > 0.0)) {
-          lo = -8;
-          hi = 7;
+          lo = lmin;
+          hi = lmax;
         } else {
           double c[4] = {Ylo[f] / slo, Ylo[f] / shi, Yhi[f] / slo, Yhi[f] / shi};
           double qlo = c[0], qhi = c[0];
@@ -409,15 +528,20 @@ static int slice(const fqo_params* p, const uint16_t* xs, const double* P1, cons
           double w = 2.4e-7 + TIE_REL;
           qlo -= fabs(qlo) * w;
           qhi += fabs(qhi) * w;
-          double dl = ceil(qlo - 0.5), dh = floor(qhi + 0.5);
-          if (dl < -8) dl = -8;
-          if (dl > 7) dl = 7;
-          if (dh < -8) dh = -8;
-          if (dh > 7) dh = 7;
-          lo = (int)dl;
-          hi = (int)dh;
-          if (lo > code) lo = code;
-          if (hi < code) hi = code;
+          if (fmt == FQO_Q_E4M3 || fmt == FQO_Q_E5M2) {
+            lo = fp8_level_down(qlo, fmt);
+            hi = fp8_level_up(qhi, fmt);
+          } else {
+            double dl = ceil(qlo - 0.5), dh = floor(qhi + 0.5);
+            if (dl < lmin) dl = lmin;
+            if (dl > lmax) dl = lmax;
+            if (dh < lmin) dh = lmin;
+            if (dh > lmax) dh = lmax;
+            lo = (int)dl;
+            hi = (int)dh;
+          }
+          if (lo > level) lo = level;
+          if (hi < level) hi = level;
         }
         if (o->lo) o->lo[s * MN + f] = (int8_t)lo;
         if (o->hi) o->hi[s * MN + f] = (int8_t)hi;
@@ -540,6 +664,7 @@ int fqo_run(const fqo_params* p, const uint16_t* x, const uint16_t* p1, const ui
   if (p->dtype != FQO_F16 && p->dtype != FQO_BF16) return -1;
   if (p->M < 1 || p->N < 1 || p->M > 4096 || p->N > 4096) return -1;
   if (p->mode == FQO_PER_TOKEN && !(p->clip_ratio > 0.0 && p->clip_ratio <= 1.0)) return -1;
+  if (p->mode == FQO_PER_TOKEN && (p->qfmt < FQO_Q_INT4 || p->qfmt > FQO_Q_E5M2)) return -1;
   if (p->two_sided && !p2) return -1;
   if ((p->M * p->N) % 2 != 0 && o->packed) return -1;
   const int want = (o->lo || o->hi || o->zsign || o->alt_lvl || o->alt_lo || o->alt_hi ||

@@ -543,3 +543,112 @@ def test_mx_gemm_weight_scale_step_doubles_exactly():
     c1, _ = oracle.mx_gemm(a, ae, w, we, 512)
     c2, _ = oracle.mx_gemm(a, ae, w, we + 1, 512)
     assert np.array_equal(c2, 2 * c1)
+
+
+# ---------------------------------------------------------------- per-token 8-bit modes
+# (the dequant_swiglu_quant page, section 3.4: dynamic per-row quantization with max_val
+# 127 / 448 / 57344; section 6.1: round half to even)
+
+FP8_TORCH = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
+
+
+def test_int8_rne_examples_and_symmetric_clamp_from_page():
+    assert [oracle.int8_code(v) for v in (2.5, 3.5, -2.5, -3.5, 0.5, 1.5)] == [2, 4, -2, -4, 0, 2]
+    assert oracle.int8_code(127.4) == 127 and oracle.int8_code(-127.4) == -127
+    # clamp(round(.), -max_val, max_val): -127.6 rounds to -128, which the clamp takes to -127
+    assert oracle.int8_code(-127.6) == -127 and oracle.int8_code(-1e9) == -127 and oracle.int8_code(1e9) == 127
+
+
+def test_qmax_values_from_page():
+    assert [oracle.qmax(m) for m in ("int4", "int8", "e4m3", "e5m2")] == [7.0, 127.0, 448.0, 57344.0]
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_value_table(fmt):
+    vals = np.array([oracle.fp8_value(c, fmt) for c in range(128)])
+    top = 0x7E if fmt == "e4m3" else 0x7B
+    # the page's max_val is the largest finite value; the smallest subnormal and 1.0
+    assert vals[top] == oracle.qmax(fmt)
+    assert vals[1] == (2.0 ** -9 if fmt == "e4m3" else 2.0 ** -16)
+    assert oracle.fp8_code(1.0, fmt) == (0x38 if fmt == "e4m3" else 0x3C)
+    assert np.all(np.diff(vals[: top + 1]) > 0)  # values grow with the code
+    # the same table as torch's float8 dtype decodes it
+    codes = torch.arange(top + 1, dtype=torch.uint8).view(FP8_TORCH[fmt]).to(torch.float64).numpy()
+    assert np.array_equal(codes, vals[: top + 1])
+    assert oracle.fp8_value(0x80 | 0x38, fmt) == -vals[0x38]
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_encoder_against_torch_conversion(fmt):
+    """Every FP8 value, every midpoint between neighbours and one fp32 step either side of
+    it, and random values over the whole range, both signs: the oracle's nearest-value
+    search equals torch's float32 -> float8 conversion (round half to even) inside
+    +-max_val; beyond it the oracle saturates."""
+    top = 0x7E if fmt == "e4m3" else 0x7B
+    v = np.array([oracle.fp8_value(c, fmt) for c in range(top + 1)])
+    mids = 0.5 * (v[:-1] + v[1:])
+    pts = [v, mids, np.nextafter(mids.astype(np.float32), np.float32(np.inf)),
+           np.nextafter(mids.astype(np.float32), np.float32(0))]
+    rng = np.random.default_rng(5)
+    pts.append(np.exp(rng.uniform(np.log(v[1] / 4), np.log(v[top]), 20000)))
+    a = np.concatenate([np.asarray(p, dtype=np.float32) for p in pts])
+    a = np.concatenate([a, -a, np.float32([0.0, -0.0])])
+    a = a[np.abs(a) <= v[top]]
+    want = torch.from_numpy(a).to(FP8_TORCH[fmt]).view(torch.uint8).numpy()
+    got = np.array([oracle.fp8_code(float(q), fmt) for q in a], dtype=np.uint8)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(float(a[i]), int(got[i]), int(want[i])) for i in bad[:5]]
+    assert oracle.fp8_code(1e30, fmt) == top and oracle.fp8_code(-1e30, fmt) == 0x80 | top
+
+
+@pytest.mark.parametrize("mode", ["int8", "e4m3", "e5m2"])
+@pytest.mark.parametrize("clip", [1.0, 0.9])
+def test_pertoken_8bit_invariants(mode, clip):
+    """scale = amax / fl32(max_val / clip) within one fp32 rounding; the largest element
+    maps to the largest level; every unclipped code dequantizes to within half a step of y
+    (int8: scale/2; FP8: half the spacing of the neighbouring values at that magnitude);
+    levels grow with y; the reachable interval holds the oracle's own level."""
+    w = synth.WORKLOADS["c2"]
+    x, p1, p2 = synth.make_inputs(w, 0, 6)
+    r = oracle.run(x, p1, p2, w.dtype, mode, clip, want_y=True)
+    S = x.shape[0]
+    y = r["y"].reshape(S, -1).astype(np.float64)
+    amax = np.abs(y).max(axis=1)
+    s = r["scale"].astype(np.float64)
+    d = float(np.float32(oracle.qmax(mode) / clip))
+    assert np.all(np.abs(s * d - amax) <= amax * 2.0 ** -23)
+    lvl = r["lvl"].astype(np.int64)
+    codes = r["packed"].reshape(S, -1)
+    top = 127 if mode == "int8" else (0x7E if mode == "e4m3" else 0x7B)
+    assert np.abs(lvl).max() <= top
+    if clip == 1.0:
+        i = np.argmax(np.abs(y), axis=1)
+        assert np.all(np.abs(lvl[np.arange(S), i]) == top)
+    if mode == "int8":
+        val = lvl.astype(np.float64)
+        half = np.full_like(val, 0.5)
+    else:
+        table = np.array([oracle.fp8_value(c, mode) for c in range(top + 1)])
+        mag = table[np.abs(lvl)]
+        val = np.where(lvl < 0, -mag, mag)
+        up = table[np.minimum(np.abs(lvl) + 1, top)] - mag
+        dn = mag - table[np.maximum(np.abs(lvl) - 1, 0)]
+        half = 0.5 * np.maximum(up, dn)
+        assert np.array_equal(codes & 0x7F, np.abs(lvl))
+    q = y / s[:, None]
+    inside = np.abs(q) <= top * (1 - 1e-6) if mode == "int8" else np.abs(q) <= table[top] * (1 - 1e-6)
+    err = np.abs(q - val)
+    assert np.all(err[inside] <= half[inside] * (1 + 1e-5) + 1e-6)
+    order = np.argsort(y, axis=1)
+    assert np.all(np.diff(np.take_along_axis(lvl, order, axis=1), axis=1) >= 0)
+    assert np.all(r["lo"] <= r["lvl"]) and np.all(r["lvl"] <= r["hi"])
+
+
+def test_pertoken_8bit_zero_slice_and_sign_of_fp8_zero():
+    x = np.zeros((1, 4, 8), np.uint16)
+    for mode in ("int8", "e4m3", "e5m2"):
+        r = oracle.run(x, bf16(np.eye(4)), bf16(np.eye(8)), "bf16", mode)
+        assert (r["scale"] == 0).all() and (r["packed"] == 0).all()
+        assert r["packed"].shape == (1, 32)
+    # a tiny negative value keeps its sign in FP8 (code 0x80), not in INT8
+    assert oracle.fp8_code(-1e-30, "e4m3") == 0x80 and oracle.int8_code(-1e-30) == 0
