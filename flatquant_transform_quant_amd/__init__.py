@@ -12,7 +12,10 @@ Output storage in torch:
     (2 codes per byte, low nibble first), quantScale ``torch.float32`` [K];
   * ``fp4``   mode: out is ``torch.uint8`` (or ``torch.float4_e2m1fn_x2``) [K, M*N/2]
     holding the logical FLOAT4_E2M1 [K, M*N], quantScale ``torch.uint8`` (or
-    ``torch.float8_e8m0fnu``) [K, ceilDiv(M*N, 64), 2].
+    ``torch.float8_e8m0fnu``) [K, ceilDiv(M*N, 64), 2];
+  * ``int8`` / ``e4m3`` / ``e5m2`` modes (per-token 8-bit codes): out is ``torch.int8`` /
+    ``torch.float8_e4m3fn`` / ``torch.float8_e5m2`` (or ``torch.uint8``) [K, M, N],
+    quantScale ``torch.float32`` [K].
 """
 from __future__ import annotations
 
@@ -28,6 +31,9 @@ FQ_ERR_PARAM_INVALID = 161002
 FQ_ERR_RUNTIME = 161003
 
 DT_FLOAT16, DT_BFLOAT16, DT_FLOAT32, DT_INT32, DT_INT4, DT_FLOAT4_E2M1, DT_FLOAT8_E8M0 = range(1, 8)
+DT_INT8, DT_FLOAT8_E4M3FN, DT_FLOAT8_E5M2 = range(8, 11)
+BYTE_MODES = {"int8": DT_INT8, "e4m3": DT_FLOAT8_E4M3FN, "e5m2": DT_FLOAT8_E5M2}
+PER_TOKEN_MODES = ("int32", "int4") + tuple(BYTE_MODES)
 KERNEL_AUTO, KERNEL_GENERIC, KERNEL_MFMA_SMALL, KERNEL_MFMA_WIDE = 0, 1, 2, 3
 
 
@@ -198,11 +204,13 @@ def describe_out(out, mode: str, K: int, M: int, N: int) -> FqTensor:
         return make_tensor(out.data_ptr(), DT_INT4, (K, M, N), (2 * st[0], 2 * st[1], 1 if st[2] == 1 else 2 * st[2]))
     if mode == "fp4":
         return make_tensor(out.data_ptr(), DT_FLOAT4_E2M1, (K, M * N), (2 * st[0], 1 if st[1] == 1 else 2 * st[1]))
+    if mode in BYTE_MODES:
+        return make_tensor(out.data_ptr(), BYTE_MODES[mode], out.shape, out.stride())
     raise ValueError(f"unknown mode {mode!r}")
 
 
 def describe_scale(scale, mode: str) -> FqTensor:
-    dt = DT_FLOAT32 if mode in ("int32", "int4") else DT_FLOAT8_E8M0
+    dt = DT_FLOAT32 if mode in PER_TOKEN_MODES else DT_FLOAT8_E8M0
     return make_tensor(scale.data_ptr(), dt, scale.shape, scale.stride())
 
 
@@ -218,6 +226,10 @@ def empty_outputs(K: int, M: int, N: int, mode: str, device="cuda"):
     if mode == "fp4":
         return (torch.empty((K, M * N // 2), dtype=torch.uint8, device=device),
                 torch.empty((K, -(-(M * N) // 64), 2), dtype=torch.uint8, device=device))
+    if mode in BYTE_MODES:
+        dt = {"int8": torch.int8, "e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}[mode]
+        return (torch.empty((K, M, N), dtype=dt, device=device),
+                torch.empty((K,), dtype=torch.float32, device=device))
     raise ValueError(f"unknown mode {mode!r}")
 
 

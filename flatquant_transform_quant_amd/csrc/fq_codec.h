@@ -57,6 +57,52 @@ __device__ __forceinline__ uint32_t int4_nibble(float q) {
   return static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xFu;
 }
 
+// Per-token 8-bit codes (the dequant_swiglu_quant page, section 3.4: dynamic per-row
+// quantization, clamp(round(q), -max_val, max_val) with max_val 127 for INT8, 448 for FP8
+// E4M3FN and 57344 for FP8 E5M2; round half to even, section 6.1).
+//
+// INT8: the two's-complement byte of clamp(RNE(q), -127, 127).
+__device__ __forceinline__ uint32_t int8_code(float q) {
+  float r = __builtin_rintf(q);
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xFFu;
+}
+
+// FP8 (OCP encodings: E4M3FN = sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+// infinities; E5M2 = sign, 5 exponent bits with bias 15, 2 mantissa bits): the value nearest
+// clamp(|q|, 0, max_val), a tie to the even code, with q's sign bit.  Below the smallest
+// normal (2^-6, 2^-14) the code is the count of subnormal steps (2^-9, 2^-16), rounded half
+// to even; above it the fp32 mantissa is rounded half to even to MB bits and the exponent
+// rebiased (a carry out of the mantissa moves into the exponent, which is the next code).
+template <int MB, int BIAS>
+__device__ __forceinline__ uint32_t fp8_code(float q, float maxv) {
+  constexpr int kEminN = 1 - BIAS;  // exponent of the smallest normal
+  const float a = fminf(__builtin_fabsf(q), maxv);
+  const uint32_t sign = (__float_as_uint(q) >> 24) & 0x80u;
+  uint32_t mag;
+  if (a < __builtin_amdgcn_ldexpf(1.0f, kEminN)) {
+    mag = static_cast<uint32_t>(__builtin_rintf(__builtin_amdgcn_ldexpf(a, MB - kEminN)));
+  } else {
+    uint32_t b = __float_as_uint(a);
+    b += ((1u << (22 - MB)) - 1u) + ((b >> (23 - MB)) & 1u);
+    mag = ((((b >> 23) & 0xFFu) - 127u + BIAS) << MB) | ((b >> (23 - MB)) & ((1u << MB) - 1u));
+  }
+  return sign | mag;
+}
+__device__ __forceinline__ uint32_t e4m3_code(float q) { return fp8_code<3, 7>(q, 448.0f); }
+__device__ __forceinline__ uint32_t e5m2_code(float q) { return fp8_code<2, 15>(q, 57344.0f); }
+
+// The byte of a per-token 8-bit mode for q = y / scale (y * (1 / scale) in the MFMA kernels).
+template <int MODE>
+__device__ __forceinline__ uint32_t code8(float q) {
+  if constexpr (MODE == kPerTokenInt8)
+    return int8_code(q);
+  else if constexpr (MODE == kPerTokenE4M3)
+    return e4m3_code(q);
+  else
+    return e5m2_code(q);
+}
+
 // E2M1 code (sign << 3 | magnitude index) by counting the decision points passed.
 // At a decision point the even index wins: the points in front of an even index
 // (0.75, 1.75, 3.5) are passed at equality, the others (0.25, 1.25, 2.5, 5) only when

@@ -1,9 +1,9 @@
-// Generic libfq kernel: any shape 1 <= M, N <= 256, both modes, both dtypes.
+// Generic libfq kernel: any shape 1 <= M, N <= 256, every mode, both dtypes.
 //
 // One workgroup per slice (grid-stride over K).  Step 1 ([FQV2] 第1步) forms
-// T = round_dtype(x_k . P2) element by element with sequential fp32 FMAs and keeps T in
-// LDS (at most 256 x 256 x 2 B = 128 KB).  Step 2 ([FQV2] 第2步) forms each y with a
-// sequential fp32 FMA chain over m and feeds it straight to the encoder, so y is never
+// T = round_dtype(fl32(x_k . P2)) element by element with an fp64 FMA chain rounded once
+// to fp32, and keeps T in LDS (at most 256 x 256 x 2 B = 128 KB).  Step 2 ([FQV2] 第2步)
+// forms each y the same way over m and feeds it straight to the encoder, so y is never
 // stored.  Per token, y is formed twice -- once for max|y|, once to encode -- by the
 // same code, so both passes see identical values.  Per group, one thread forms the 32
 // values of a group, its scale and its 16 code bytes.
@@ -21,13 +21,17 @@ namespace {
 
 constexpr int kGenericThreads = 256;
 
+// The sums are accumulated in fp64 (the 16-bit products are exact there) and rounded once
+// to fp32: y and T are then the correctly rounded fp32 values of the products, whatever
+// the length of the contraction.
 template <int DT>
 __device__ __forceinline__ float y_at(const uint16_t* __restrict__ p1, const uint16_t* Ts, int M, int N,
                                       int i, int n) {
-  float acc = 0.0f;
+  double acc = 0.0;
   const uint16_t* prow = p1 + static_cast<int64_t>(i) * M;
-  for (int m = 0; m < M; ++m) acc = __builtin_fmaf(load16<DT>(prow[m]), load16<DT>(Ts[m * N + n]), acc);
-  return acc;
+  for (int m = 0; m < M; ++m)
+    acc = __builtin_fma(static_cast<double>(load16<DT>(prow[m])), static_cast<double>(load16<DT>(Ts[m * N + n])), acc);
+  return static_cast<float>(acc);
 }
 
 __device__ __forceinline__ float block_max(float v, float* red) {
@@ -53,16 +57,22 @@ __global__ __launch_bounds__(kGenericThreads) void generic_kernel(Problem pb, Bu
     for (int e = tid; e < MN; e += kGenericThreads) {
       if (pb.two_sided) {
         const int m = e / N, n = e % N;
-        float acc = 0.0f;
+        double acc = 0.0;
         for (int j = 0; j < N; ++j)
-          acc = __builtin_fmaf(load16<DT>(xk[m * N + j]), load16<DT>(b.p2[j * N + n]), acc);
-        Ts[e] = round16<DT>(acc);
+          acc = __builtin_fma(static_cast<double>(load16<DT>(xk[m * N + j])),
+                              static_cast<double>(load16<DT>(b.p2[j * N + n])), acc);
+        // T is the fp32 value rounded to the dtype: two roundings.  The register barrier
+        // keeps the compiler from merging them into one fp64 -> dtype rounding, which
+        // differs where the fp32 value is a tie of the dtype.
+        float t32 = static_cast<float>(acc);
+        asm volatile("" : "+v"(t32));
+        Ts[e] = round16<DT>(t32);
       } else {
         Ts[e] = xk[e];
       }
     }
     __syncthreads();
-    uint8_t* codes = b.codes + k * (MN / 2);
+    uint8_t* codes = b.codes + k * (byte_codes(pb.mode) ? MN : MN / 2);
     if (pb.mode == kPerGroupFp4) {
       const int G = static_cast<int>(ceil_div(MN, 32));
       const int GS = static_cast<int>(e8m0_bytes_per_slice(MN));
@@ -90,14 +100,26 @@ __global__ __launch_bounds__(kGenericThreads) void generic_kernel(Problem pb, Bu
       }
       if (tid == 0 && GS > G) e8[G] = 0;
     } else {
-      // [FQV2] 第3步 pertoken: scale = max|y| / (7 / clipRatio), codes = y / scale.
+      // [FQV2] 第3步 pertoken: scale = max|y| / (max_val / clipRatio), codes = y / scale
+      // (max_val 7 for int4; 127 / 448 / 57344 for the 8-bit codes of the dequant_swiglu_quant
+      // page, section 3.4).
       float amax = 0.0f;
       for (int e = tid; e < MN; e += kGenericThreads)
         amax = fmaxf(amax, __builtin_fabsf(y_at<DT>(b.p1, Ts, M, N, e / N, e % N)));
       amax = block_max(amax, red);
       const float scale = amax / pb.d;
       if (tid == 0) static_cast<float*>(b.scale)[k] = scale;
-      for (int p = tid; p < MN / 2; p += kGenericThreads) {
+      if (byte_codes(pb.mode)) {
+        for (int e = tid; e < MN; e += kGenericThreads) {
+          uint32_t c = 0;
+          if (scale > 0.0f) {
+            const float q = y_at<DT>(b.p1, Ts, M, N, e / N, e % N) / scale;
+            c = pb.mode == kPerTokenInt8 ? int8_code(q) : (pb.mode == kPerTokenE4M3 ? e4m3_code(q) : e5m2_code(q));
+          }
+          codes[e] = static_cast<uint8_t>(c);
+        }
+      }
+      for (int p = tid; p < (byte_codes(pb.mode) ? 0 : MN / 2); p += kGenericThreads) {
         const int e = 2 * p;
         uint32_t c0 = 0, c1 = 0;
         if (scale > 0.0f) {

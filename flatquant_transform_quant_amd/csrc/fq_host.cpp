@@ -182,6 +182,13 @@ fq_status fq_get_workspace_size(const fq_tensor* x, const fq_tensor* kroneckerP1
       if (N % 2 != 0 || !shape_is(*out, 2, K, MN)) return FQ_ERR_PARAM_INVALID;
       mode = fq::kPerGroupFp4;
       break;
+    case FQ_DT_INT8:
+    case FQ_DT_FLOAT8_E4M3FN:
+    case FQ_DT_FLOAT8_E5M2:
+      if (!shape_is(*out, 3, K, M, N)) return FQ_ERR_PARAM_INVALID;
+      mode = out->dtype == FQ_DT_INT8 ? fq::kPerTokenInt8
+                                      : (out->dtype == FQ_DT_FLOAT8_E4M3FN ? fq::kPerTokenE4M3 : fq::kPerTokenE5M2);
+      break;
     default:
       return FQ_ERR_PARAM_INVALID;
   }
@@ -209,7 +216,13 @@ fq_status fq_get_workspace_size(const fq_tensor* x, const fq_tensor* kroneckerP1
   e->pb.M = M;
   e->pb.N = N;
   e->pb.two_sided = p2_empty ? 0 : 1;
-  e->pb.d = static_cast<float>(7.0 / clipRatio);
+  // per-token divisor max_val / clipRatio: int4 7 ([FQV2] 第3步 pertoken); INT8 127, FP8
+  // E4M3FN 448, FP8 E5M2 57344 (the dequant_swiglu_quant page, section 3.4)
+  const double qmax = mode == fq::kPerTokenInt8 ? 127.0
+                      : mode == fq::kPerTokenE4M3 ? 448.0
+                      : mode == fq::kPerTokenE5M2 ? 57344.0
+                                                  : 7.0;
+  e->pb.d = static_cast<float>(qmax / clipRatio);
   e->pb.dmax = static_cast<float>(dstTypeMax);
   {
     int ex = 0;
@@ -237,7 +250,7 @@ fq_status fq_get_workspace_size(const fq_tensor* x, const fq_tensor* kroneckerP1
   e->off_x = take(e->stage_x, uint64_t(K * MN) * 2);
   e->off_p1 = take(e->stage_p1, uint64_t(M * M) * 2);
   e->off_p2 = take(e->stage_p2, uint64_t(N * N) * 2);
-  e->off_out = take(e->stage_out, uint64_t(K * MN / 2));
+  e->off_out = take(e->stage_out, uint64_t(fq::byte_codes(mode) ? K * MN : K * MN / 2));
   e->off_scale = take(e->stage_scale, mode == fq::kPerGroupFp4
                                           ? uint64_t(K * fq::e8m0_bytes_per_slice(MN))
                                           : uint64_t(K) * 4);
@@ -302,7 +315,8 @@ fq_status fq_run(void* workspace, uint64_t workspaceSize, fq_executor* executor,
     if (err != hipSuccess) { st = fail_runtime("transform-quantize kernel launch", err); break; }
     if (e->stage_out) {
       // The codes as bytes: INT32 [K, M, N/8] words, INT4 [K, M, N/2] and
-      // FLOAT4_E2M1 [K, M*N/2] byte rows (strides in 4-bit elements halve).
+      // FLOAT4_E2M1 [K, M*N/2] byte rows (strides in 4-bit elements halve), the 8-bit
+      // codes [K, M, N] bytes.
       int64_t shape[3], strides[3];
       int eb;
       if (e->out.dtype == FQ_DT_INT32) {
@@ -312,6 +326,9 @@ fq_status fq_run(void* workspace, uint64_t workspaceSize, fq_executor* executor,
         eb = 1;
         shape[0] = pb.K; shape[1] = pb.M; shape[2] = pb.N / 2;
         strides[0] = e->out.strides[0] / 2; strides[1] = e->out.strides[1] / 2; strides[2] = 1;
+      } else if (fq::byte_codes(pb.mode)) {
+        eb = 1;
+        for (int d = 0; d < 3; ++d) { shape[d] = e->out.shape[d]; strides[d] = e->out.strides[d]; }
       } else {
         eb = 1;
         shape[0] = 1; shape[1] = pb.K; shape[2] = MN / 2;

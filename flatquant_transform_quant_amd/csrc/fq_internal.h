@@ -8,7 +8,16 @@
 namespace fq {
 
 enum Dtype16 : int32_t { kF16 = 1, kBF16 = 2 };
-enum Mode : int32_t { kPerTokenInt32 = 0, kPerTokenInt4 = 1, kPerGroupFp4 = 2 };
+enum Mode : int32_t {
+  kPerTokenInt32 = 0,
+  kPerTokenInt4 = 1,
+  kPerGroupFp4 = 2,
+  kPerTokenInt8 = 3,  // one byte a code: INT8, FP8 E4M3FN, FP8 E5M2
+  kPerTokenE4M3 = 4,
+  kPerTokenE5M2 = 5
+};
+// codes of one byte each (the 8-bit per-token modes) rather than two codes a byte
+__host__ __device__ inline bool byte_codes(int32_t mode) { return mode >= kPerTokenInt8; }
 enum Kernel : int32_t { kAuto = 0, kGeneric = 1, kMfmaSmall = 2, kMfmaWide = 3 };
 
 // One planned problem, as the kernels see it (all tensors contiguous).
@@ -17,14 +26,15 @@ struct Problem {
   int32_t mode;       // Mode
   int64_t K, M, N;
   int32_t two_sided;  // 0: P2 is [0, 0], the right multiply is skipped
-  float d;            // fl32(7 / clipRatio), the per-token divisor
+  float d;            // fl32(max_val / clipRatio), the per-token divisor (max_val 7, 127, 448, 57344)
   float dmax;         // fl32(dstTypeMax); 0 selects V1
   float dmax_inv;     // 1/dmax when dmax is a power of two (then exact), else 0
 };
 
 // Device buffers of one launch, in the packed contiguous layouts:
 //   x [K, M, N], p1 [M, M], p2 [N, N] (16-bit bits);
-//   codes: K * M*N/2 bytes, low nibble = lower flattened index;
+//   codes: K * M*N/2 bytes, low nibble = lower flattened index (K * M*N bytes for the
+//          8-bit modes);
 //   scale: float [K] (per token) or uint8 [K, 2*ceil(M*N/64)] (e8m0).
 struct Buffers {
   const uint16_t* x;

@@ -51,8 +51,9 @@ constexpr int small_workgroups_per_cu() {
   return (M * N >= 4096 && prefetch_depth<M, N, PG>() == 2) ? 1 : 0;
 }
 
-// CLAMP (per token): the int4 clamp is compiled in.  SV (per group): the e8m0 rule.
-template <int DT, int M, int N, bool PG, bool CLAMP, int SV>
+// CLAMP (per token): the int4 clamp is compiled in.  SV (per group): the e8m0 rule.  Q (per
+// token): 0 for int4 codes, else the 8-bit mode (kPerTokenInt8 / E4M3 / E5M2), one byte a code.
+template <int DT, int M, int N, bool PG, bool CLAMP, int SV, int Q>
 // (The second launch bound is HIP's minimum of waves per SIMD: 2 keeps the 4-wave variants
 // to 256 registers, the budget they were written for, also where one wave per SIMD is
 // launched; an 8-wave workgroup already puts two on each SIMD.)
@@ -69,8 +70,9 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()), (small_waves<M, N, 
 
   __shared__ u32x4_t frag2[KS1 * NT * 64];  // B fragments of P2 (or of I)
   __shared__ u32x4_t frag1[MT * KS2 * 64];  // A fragments of P1 (k relabelled)
-  // per-wave staging of one slice's output: codes (M*N/2 bytes), then e8m0 bytes
-  constexpr int CODE_BYTES = MN / 2;
+  // per-wave staging of one slice's output: codes (M*N/2 bytes, M*N for 8-bit codes), then
+  // e8m0 bytes
+  constexpr int CODE_BYTES = Q ? MN : MN / 2;
   constexpr int E8_BYTES = PG ? MN / 32 : 0;
   constexpr int STAGE_BYTES = (CODE_BYTES + E8_BYTES + 15) / 16 * 16;
   __shared__ u32x4_t stage[kSmallWaves][STAGE_BYTES / 16];
@@ -166,7 +168,7 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()), (small_waves<M, N, 
     // e8m0 byte).  Made opaque per slice so the per-row addresses are formed here, with
     // the row as an immediate offset, instead of being hoisted out of the slice loop and
     // held in registers.
-    int code_off = 4 * g * (N / 2) + (R / 2) * c;
+    int code_off = Q ? 4 * g * N + R * c : 4 * g * (N / 2) + (R / 2) * c;
     int e8_off = CODE_BYTES + 4 * g * (N / 32) + (R * c) / 32;
     asm volatile("" : "+v"(code_off), "+v"(e8_off));
     // ---- GEMM1: T = x . P2 (fp32), rounded to the dtype and written straight into the
@@ -227,6 +229,26 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()), (small_waves<M, N, 
       const float scale = amax / pb.d;
       const float inv = scale > 0.0f ? 1.0f / scale : 0.0f;
       if (lane == 0) static_cast<float*>(b.scale)[s] = scale;
+      if constexpr (Q != 0) {
+        // 8-bit codes (the dequant_swiglu_quant page, section 3.4): the lane's R codes of a
+        // row are R consecutive bytes
+#pragma unroll
+        for (int it = 0; it < MT; ++it)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r0 = 16 * it + i;  // row - 4g
+            uint32_t w[(R + 3) / 4] = {};
+#pragma unroll
+            for (int nt = 0; nt < R; ++nt) w[nt / 4] |= code8<Q>(y[it][nt][i] * inv) << (8 * (nt % 4));
+            uint8_t* dst = st + code_off + r0 * N;
+            if constexpr (R == 2) {
+              *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(w[0]);
+            } else {
+#pragma unroll
+              for (int q = 0; q < R / 4; ++q) reinterpret_cast<uint32_t*>(dst)[q] = w[q];
+            }
+          }
+      } else {
 #pragma unroll
       for (int it = 0; it < MT; ++it)
 #pragma unroll
@@ -247,6 +269,7 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()), (small_waves<M, N, 
             *reinterpret_cast<uint32_t*>(dst) = unbias(gather4(by[0], by[1], by[2], by[3]));
           }
         }
+      }
     } else {
       // [FQV2] 第3步 pergroup / 第4步: one e8m0 scale per 32 consecutive elements of a row.
       // GEMM2 and the encoding run one 16-row tile at a time.
@@ -306,7 +329,7 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()), (small_waves<M, N, 
     if (s + q * waves < pb.K) process(q, s + q * waves);
 }
 
-template <int DT, int M, int N, bool PG, bool CLAMP, int SV>
+template <int DT, int M, int N, bool PG, bool CLAMP, int SV, int Q = 0>
 hipError_t launch_one(const Problem& pb, const Buffers& b, hipStream_t s) {
   constexpr int kWaves = small_waves<M, N, PG>(), kThreads = 64 * kWaves;
   static int grid_cap = 0;  // workgroups that fit the device at once (per instantiation)
@@ -315,7 +338,7 @@ hipError_t launch_one(const Problem& pb, const Buffers& b, hipStream_t s) {
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e == hipSuccess)
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_small_kernel<DT, M, N, PG, CLAMP, SV>,
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_small_kernel<DT, M, N, PG, CLAMP, SV, Q>,
                                                        kThreads, 0);
     if (e != hipSuccess) return e;
     constexpr int wg = small_workgroups_per_cu<M, N, PG>();
@@ -323,7 +346,7 @@ hipError_t launch_one(const Problem& pb, const Buffers& b, hipStream_t s) {
   }
   const int64_t need = (pb.K + kWaves - 1) / kWaves;
   const int grid = static_cast<int>(need < grid_cap ? need : grid_cap);
-  mfma_small_kernel<DT, M, N, PG, CLAMP, SV><<<grid, kThreads, 0, s>>>(pb, b);
+  mfma_small_kernel<DT, M, N, PG, CLAMP, SV, Q><<<grid, kThreads, 0, s>>>(pb, b);
   return hipGetLastError();
 }
 
@@ -336,6 +359,12 @@ hipError_t dispatch_clamp(const Problem& pb, const Buffers& b, hipStream_t s) {
       default: return launch_one<DT, M, N, true, false, kE8V2Div>(pb, b, s);
     }
   } else {
+    switch (pb.mode) {
+      case kPerTokenInt8: return launch_one<DT, M, N, false, false, kE8V1, kPerTokenInt8>(pb, b, s);
+      case kPerTokenE4M3: return launch_one<DT, M, N, false, false, kE8V1, kPerTokenE4M3>(pb, b, s);
+      case kPerTokenE5M2: return launch_one<DT, M, N, false, false, kE8V1, kPerTokenE5M2>(pb, b, s);
+      default: break;
+    }
     // The int4 clamp can only bite when (7/clipRatio) * (1 + 4 ulp) reaches 7.5.
     if (pb.d >= 7.4999f) return launch_one<DT, M, N, false, true, kE8V1>(pb, b, s);
     return launch_one<DT, M, N, false, false, kE8V1>(pb, b, s);

@@ -568,7 +568,8 @@ hipError_t dispatch_w1(const Problem& pb, const Buffers& b, hipStream_t s) {
 }  // namespace
 
 bool mfma_wide_supports(const Problem& pb) {
-  return pb.M == kW && pb.N == kW && (pb.two_sided || pb.mode == kPerGroupFp4);
+  // (the 8-bit per-token codes are not written by this kernel's epilogue)
+  return pb.M == kW && pb.N == kW && (pb.two_sided || pb.mode == kPerGroupFp4) && !byte_codes(pb.mode);
 }
 
 hipError_t launch_mfma_wide(const Problem& pb, const Buffers& b, hipStream_t s) {

@@ -65,8 +65,15 @@ typedef int32_t fq_status;
  *   out          INT32        [K, M, N/8]  (N % 8 == 0; 8 int4 codes per word)
  *                INT4         [K, M, N]    (N even; 2 codes per byte)
  *                FLOAT4_E2M1  [K, M*N]     (N even; 2 codes per byte)
- *   quantScale   FLOAT32      [K]                          with INT32 / INT4 out
+ *                INT8 | FLOAT8_E4M3FN | FLOAT8_E5M2  [K, M, N]   (1 code per byte)
+ *   quantScale   FLOAT32      [K]                          with INT32 / INT4 / 8-bit out
  *                FLOAT8_E8M0  [K, ceilDiv(M*N, 64), 2]     with FLOAT4_E2M1 out
+ * The 8-bit outputs extend the per-token mode with the dynamic per-row quantization of
+ * the dequant_swiglu_quant page (section 3.4): scale_k = fl32(max|y_k| /
+ * fl32(max_val / clipRatio)) with max_val 127 (INT8), 448 (FLOAT8_E4M3FN), 57344
+ * (FLOAT8_E5M2); INT8 codes clamp(RNE(y / scale), -127, 127) as two's-complement bytes;
+ * FP8 codes the OCP E4M3FN / E5M2 value nearest clamp(y / scale, -max_val, max_val), a
+ * tie to the even code, keeping y's sign.  They need a [N, N] P2 (as INT32 / INT4 do).
  * `data` is a device pointer; it is never dereferenced by fq_get_workspace_size.
  * `strides` are in elements of the tensor's dtype (for INT4 and FLOAT4_E2M1, in 4-bit
  * elements).  Inputs may have any non-negative strides.  Outputs may be strided too,
@@ -81,7 +88,10 @@ typedef enum {
   FQ_DT_INT32 = 4,
   FQ_DT_INT4 = 5,
   FQ_DT_FLOAT4_E2M1 = 6,
-  FQ_DT_FLOAT8_E8M0 = 7
+  FQ_DT_FLOAT8_E8M0 = 7,
+  FQ_DT_INT8 = 8,           /* per-token 8-bit codes (see fq_get_workspace_size) */
+  FQ_DT_FLOAT8_E4M3FN = 9,
+  FQ_DT_FLOAT8_E5M2 = 10
 } fq_dtype;
 
 typedef struct {

@@ -666,7 +666,8 @@ int fqo_run(const fqo_params* p, const uint16_t* x, const uint16_t* p1, const ui
   if (p->mode == FQO_PER_TOKEN && !(p->clip_ratio > 0.0 && p->clip_ratio <= 1.0)) return -1;
   if (p->mode == FQO_PER_TOKEN && (p->qfmt < FQO_Q_INT4 || p->qfmt > FQO_Q_E5M2)) return -1;
   if (p->two_sided && !p2) return -1;
-  if ((p->M * p->N) % 2 != 0 && o->packed) return -1;
+  /* two 4-bit codes a byte need an even M*N; the 8-bit codes take one byte each */
+  if ((p->M * p->N) % 2 != 0 && o->packed && !(p->mode == FQO_PER_TOKEN && p->qfmt != FQO_Q_INT4)) return -1;
   const int want = (o->lo || o->hi || o->zsign || o->alt_lvl || o->alt_lo || o->alt_hi ||
                     o->g_lo || o->g_hi || o->g_alt || o->scale_lo || o->scale_hi) ? 1 : 0;
   if (nthreads < 1) nthreads = 1;

@@ -51,6 +51,8 @@ def problem(K=4, M=16, N=16, dt=fq.DT_BFLOAT16, mode="int32", p2_empty=False):
         out, sc = tens(fq.DT_INT32, (K, M, N // 8)), tens(fq.DT_FLOAT32, (K,))
     elif mode == "int4":
         out, sc = tens(fq.DT_INT4, (K, M, N)), tens(fq.DT_FLOAT32, (K,))
+    elif mode in fq.BYTE_MODES:
+        out, sc = tens(fq.BYTE_MODES[mode], (K, M, N)), tens(fq.DT_FLOAT32, (K,))
     else:
         out = tens(fq.DT_FLOAT4_E2M1, (K, M * N))
         sc = tens(fq.DT_FLOAT8_E8M0, (K, -(-(M * N) // 64), 2))
@@ -64,7 +66,7 @@ def plan(p, clip=1.0, dmax=0.0):
     return st, ws
 
 
-@pytest.mark.parametrize("mode", ["int32", "int4", "fp4"])
+@pytest.mark.parametrize("mode", ["int32", "int4", "fp4", "int8", "e4m3", "e5m2"])
 def test_valid_plans_have_zero_workspace(mode):
     st, ws = plan(problem(mode=mode))
     assert (st, ws) == (OK, 0)
@@ -407,3 +409,45 @@ def test_mx_gemm_invalid_is_161002(case):
     elif case == "too_big":
         args = mx_args(T=1 << 18, H=1 << 14)
     assert fq.fq_mx_gemm(*args, 0) == INVAL
+
+
+# ---------------------------------------------------------------- 8-bit per-token outputs
+# (dynamic per-row quantization of the dequant_swiglu_quant page, section 3.4)
+
+@pytest.mark.parametrize("mode", ["int8", "e4m3", "e5m2"])
+def test_8bit_outputs_shape_scale_and_p2_rules(mode):
+    dt = fq.BYTE_MODES[mode]
+    assert plan(problem(K=3, M=5, N=7, mode=mode)) == (OK, 0)  # any N: one code a byte
+    p = problem(mode=mode)
+    p["out"] = tens(dt, (4, 16 * 16))  # must be [K, M, N]
+    assert plan(p)[0] == INVAL
+    p = problem(mode=mode)
+    p["out"] = tens(dt, (4, 16, 8))
+    assert plan(p)[0] == INVAL
+    p = problem(mode=mode)
+    p["sc"] = tens(fq.DT_FLOAT8_E8M0, (4, 4, 2))  # per-token scales are FLOAT32 [K]
+    assert plan(p)[0] == INVAL
+    p = problem(mode=mode)
+    p["sc"] = tens(fq.DT_FLOAT32, (5,))
+    assert plan(p)[0] == INVAL
+    assert plan(problem(mode=mode, p2_empty=True))[0] == INVAL  # [0, 0] P2 is per-group only
+    assert plan(problem(mode=mode), clip=1.5)[0] == INVAL
+    assert plan(problem(mode=mode), dmax=5.0)[0] == INVAL  # validated in every mode
+
+
+@pytest.mark.parametrize("mode", ["int8", "e4m3", "e5m2"])
+def test_8bit_strided_output_is_staged_in_the_workspace(mode):
+    p = problem(K=4, M=16, N=16, mode=mode)
+    p["out"] = tens(fq.BYTE_MODES[mode], (4, 16, 16), (16 * 32, 32, 1))  # padded rows
+    st, ws = plan(p)
+    assert st == OK and ws >= 4 * 16 * 16
+
+
+def test_8bit_modes_pick_a_kernel_by_shape():
+    for M, N, want in [(64, 64, 2), (32, 128, 2), (256, 256, 1), (48, 40, 1)]:
+        p = problem(K=8, M=M, N=N, mode="int8")
+        st, ws, ex = fq.fq_get_workspace_size(p["x"], p["p1"], p["p2"], 1.0, 0.0, p["out"], p["sc"])
+        assert st == OK
+        k = fq.lib.fq_executor_kernel(ex)
+        fq.fq_executor_destroy(ex)
+        assert k == want, (M, N, k)

@@ -1,0 +1,74 @@
+"""GPU parity of the per-token 8-bit codes (INT8, FP8 E4M3FN, FP8 E5M2: the dynamic per-row
+quantization of the dequant_swiglu_quant page, section 3.4, on the transformed slice) with
+the oracle, element by element, under the same rule as the 4-bit modes (oracle/compare.py):
+codes equal except one step at a reachable rounding tie (at most ceil(1e-4 * elements)),
+the sign of an FP8 zero free where y is within error of 0, scales within 1e-5 relative.
+Every kernel that accepts the shape is run: the generic one always, the one-wave-per-slice
+MFMA kernel for its shapes (M in 16..128, N in 32..128, M*N <= 4096)."""
+import numpy as np
+import pytest
+
+import flatquant_transform_quant_amd as fq
+import synth
+from gpu_util import check, fetch, run_lib, say, supported_kernels, to_dev
+
+pytestmark = pytest.mark.gpu
+
+MODES = ["int8", "e4m3", "e5m2"]
+SHAPES = [(1, 1), (3, 5), (16, 32), (17, 24), (32, 32), (64, 64), (16, 128), (128, 32), (32, 128),
+          (64, 128), (255, 254), (256, 256)]
+
+
+def _inputs(M, N, dt, K, seed):
+    x = synth.gen_x(M, N, dt, "gauss", 0.02, 30.0, seed=seed, k0=0, k1=K)
+    return x, synth.gen_orthogonal(M, dt, seed, 2), synth.gen_orthogonal(N, dt, seed, 3)
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_8bit_shapes_every_kernel(mode, dt):
+    for i, (M, N) in enumerate(SHAPES):
+        K = 6 if M * N <= 64 * 64 else 3
+        x, p1, p2 = _inputs(M, N, dt, K, seed=M * 1000 + N)
+        clip = 1.0 if i % 2 == 0 else 0.9
+        xd, p1d, p2d = to_dev(x, dt), to_dev(p1, dt), to_dev(p2, dt)
+        ks = supported_kernels(xd, p1d, p2d, mode, clip, 0.0)
+        assert fq.KERNEL_GENERIC in ks and fq.KERNEL_MFMA_WIDE not in ks
+        for k in ks:
+            rep = check(x, p1, p2, dt, mode, clip, 0.0, kernel=k, label=f"8-bit {M}x{N}")
+            assert rep["ok"], rep["errors"]
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_8bit_ragged_k(mode):
+    w = synth.WORKLOADS["c2i8"]
+    for K in (1, 7, 257, 1031):
+        x, p1, p2 = synth.make_inputs(w, 0, K)
+        rep = check(x, p1, p2, w.dtype, mode, 1.0, 0.0, label=f"8-bit ragged K={K}",
+                    slices=sorted({0, K // 2, K - 1}))
+        assert rep["ok"], rep["errors"]
+
+
+def test_8bit_zero_input_gives_zero_scale_and_zero_codes():
+    for mode in MODES:
+        x = np.zeros((4, 64, 64), np.uint16)
+        p = synth.gen_orthogonal(64, "bf16", 0, 2)
+        xd, pd = to_dev(x, "bf16"), to_dev(p, "bf16")
+        for k in supported_kernels(xd, pd, pd, mode, 1.0, 0.0):
+            out, sc = run_lib(xd, pd, pd, mode, 1.0, 0.0, k)
+            packed, scale = fetch(out, sc, mode, 4)
+            assert (scale == 0).all()
+            assert ((packed & 0x7F) == 0).all() if mode != "int8" else (packed == 0).all()
+
+
+@pytest.mark.parametrize("key", ["c2i8", "c2e4m3", "c2e5m2"])
+def test_8bit_full_size_sampled(key):
+    """The full 64 x 64 workload (K = 8192) in the launch the benchmark times, checked on
+    sampled slices that the oracle computes one by one."""
+    w = synth.WORKLOADS[key]
+    say(f"[gpu] generating {key} full size K={w.K}")
+    x, p1, p2 = synth.make_inputs(w)
+    rng = np.random.default_rng(3)
+    slices = sorted({0, 1, w.K // 2, w.K - 1, *rng.integers(0, w.K, 12).tolist()})
+    rep = check(x, p1, p2, w.dtype, w.mode, w.clip_ratio, w.dst_type_max, label=f"{key} full", slices=slices)
+    assert rep["ok"], rep["errors"]
