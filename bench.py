@@ -29,10 +29,12 @@ MFMA_FP4_PEAK_TFS = 10100.0    # MI355X dense fp4 MFMA, TFLOP/s
 
 
 def algorithmic_bytes(w, K=None) -> int:
-    """Bytes one launch must move: read x, P1, P2 once; write codes (0.5 B/elem) and scales."""
+    """Bytes one launch must move: read x, P1, P2 once; write codes (0.5 B/elem, 1 B/elem for
+    the 8-bit modes) and scales."""
     K = w.K if K is None else K
     MN = w.M * w.N
-    b = 2 * K * MN + 2 * w.M * w.M + (2 * w.N * w.N if w.two_sided else 0) + K * MN // 2
+    codes = K * MN if w.mode in ("int8", "e4m3", "e5m2") else K * MN // 2
+    b = 2 * K * MN + 2 * w.M * w.M + (2 * w.N * w.N if w.two_sided else 0) + codes
     if w.mode == "fp4":
         b += K * 2 * (-(-MN // 64))
     else:

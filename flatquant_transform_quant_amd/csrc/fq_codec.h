@@ -70,37 +70,30 @@ __device__ __forceinline__ uint32_t int8_code(float q) {
 
 // FP8 (OCP encodings: E4M3FN = sign, 4 exponent bits with bias 7, 3 mantissa bits, no
 // infinities; E5M2 = sign, 5 exponent bits with bias 15, 2 mantissa bits): the value nearest
-// clamp(|q|, 0, max_val), a tie to the even code, with q's sign bit.  Below the smallest
-// normal (2^-6, 2^-14) the code is the count of subnormal steps (2^-9, 2^-16), rounded half
-// to even; above it the fp32 mantissa is rounded half to even to MB bits and the exponent
-// rebiased (a carry out of the mantissa moves into the exponent, which is the next code).
-template <int MB, int BIAS>
-__device__ __forceinline__ uint32_t fp8_code(float q, float maxv) {
-  constexpr int kEminN = 1 - BIAS;  // exponent of the smallest normal
-  const float a = fminf(__builtin_fabsf(q), maxv);
-  const uint32_t sign = (__float_as_uint(q) >> 24) & 0x80u;
-  uint32_t mag;
-  if (a < __builtin_amdgcn_ldexpf(1.0f, kEminN)) {
-    mag = static_cast<uint32_t>(__builtin_rintf(__builtin_amdgcn_ldexpf(a, MB - kEminN)));
-  } else {
-    uint32_t b = __float_as_uint(a);
-    b += ((1u << (22 - MB)) - 1u) + ((b >> (23 - MB)) & 1u);
-    mag = ((((b >> 23) & 0xFFu) - 127u + BIAS) << MB) | ((b >> (23 - MB)) & ((1u << MB) - 1u));
-  }
-  return sign | mag;
+// clamp(q, -max_val, max_val), a tie to the even code, with q's sign bit.  gfx950's packed
+// conversions to the OCP formats round to nearest even; with the clamp applied first they
+// never overflow, and over every fp32 input in [-max_val, max_val] they equal the rounding
+// of the fp32 mantissa to the format's bits (checked exhaustively against a bitwise encoder).
+// Two codes per call, in bytes 0 and 1.
+__device__ __forceinline__ uint32_t e4m3x2(float a, float b) {
+  const float ca = fminf(fmaxf(a, -448.0f), 448.0f), cb = fminf(fmaxf(b, -448.0f), 448.0f);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false)) & 0xFFFFu;
 }
-__device__ __forceinline__ uint32_t e4m3_code(float q) { return fp8_code<3, 7>(q, 448.0f); }
-__device__ __forceinline__ uint32_t e5m2_code(float q) { return fp8_code<2, 15>(q, 57344.0f); }
+__device__ __forceinline__ uint32_t e5m2x2(float a, float b) {
+  const float ca = fminf(fmaxf(a, -57344.0f), 57344.0f), cb = fminf(fmaxf(b, -57344.0f), 57344.0f);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_bf8_f32(ca, cb, 0, false)) & 0xFFFFu;
+}
 
-// The byte of a per-token 8-bit mode for q = y / scale (y * (1 / scale) in the MFMA kernels).
+// Two bytes of a per-token 8-bit mode (byte 0 = a) for q = y / scale (y * (1 / scale) in the
+// MFMA kernels).
 template <int MODE>
-__device__ __forceinline__ uint32_t code8(float q) {
+__device__ __forceinline__ uint32_t code8x2(float a, float b) {
   if constexpr (MODE == kPerTokenInt8)
-    return int8_code(q);
+    return int8_code(a) | (int8_code(b) << 8);
   else if constexpr (MODE == kPerTokenE4M3)
-    return e4m3_code(q);
+    return e4m3x2(a, b);
   else
-    return e5m2_code(q);
+    return e5m2x2(a, b);
 }
 
 // E2M1 code (sign << 3 | magnitude index) by counting the decision points passed.

@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kGenericThreads) void generic_kernel(Problem pb, Bu
           uint32_t c = 0;
           if (scale > 0.0f) {
             const float q = y_at<DT>(b.p1, Ts, M, N, e / N, e % N) / scale;
-            c = pb.mode == kPerTokenInt8 ? int8_code(q) : (pb.mode == kPerTokenE4M3 ? e4m3_code(q) : e5m2_code(q));
+            c = (pb.mode == kPerTokenInt8 ? int8_code(q) : (pb.mode == kPerTokenE4M3 ? e4m3x2(q, q) : e5m2x2(q, q))) & 0xFFu;
           }
           codes[e] = static_cast<uint8_t>(c);
         }

@@ -239,7 +239,8 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()), (small_waves<M, N, 
             const int r0 = 16 * it + i;  // row - 4g
             uint32_t w[(R + 3) / 4] = {};
 #pragma unroll
-            for (int nt = 0; nt < R; ++nt) w[nt / 4] |= code8<Q>(y[it][nt][i] * inv) << (8 * (nt % 4));
+            for (int nt = 0; nt < R; nt += 2)
+              w[nt / 4] |= code8x2<Q>(y[it][nt][i] * inv, y[it][nt + 1][i] * inv) << (8 * (nt % 4));
             uint8_t* dst = st + code_off + r0 * N;
             if constexpr (R == 2) {
               *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(w[0]);

@@ -72,3 +72,54 @@ def test_8bit_full_size_sampled(key):
     slices = sorted({0, 1, w.K // 2, w.K - 1, *rng.integers(0, w.K, 12).tolist()})
     rep = check(x, p1, p2, w.dtype, w.mode, w.clip_ratio, w.dst_type_max, label=f"{key} full", slices=slices)
     assert rep["ok"], rep["errors"]
+
+
+def _bf16_bits(v):
+    f = np.asarray(v, np.float32).view(np.uint32).astype(np.uint64)
+    return ((f + 0x7FFF + ((f >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def _bf16_next(bits, up):
+    """The neighbouring bf16 value away from / towards zero for positive bits."""
+    return (bits.astype(np.int32) + (1 if up else -1)).astype(np.uint16)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_8bit_every_code_midpoint_and_neighbour_exact(mode):
+    """Identity transforms and a slice whose largest value is max_val make scale = 1 and
+    y / scale = x exactly, so each element's code is the encoding of a chosen value: every
+    FP8 value (every integer for INT8), every midpoint between neighbours (an exact tie,
+    which goes to the even code) and the bf16 values next to each midpoint, both signs.
+    The codes must equal the oracle's bit for bit on every kernel."""
+    import oracle
+
+    qmax = oracle.qmax(mode)
+    if mode == "int8":
+        vals = np.arange(0, 128, dtype=np.float64)
+        mids = np.arange(0, 127, dtype=np.float64) + 0.5
+    else:
+        top = 0x7E if mode == "e4m3" else 0x7B
+        vals = np.array([oracle.fp8_value(c, mode) for c in range(top + 1)])
+        mids = 0.5 * (vals[:-1] + vals[1:])
+    mb = _bf16_bits(mids)
+    assert np.array_equal(oracle.dt_to_float(mb, "bf16"), mids)  # the ties are bf16 values
+    pos = np.concatenate([_bf16_bits(vals), mb, _bf16_next(mb, True), _bf16_next(mb[1:], False)])
+    pos = pos[oracle.dt_to_float(pos, "bf16") <= qmax]
+    allv = np.concatenate([pos, pos | 0x8000, _bf16_bits([qmax])])
+    M = N = 64
+    assert allv.size <= M * N
+    x = np.zeros(M * N, np.uint16)
+    x[: allv.size] = allv
+    x = x.reshape(1, M, N)
+    eye = _bf16_bits(np.eye(M))
+    r = oracle.run(x, eye, eye, "bf16", mode, 1.0, ranges=False)
+    assert r["scale"][0] == 1.0
+    xd, pd = to_dev(x, "bf16"), to_dev(eye, "bf16")
+    ks = supported_kernels(xd, pd, pd, mode, 1.0, 0.0)
+    assert fq.KERNEL_MFMA_SMALL in ks
+    for k in ks:
+        out, sc = run_lib(xd, pd, pd, mode, 1.0, 0.0, k)
+        packed, scale = fetch(out, sc, mode, 1)
+        say(f"[gpu] {mode} exhaustive codes kernel={k}: {int((packed != r['packed']).sum())} differ")
+        assert scale[0] == 1.0
+        assert np.array_equal(packed, r["packed"]), np.nonzero(packed != r["packed"])[1][:8]
