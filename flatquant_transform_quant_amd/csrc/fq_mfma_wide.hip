@@ -32,8 +32,9 @@ constexpr int kChunk = 32;    // rows of x per chunk
 constexpr int kNChunk = kW / kChunk;
 constexpr int kIT = kW / 16;  // 16-row tiles of y
 
-// CLAMP (per token): the int4 clamp is compiled in.  SV (per group): the e8m0 rule.
-template <int DT, bool PG, bool CLAMP, int SV>
+// CLAMP (per token): the int4 clamp is compiled in.  SV (per group): the e8m0 rule.  Q (per
+// token): 0 for int4 codes, else the 8-bit mode (kPerTokenInt8 / E4M3 / E5M2), one byte a code.
+template <int DT, bool PG, bool CLAMP, int SV, int Q>
 __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb, Buffers b) {
   __shared__ u32x4_t frag1[kIT * kNChunk * 64];   // 128 KB: P1 A fragments
   // 2 x 16 KB: x chunks in GEMM1 A-fragment order.  The 16-byte slot q = 4ks + g of chunk
@@ -233,9 +234,11 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb,
   // registers) plus the row as a scalar offset.
   auto epilogue = [&]() {
     agpr_fence<16>(y);
-    const auto rs_codes = __builtin_amdgcn_make_buffer_rsrc(b.codes + s * (kW * kW / 2), static_cast<int16_t>(0),
-                                                            kW * kW / 2, kBufferWord3);
-    int code_off = 4 * g * (kW / 2) + 32 * w + 2 * c;
+    constexpr int kCodeB = Q ? kW * kW : kW * kW / 2;  // code bytes of a slice
+    const auto rs_codes = __builtin_amdgcn_make_buffer_rsrc(b.codes + s * kCodeB, static_cast<int16_t>(0), kCodeB,
+                                                            kBufferWord3);
+    // the lane's 4 codes of a row are columns 64 w + 4 c .. +3
+    int code_off = Q ? 4 * g * kW + 64 * w + 4 * c : 4 * g * (kW / 2) + 32 * w + 2 * c;
     asm volatile("" : "+v"(code_off));
     if constexpr (!PG) {
       // [FQV2] 第3步 pertoken: max|y| over the slice (4 waves), scale, codes.  The partial
@@ -265,6 +268,19 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb,
                                                                 4, kBufferWord3);
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(scale), rs_scale, 0, 0, 0);
       }
+      if constexpr (Q != 0) {
+        // 8-bit codes (the dequant_swiglu_quant page, section 3.4): 4 bytes a row
+#pragma unroll
+        for (int it = 0; it < kIT; ++it)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r0 = 16 * it + i;  // row - 4g
+            const uint32_t v = code8x2<Q>(y[it][0][i] * inv, y[it][1][i] * inv) |
+                               (code8x2<Q>(y[it][2][i] * inv, y[it][3][i] * inv) << 16);
+            __builtin_amdgcn_raw_buffer_store_b32(v, rs_codes, code_off, r0 * kW, 0);
+            if (i == 3) __builtin_amdgcn_sched_barrier(0);
+          }
+      } else {
 #pragma unroll
       for (int it = 0; it < kIT; ++it)
 #pragma unroll
@@ -276,6 +292,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb,
                                                 rs_codes, code_off, r0 * (kW / 2), 0);
           if (i == 3) __builtin_amdgcn_sched_barrier(0);
         }
+      }
     } else {
       // [FQV2] 第3步 pergroup / 第4步: a 32-group is 8 neighbouring lanes of one row
       const auto rs_e8 = __builtin_amdgcn_make_buffer_rsrc(
@@ -529,7 +546,7 @@ hipError_t launch_w1(const Problem& pb, const Buffers& b, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int DT, bool PG, bool CLAMP, int SV>
+template <int DT, bool PG, bool CLAMP, int SV, int Q = 0>
 hipError_t launch_w2(const Problem& pb, const Buffers& b, hipStream_t s) {
   static int cus = 0;
   if (cus == 0) {
@@ -539,7 +556,7 @@ hipError_t launch_w2(const Problem& pb, const Buffers& b, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   const int grid = static_cast<int>(pb.K < cus ? pb.K : cus);
-  mfma_wide2_kernel<DT, PG, CLAMP, SV><<<grid, kWideThreads, 0, s>>>(pb, b);
+  mfma_wide2_kernel<DT, PG, CLAMP, SV, Q><<<grid, kWideThreads, 0, s>>>(pb, b);
   return hipGetLastError();
 }
 
@@ -551,6 +568,12 @@ hipError_t dispatch_w2(const Problem& pb, const Buffers& b, hipStream_t s) {
       case kE8V2Pow2: return launch_w2<DT, true, false, kE8V2Pow2>(pb, b, s);
       default: return launch_w2<DT, true, false, kE8V2Div>(pb, b, s);
     }
+  }
+  switch (pb.mode) {
+    case kPerTokenInt8: return launch_w2<DT, false, false, kE8V1, kPerTokenInt8>(pb, b, s);
+    case kPerTokenE4M3: return launch_w2<DT, false, false, kE8V1, kPerTokenE4M3>(pb, b, s);
+    case kPerTokenE5M2: return launch_w2<DT, false, false, kE8V1, kPerTokenE5M2>(pb, b, s);
+    default: break;
   }
   if (pb.d >= 7.4999f) return launch_w2<DT, false, true, kE8V1>(pb, b, s);
   return launch_w2<DT, false, false, kE8V1>(pb, b, s);
@@ -568,8 +591,8 @@ hipError_t dispatch_w1(const Problem& pb, const Buffers& b, hipStream_t s) {
 }  // namespace
 
 bool mfma_wide_supports(const Problem& pb) {
-  // (the 8-bit per-token codes are not written by this kernel's epilogue)
-  return pb.M == kW && pb.N == kW && (pb.two_sided || pb.mode == kPerGroupFp4) && !byte_codes(pb.mode);
+  // two-sided: every mode; left-only: per group (the only mode an empty P2 is valid for)
+  return pb.M == kW && pb.N == kW && (pb.two_sided || pb.mode == kPerGroupFp4);
 }
 
 hipError_t launch_mfma_wide(const Problem& pb, const Buffers& b, hipStream_t s) {

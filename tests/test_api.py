@@ -444,7 +444,7 @@ def test_8bit_strided_output_is_staged_in_the_workspace(mode):
 
 
 def test_8bit_modes_pick_a_kernel_by_shape():
-    for M, N, want in [(64, 64, 2), (32, 128, 2), (256, 256, 1), (48, 40, 1)]:
+    for M, N, want in [(64, 64, 2), (32, 128, 2), (256, 256, 3), (48, 40, 1)]:
         p = problem(K=8, M=M, N=N, mode="int8")
         st, ws, ex = fq.fq_get_workspace_size(p["x"], p["p1"], p["p2"], 1.0, 0.0, p["out"], p["sc"])
         assert st == OK

@@ -1,5 +1,6 @@
 """The comparator accepts what the tolerance rule allows and rejects the rest (CPU only)."""
 import numpy as np
+import pytest
 
 import oracle
 import synth
@@ -153,3 +154,45 @@ def test_zero_sign_rule():
     c = codes.copy()
     c[0, 7] ^= 0x8
     assert not compare(g, _repack(c), g["e8m0"])["ok"]
+
+
+def _byte_mode(mode, K=6):
+    w = synth.WORKLOADS["c2i8"]
+    x, p1, p2 = synth.make_inputs(w, 0, K)
+    return oracle.run(x, p1, p2, w.dtype, mode, 1.0)
+
+
+def _level_to_code(level, mode):
+    level = np.asarray(level, np.int16)
+    if mode == "int8":
+        return level.astype(np.int8).view(np.uint8)
+    return np.where(level < 0, 0x80 | (-level), level).astype(np.uint8)
+
+
+@pytest.mark.parametrize("mode", ["int8", "e4m3", "e5m2"])
+def test_byte_codes_rule(mode):
+    """8-bit codes: identical passes; a change of an element whose reachable range is one
+    level fails; a change to the far end of the widest reachable range passes (two or more
+    levels away where the range allows it); a change outside the range fails; a changed
+    scale fails."""
+    r = _byte_mode(mode)
+    assert compare(r, r["packed"], r["scale"])["ok"]
+    one = np.argwhere(r["lo"] == r["hi"])
+    s, f = one[len(one) // 2]
+    g = r["packed"].copy()
+    g[s, f] = _level_to_code(int(r["lvl"][s, f]) + 1, mode)
+    assert not compare(r, g, r["scale"])["ok"]
+    span = r["hi"].astype(int) - r["lo"].astype(int)
+    wide = np.argwhere(span == span.max())
+    assert span.max() >= 1
+    s, f = wide[0]
+    lv = int(r["lvl"][s, f])
+    # the end of the reachable range farthest from the oracle's level
+    target = int(r["lo"][s, f]) if lv - int(r["lo"][s, f]) >= int(r["hi"][s, f]) - lv else int(r["hi"][s, f])
+    g = r["packed"].copy()
+    g[s, f] = _level_to_code(target, mode)
+    rep = compare(r, g, r["scale"])
+    assert rep["ok"] and rep["mismatch"] == 1, rep["errors"]
+    g[s, f] = _level_to_code(int(r["hi"][s, f]) + 1, mode)
+    assert not compare(r, g, r["scale"])["ok"]
+    assert not compare(r, r["packed"], r["scale"] * np.float32(1.001))["ok"]

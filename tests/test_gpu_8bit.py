@@ -4,7 +4,8 @@ the oracle, element by element, under the same rule as the 4-bit modes (oracle/c
 codes equal except one step at a reachable rounding tie (at most ceil(1e-4 * elements)),
 the sign of an FP8 zero free where y is within error of 0, scales within 1e-5 relative.
 Every kernel that accepts the shape is run: the generic one always, the one-wave-per-slice
-MFMA kernel for its shapes (M in 16..128, N in 32..128, M*N <= 4096)."""
+MFMA kernel for its shapes (M in 16..128, N in 32..128, M*N <= 4096), the whole-workgroup
+MFMA kernel for M = N = 256."""
 import numpy as np
 import pytest
 
@@ -33,7 +34,7 @@ def test_8bit_shapes_every_kernel(mode, dt):
         clip = 1.0 if i % 2 == 0 else 0.9
         xd, p1d, p2d = to_dev(x, dt), to_dev(p1, dt), to_dev(p2, dt)
         ks = supported_kernels(xd, p1d, p2d, mode, clip, 0.0)
-        assert fq.KERNEL_GENERIC in ks and fq.KERNEL_MFMA_WIDE not in ks
+        assert fq.KERNEL_GENERIC in ks and (fq.KERNEL_MFMA_WIDE in ks) == (M == N == 256)
         for k in ks:
             rep = check(x, p1, p2, dt, mode, clip, 0.0, kernel=k, label=f"8-bit {M}x{N}")
             assert rep["ok"], rep["errors"]
@@ -46,6 +47,18 @@ def test_8bit_ragged_k(mode):
         x, p1, p2 = synth.make_inputs(w, 0, K)
         rep = check(x, p1, p2, w.dtype, mode, 1.0, 0.0, label=f"8-bit ragged K={K}",
                     slices=sorted({0, K // 2, K - 1}))
+        assert rep["ok"], rep["errors"]
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_8bit_whole_workgroup_kernel_ragged_k(mode):
+    """M = N = 256 (the two-sided 256-class kernel) with K leaving some CUs two or three
+    slices and others one, on the 256-class activation workload's distribution."""
+    w = synth.WORKLOADS["c4"]
+    for K in (257, 515):
+        x, p1, p2 = synth.make_inputs(w, 0, K)
+        rep = check(x, p1, p2, w.dtype, mode, 1.0, 0.0, kernel=fq.KERNEL_MFMA_WIDE, label=f"8-bit 256 K={K}",
+                    slices=sorted({0, 1, 255, 256, 257 % K, K // 2, K - 2, K - 1}))
         assert rep["ok"], rep["errors"]
 
 
