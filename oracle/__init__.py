@@ -89,6 +89,9 @@ def lib():
         L.fqo_dequant.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                   p, p, p]
         L.fqo_dequant.restype = ctypes.c_int
+        L.fqo_dequant8.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                   p, p, p]
+        L.fqo_dequant8.restype = ctypes.c_int
         L.fqo_mx_gemm.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, p, p, p, p, p, p]
         L.fqo_mx_gemm.restype = ctypes.c_int
         _lib = L
@@ -252,9 +255,19 @@ def dequant(packed: np.ndarray, scale: np.ndarray, M: int, N: int, dtype: str, m
     """Values of the codes (uint16 bits of the output dtype, [S, M, N]): q * scale per
     token, E2M1 value * 2^(e8m0 - 127) per group (see fqo_dequant in fq_oracle.c).
 
-    packed: [S, M*N/2] bytes as the quantizer writes them (low nibble first); scale: fp32
-    [S] per token ("int32" / "int4"), e8m0 bytes [S, 2*ceil(M*N/64)] per group ("fp4")."""
+    packed: [S, M*N/2] bytes as the quantizer writes them (low nibble first), [S, M*N] for
+    the 8-bit codes; scale: fp32 [S] per token ("int32" / "int4" / "int8" / "e4m3" / "e5m2"),
+    e8m0 bytes [S, 2*ceil(M*N/64)] per group ("fp4")."""
     S = packed.shape[0]
+    if mode in ("int8", "e4m3", "e5m2"):  # one byte a code, fp32 scales [S]
+        codes = np.ascontiguousarray(packed, dtype=np.uint8).reshape(S, M * N)
+        scale = np.ascontiguousarray(scale, dtype=np.float32).reshape(S)
+        out = np.empty((S, M, N), np.uint16)
+        st = lib().fqo_dequant8(_DT[dtype], QFMT[mode], S, M, N, codes.ctypes.data, scale.ctypes.data,
+                                out.ctypes.data)
+        if st != 0:
+            raise ValueError(f"fqo_dequant8 rejected the arguments ({st})")
+        return out
     packed = np.ascontiguousarray(packed, dtype=np.uint8).reshape(S, M * N // 2)
     if mode in ("int32", "int4"):
         scale = np.ascontiguousarray(scale, dtype=np.float32).reshape(S)

@@ -733,6 +733,25 @@ static uint16_t f16_bits(double v) {
   return s | (uint16_t)((e + 15) << 10) | mant;
 }
 
+int fqo_dequant8(int dtype, int qfmt, int64_t S, int64_t M, int64_t N, const uint8_t* codes,
+                 const float* scale, uint16_t* out) {
+  /* 8-bit per-token codes: value = RNE_dt(fl32(v * scale_k)), v the INT8 integer or the FP8
+   * value of the code (the same rule as the int4 codes) */
+  if (dtype != FQO_F16 && dtype != FQO_BF16) return -1;
+  if (qfmt != FQO_Q_INT8 && qfmt != FQO_Q_E4M3 && qfmt != FQO_Q_E5M2) return -1;
+  const int64_t MN = M * N;
+  if (M < 1 || N < 1) return -1;
+  for (int64_t k = 0; k < S; ++k)
+    for (int64_t f = 0; f < MN; ++f) {
+      const int c = codes[k * MN + f];
+      const double q = qfmt == FQO_Q_INT8 ? (double)(int8_t)c : fqo_fp8_value(c, qfmt);
+      const float prod = (float)q * scale[k]; /* IEEE fp32 product (q is exact in fp32) */
+      const double r = round_dt((double)prod, dtype);
+      out[k * MN + f] = dtype == FQO_BF16 ? bf16_bits(r) : f16_bits(r);
+    }
+  return 0;
+}
+
 int fqo_dequant(int dtype, int mode, int64_t S, int64_t M, int64_t N, const uint8_t* packed,
                 const void* scale, uint16_t* out) {
   if (dtype != FQO_F16 && dtype != FQO_BF16) return -1;

@@ -652,3 +652,51 @@ def test_pertoken_8bit_zero_slice_and_sign_of_fp8_zero():
         assert r["packed"].shape == (1, 32)
     # a tiny negative value keeps its sign in FP8 (code 0x80), not in INT8
     assert oracle.fp8_code(-1e-30, "e4m3") == 0x80 and oracle.int8_code(-1e-30) == 0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("mode", ["int8", "e4m3", "e5m2"])
+def test_dequant_8bit_every_code_against_fp32_product(mode, dtype):
+    """Every code the quantizer can write (INT8 -127..127; every finite FP8 code, both signs)
+    times fp32 scales from subnormal to overflowing: the oracle's values equal numpy's fp32
+    product of the code's value (torch's float8 decoding for FP8) and the scale, cast to the
+    dtype."""
+    rng = np.random.default_rng(9)
+    scales = np.concatenate([
+        np.array([0.0, 1e-45, 1.2e-38, 2.0 ** -20, 0.125, 1.0, 7.0 / 3.0, 1e4, 3e37, 3.3e38], np.float32),
+        np.abs(rng.standard_normal(20) * np.exp(rng.uniform(-30, 30, 20))).astype(np.float32)])
+    if mode == "int8":
+        codes = np.arange(-127, 128).astype(np.int8).view(np.uint8)
+        q = codes.view(np.int8).astype(np.float32)
+    else:
+        top = 0x7E if mode == "e4m3" else 0x7B
+        codes = np.concatenate([np.arange(top + 1), 0x80 | np.arange(top + 1)]).astype(np.uint8)
+        q = torch.from_numpy(codes).view(FP8_TORCH[mode]).to(torch.float32).numpy()
+    S, MN = scales.size, codes.size
+    got = oracle.dequant(np.tile(codes, (S, 1)), scales, 1, MN, dtype, mode).reshape(S, MN)
+    with np.errstate(over="ignore"):
+        v32 = q[None, :] * scales[:, None]  # IEEE fp32 product
+    _same_bits(got.reshape(-1), _to_dt_bits(v32, dtype).reshape(-1), dtype)
+
+
+@pytest.mark.parametrize("mode", ["int8", "e4m3", "e5m2"])
+def test_dequant_8bit_round_trip_within_half_a_step(mode):
+    """dequantize(quantize(y)) is within half a code step of y (times the scale), plus half
+    an output ulp, for every element (clip 1: nothing saturates)."""
+    w = synth.WORKLOADS["c2i8"]
+    x, p1, p2 = synth.make_inputs(w, 0, 4)
+    r = oracle.run(x, p1, p2, w.dtype, mode, 1.0, want_y=True, ranges=False)
+    v = oracle.dt_to_float(oracle.dequant(r["packed"], r["scale"], w.M, w.N, w.dtype, mode), w.dtype)
+    y = r["y"].reshape(4, -1).astype(np.float64)
+    v = v.reshape(4, -1)
+    s = r["scale"].astype(np.float64)[:, None]
+    if mode == "int8":
+        step = np.full_like(y, 1.0)
+    else:
+        top = 0x7E if mode == "e4m3" else 0x7B
+        table = np.array([oracle.fp8_value(c, mode) for c in range(top + 1)])
+        q = np.minimum(np.abs(y / s), table[top])
+        idx = np.clip(np.searchsorted(table, q), 1, top)
+        step = table[idx] - table[idx - 1]
+    bound = 0.5 * step * s * (1 + 1e-5) + np.abs(v) * 2.0 ** -8 + 1e-30
+    assert np.all(np.abs(v - y) <= bound)
