@@ -43,11 +43,12 @@ def algorithmic_bytes(w, K=None) -> int:
 
 
 def dequant_bytes(w, K=None) -> int:
-    """Bytes one dequantization launch must move: read the codes (0.5 B/elem) and scales,
-    write the values (2 B/elem)."""
+    """Bytes one dequantization launch must move: read the codes (0.5 B/elem, 1 B/elem for
+    the 8-bit modes) and scales, write the values (2 B/elem)."""
     K = w.K if K is None else K
     MN = w.M * w.N
-    b = K * MN // 2 + 2 * K * MN
+    codes = K * MN if w.mode in ("int8", "e4m3", "e5m2") else K * MN // 2
+    b = codes + 2 * K * MN
     b += K * 2 * (-(-MN // 64)) if w.mode == "fp4" else 4 * K
     return b
 
@@ -304,7 +305,9 @@ def bench_dequant(args, w, x_host, p1, p2, to_dev, dev, tdt):
     gbs = bytes_ / (ms / 1e3) / 1e9
     roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": profiled_traffic(w, "dequant"),
-            "kernel": "dequant32_kernel" if (w.M * w.N) % 32 == 0 else "dequant_bytes_kernel",
+            "kernel": (("dequant8_kernel" if (w.M * w.N) % 8 == 0 else "dequant8_each_kernel")
+                       if w.mode in ("int8", "e4m3", "e5m2") else
+                       ("dequant32_kernel" if (w.M * w.N) % 32 == 0 else "dequant_bytes_kernel")),
             "avg_launch_us": round(ms * 1e3, 3), "algorithmic_bytes": bytes_}
     cpu = None
     if not args.no_cpu:

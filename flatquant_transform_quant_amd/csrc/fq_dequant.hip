@@ -13,7 +13,13 @@
 // even, to the output dtype.  Codes are read in the packed layouts the quantizer writes:
 // K * M*N/2 bytes, low nibble = lower flattened index; e8m0 [K, 2*ceil(M*N/64)] bytes.
 //
-// HBM-bound streaming (0.5 byte in, 2 bytes out per element).  Slices whose element
+// 8-bit per-token codes (INT8, FP8 E4M3FN, FP8 E5M2; the quantizer writes them from the
+// dynamic per-row rule of the dequant_swiglu_quant page, section 3.4): value = q * scale_k in
+// IEEE fp32, rounded once to the dtype, q the INT8 integer or the FP8 value (gfx950's exact
+// fp8 -> fp32 conversion).  Codes the quantizer never writes (INT8 -128, the FP8 NaN and
+// infinity encodings) are outside the domain.
+//
+// HBM-bound streaming (0.5 byte in, 2 bytes out per element; 1 byte in for 8-bit codes).  Slices whose element
 // count is a multiple of 32 take the fast path (8 codes -> 16 bytes per lane and step, each
 // instruction of a wave one contiguous run); other shapes take a thread per code byte.
 #include <hip/hip_runtime.h>
@@ -100,6 +106,79 @@ __global__ __launch_bounds__(kDqThreads) void dequant_bytes_kernel(const uint8_t
   reinterpret_cast<uint32_t*>(out)[bi] = round16x2<DT>(dq_value<PG>(byte & 15u, sc, e8), dq_value<PG>(byte >> 4, sc, e8));
 }
 
+// 8-bit codes, fast path: a wave covers 2048 consecutive codes in four steps; at step w lane
+// l turns the 8 codes base + 512 w + 8 l .. +7 (8 bytes) into 16 output bytes, so every load
+// and store instruction of the wave is one contiguous run (512 B of codes, 1 KB of values).
+// An 8-code run never leaves its slice (M*N is a multiple of 8).
+// values of bytes 0, 1 (HI = false) or 2, 3 (HI = true) of w
+template <int MODE, bool HI>
+__device__ __forceinline__ float2 q8x2(uint32_t w) {
+  if constexpr (MODE == kPerTokenInt8) {
+    const uint32_t h = HI ? w >> 16 : w;
+    return float2{static_cast<float>(static_cast<int8_t>(h & 0xFFu)), static_cast<float>(static_cast<int8_t>((h >> 8) & 0xFFu))};
+  } else {
+    typedef __attribute__((ext_vector_type(2))) float f2;
+    const f2 v = MODE == kPerTokenE4M3 ? __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), HI)
+                                       : __builtin_amdgcn_cvt_pk_f32_bf8(static_cast<int>(w), HI);
+    return float2{v[0], v[1]};
+  }
+}
+
+template <int DT, int MODE>
+__global__ __launch_bounds__(kDqThreads) void dequant8_kernel(const uint8_t* __restrict__ codes,
+                                                               const float* __restrict__ scale,
+                                                               uint16_t* __restrict__ out, uint32_t runs,
+                                                               uint32_t runs_per_slice) {
+  typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t wave_run = (blockIdx.x * kDqThreads + (threadIdx.x & ~63u)) * 4;  // first 8-code run
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t r = wave_run + 64 * w + lane;  // this lane's run: codes 8r .. 8r+7
+    if (r >= runs) break;
+    const u32x2_t c = reinterpret_cast<const u32x2_t*>(codes)[r];
+    const float sc = scale[r / runs_per_slice];
+    const float2 q0 = q8x2<MODE, false>(c[0]), q1 = q8x2<MODE, true>(c[0]);
+    const float2 q2 = q8x2<MODE, false>(c[1]), q3 = q8x2<MODE, true>(c[1]);
+    reinterpret_cast<u32x4_t*>(out)[r] = u32x4_t{round16x2<DT>(q0.x * sc, q0.y * sc), round16x2<DT>(q1.x * sc, q1.y * sc),
+                                                 round16x2<DT>(q2.x * sc, q2.y * sc), round16x2<DT>(q3.x * sc, q3.y * sc)};
+  }
+}
+
+// 8-bit codes, any shape: a thread per code.
+template <int DT, int MODE>
+__global__ __launch_bounds__(kDqThreads) void dequant8_each_kernel(const uint8_t* __restrict__ codes,
+                                                                    const float* __restrict__ scale,
+                                                                    uint16_t* __restrict__ out, uint64_t count,
+                                                                    uint64_t mn) {
+  const uint64_t e = static_cast<uint64_t>(blockIdx.x) * kDqThreads + threadIdx.x;
+  if (e >= count) return;
+  float v = q8x2<MODE, false>(codes[e]).x * scale[e / mn];
+  // the fp32 product is rounded to the dtype on its own: without the register barrier the
+  // compiler fuses product and conversion into one mixed-precision FMA with a +0 addend,
+  // which rounds once (not twice) and turns a -0 product into +0
+  asm volatile("" : "+v"(v));
+  out[e] = static_cast<uint16_t>(round16x2<DT>(v, 0.0f));
+}
+
+template <int DT, int MODE>
+hipError_t launch_dq8(int64_t K, int64_t MN, const uint8_t* codes, const float* scale, uint16_t* out, hipStream_t s) {
+  const bool aligned = (reinterpret_cast<uintptr_t>(codes) % 8 == 0) && (reinterpret_cast<uintptr_t>(out) % 16 == 0);
+  if (MN % 8 == 0 && aligned) {
+    const uint64_t runs = static_cast<uint64_t>(K) * (MN / 8);  // < 2^32
+    const uint64_t per_block = 4 * kDqThreads;
+    const uint32_t grid = static_cast<uint32_t>((runs + per_block - 1) / per_block);
+    dequant8_kernel<DT, MODE><<<grid, kDqThreads, 0, s>>>(codes, scale, out, static_cast<uint32_t>(runs),
+                                                          static_cast<uint32_t>(MN / 8));
+  } else {
+    const uint64_t count = static_cast<uint64_t>(K) * MN;
+    const uint64_t grid = (count + kDqThreads - 1) / kDqThreads;
+    dequant8_each_kernel<DT, MODE><<<static_cast<uint32_t>(grid), kDqThreads, 0, s>>>(codes, scale, out, count,
+                                                                                    static_cast<uint64_t>(MN));
+  }
+  return hipGetLastError();
+}
+
 template <int DT, bool PG>
 hipError_t launch_dq(int64_t K, int64_t MN, const uint8_t* codes, const void* scale, uint16_t* out,
                      hipStream_t s) {
@@ -121,6 +200,19 @@ hipError_t launch_dq(int64_t K, int64_t MN, const uint8_t* codes, const void* sc
 }
 
 }  // namespace
+
+hipError_t launch_dequant8(int32_t dtype, int32_t mode, int64_t K, int64_t M, int64_t N, const uint8_t* codes,
+                           const float* scale, uint16_t* out, hipStream_t s) {
+  const int64_t MN = M * N;
+  if (dtype == kBF16) {
+    if (mode == kPerTokenInt8) return launch_dq8<kBF16, kPerTokenInt8>(K, MN, codes, scale, out, s);
+    if (mode == kPerTokenE4M3) return launch_dq8<kBF16, kPerTokenE4M3>(K, MN, codes, scale, out, s);
+    return launch_dq8<kBF16, kPerTokenE5M2>(K, MN, codes, scale, out, s);
+  }
+  if (mode == kPerTokenInt8) return launch_dq8<kF16, kPerTokenInt8>(K, MN, codes, scale, out, s);
+  if (mode == kPerTokenE4M3) return launch_dq8<kF16, kPerTokenE4M3>(K, MN, codes, scale, out, s);
+  return launch_dq8<kF16, kPerTokenE5M2>(K, MN, codes, scale, out, s);
+}
 
 hipError_t launch_dequant(int32_t dtype, bool per_group, int64_t K, int64_t M, int64_t N, const uint8_t* codes,
                           const void* scale, uint16_t* out, hipStream_t s) {

@@ -377,10 +377,19 @@ fq_status fq_dequant(const fq_tensor* codes, const fq_tensor* scale, const fq_te
   const int64_t MN = M * N;
   // codes and scales as the quantizer writes them ([FQV2] 参数速查)
   bool per_group;
+  int32_t mode8 = -1;  // the 8-bit per-token mode, if the codes are one a byte
   switch (codes->dtype) {
     case FQ_DT_INT32:
       if (N % 8 != 0 || !shape_is(*codes, 3, K, M, N / 8)) return FQ_ERR_PARAM_INVALID;
       per_group = false;
+      break;
+    case FQ_DT_INT8:
+    case FQ_DT_FLOAT8_E4M3FN:
+    case FQ_DT_FLOAT8_E5M2:
+      if (!shape_is(*codes, 3, K, M, N)) return FQ_ERR_PARAM_INVALID;
+      per_group = false;
+      mode8 = codes->dtype == FQ_DT_INT8 ? fq::kPerTokenInt8
+                                        : (codes->dtype == FQ_DT_FLOAT8_E4M3FN ? fq::kPerTokenE4M3 : fq::kPerTokenE5M2);
       break;
     case FQ_DT_INT4:
       if (N % 2 != 0 || !shape_is(*codes, 3, K, M, N)) return FQ_ERR_PARAM_INVALID;
@@ -405,9 +414,12 @@ fq_status fq_dequant(const fq_tensor* codes, const fq_tensor* scale, const fq_te
   if (reinterpret_cast<uintptr_t>(out->data) % 4 != 0 || (!per_group && reinterpret_cast<uintptr_t>(scale->data) % 4 != 0))
     return FQ_ERR_PARAM_INVALID;
   if (!device_is_gfx950()) return fail_runtime("the current device is not gfx950", hipSuccess);
+  const int32_t odt = out->dtype == FQ_DT_FLOAT16 ? fq::kF16 : fq::kBF16;
   const hipError_t err =
-      fq::launch_dequant(out->dtype == FQ_DT_FLOAT16 ? fq::kF16 : fq::kBF16, per_group, K, M, N,
-                         static_cast<const uint8_t*>(codes->data), scale->data, static_cast<uint16_t*>(out->data), stream);
+      mode8 >= 0 ? fq::launch_dequant8(odt, mode8, K, M, N, static_cast<const uint8_t*>(codes->data),
+                                       static_cast<const float*>(scale->data), static_cast<uint16_t*>(out->data), stream)
+                 : fq::launch_dequant(odt, per_group, K, M, N, static_cast<const uint8_t*>(codes->data), scale->data,
+                                      static_cast<uint16_t*>(out->data), stream);
   if (err != hipSuccess) return fail_runtime("dequant kernel launch", err);
   return FQ_SUCCESS;
 }

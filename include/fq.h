@@ -150,6 +150,11 @@ fq_status fq_run(void* workspace, uint64_t workspaceSize, fq_executor* executor,
  *   per group (codes FLOAT4_E2M1 [K, M*N], scale FLOAT8_E8M0 [K, ceilDiv(M*N, 64), 2]):
  *       value = E2M1(code) * 2^(e8m0 - 127), E2M1 magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 with
  *       the sign bit on top (the ModelOpt page, section 6.1; [FQV2] 第3步 pergroup)
+ *   per token, 8-bit (codes INT8 | FLOAT8_E4M3FN | FLOAT8_E5M2 [K, M, N], scale FLOAT32 [K]):
+ *       value = q * scale[k], q the INT8 integer or the FP8 value of the code (the codes of
+ *       the dynamic per-row quantization of the dequant_swiglu_quant page, section 3.4);
+ *       INT8 -128 and the FP8 NaN / infinity encodings, which fq_run never writes, are
+ *       outside the domain
  * The product is formed in IEEE fp32 (per group it is exact, or overflows to infinity; an
  * e8m0 byte 0xFF, NaN in the MX encoding, makes its group NaN) and rounded once, to
  * nearest even, to out's dtype.

@@ -451,3 +451,18 @@ def test_8bit_modes_pick_a_kernel_by_shape():
         k = fq.lib.fq_executor_kernel(ex)
         fq.fq_executor_destroy(ex)
         assert k == want, (M, N, k)
+
+
+@pytest.mark.parametrize("mode", ["int8", "e4m3", "e5m2"])
+def test_dequant_8bit_codes_arguments(mode):
+    """8-bit codes: [K, M, N] one byte a code with FLOAT32 [K] scales; other shapes, e8m0
+    scales or a wrong scale count are rejected before any HIP call."""
+    dt = fq.BYTE_MODES[mode]
+    o = tens(fq.DT_BFLOAT16, (4, 16, 16))
+    s = tens(fq.DT_FLOAT32, (4,))
+    assert fq.fq_dequant(tens(dt, (4, 16, 8)), s, o, 0) == INVAL
+    assert fq.fq_dequant(tens(dt, (4, 256)), s, o, 0) == INVAL
+    assert fq.fq_dequant(tens(dt, (4, 16, 16)), tens(fq.DT_FLOAT8_E8M0, (4, 4, 2)), o, 0) == INVAL
+    assert fq.fq_dequant(tens(dt, (4, 16, 16)), tens(fq.DT_FLOAT32, (3,)), o, 0) == INVAL
+    assert fq.fq_dequant(tens(dt, (4, 16, 16), (512, 32, 1)), s, o, 0) == INVAL  # contiguous only
+    assert fq.fq_dequant(None, s, o, 0) == NULLP

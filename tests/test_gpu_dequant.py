@@ -103,3 +103,50 @@ def test_full_size_c2_round_trip():
     packed, scale = fetch(out, sc, w.mode, w.K)
     got = _gpu_dequant(out, sc, w.mode, w.M, w.N, w.dtype)
     _assert_same(got, oracle.dequant(packed, scale, w.M, w.N, w.dtype, w.mode), w.dtype, "c2 full")
+
+
+def _valid_8bit_codes(K, MN, mode, rng):
+    """Random codes the quantizer can write: INT8 -127..127, finite FP8 codes of both signs."""
+    if mode == "int8":
+        return rng.integers(-127, 128, (K, MN)).astype(np.int8).view(np.uint8)
+    top = 0x7E if mode == "e4m3" else 0x7B
+    mag = rng.integers(0, top + 1, (K, MN)).astype(np.uint8)
+    return mag | (rng.integers(0, 2, (K, MN)).astype(np.uint8) << 7)
+
+
+@pytest.mark.parametrize("mode", ["int8", "e4m3", "e5m2"])
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_dequant_8bit_codes_match_oracle(mode, dt):
+    """Every shape (the 8-codes-a-lane path when M*N is a multiple of 8, a thread a code
+    otherwise), the special scales, and every code at least once: bit-exact."""
+    rng = np.random.default_rng(13)
+    for M, N in [(16, 16), (64, 64), (256, 256), (1, 1), (3, 5), (7, 9), (33, 40)]:
+        for K in (1, 7, 300 if M * N <= 4096 else 9):
+            say(f"[gpu] dequant {mode} {dt} K={K} M={M} N={N}")
+            codes = _valid_8bit_codes(K, M * N, mode, rng)
+            sc = np.abs(rng.standard_normal(K) * np.exp(rng.uniform(-25, 25, K))).astype(np.float32)
+            special = np.array([0.0, 1e-45, 1.1e-38, 1.0, 7.0 / 3.0, 3.3e38], np.float32)
+            sc[rng.integers(0, K, min(K, special.size))] = special[: min(K, special.size)]
+            out, scd = fq.empty_outputs(K, M, N, mode, DEV)
+            out.view(torch.uint8).copy_(torch.from_numpy(codes).reshape(K, M, N))
+            scd.copy_(torch.from_numpy(sc))
+            got = _gpu_dequant(out, scd, mode, M, N, dt)
+            _assert_same(got, oracle.dequant(codes, sc, M, N, dt, mode), dt, f"{mode} {dt} {K}x{M}x{N}")
+
+
+@pytest.mark.parametrize("key", ["c2i8", "c2e4m3", "c2e5m2", "c4i8"])
+def test_8bit_round_trip_matches_oracle_and_reports_rms(key):
+    w = synth.WORKLOADS[key]
+    K = 64 if w.M * w.N <= 8192 else 8
+    x, p1, p2 = synth.make_inputs(w, 0, K)
+    out, sc = run_lib(to_dev(x, w.dtype), to_dev(p1, w.dtype), to_dev(p2, w.dtype), w.mode, w.clip_ratio,
+                      w.dst_type_max)
+    packed, scale = fetch(out, sc, w.mode, K)
+    got = _gpu_dequant(out, sc, w.mode, w.M, w.N, w.dtype)
+    _assert_same(got, oracle.dequant(packed, scale, w.M, w.N, w.dtype, w.mode), w.dtype, f"{key} round trip")
+    y = oracle.run(x[:4], p1, p2, w.dtype, w.mode, w.clip_ratio, w.dst_type_max, ranges=False,
+                   want_y=True)["y"].reshape(4, -1).astype(np.float64)
+    v = oracle.dt_to_float(got[:4], w.dtype).reshape(4, -1)
+    rel = np.sqrt(((v - y) ** 2).sum() / (y ** 2).sum())
+    say(f"[gpu]   {key}: relative RMS error of dequantize(quantize(y)) against y = {rel:.4f}")
+    assert rel < 0.1
