@@ -92,6 +92,8 @@ def lib():
         L.fqo_dequant8.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                    p, p, p]
         L.fqo_dequant8.restype = ctypes.c_int
+        L.fqo_int4_gemm.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, p, p, p, p, p]
+        L.fqo_int4_gemm.restype = ctypes.c_int
         L.fqo_mx_gemm.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, p, p, p, p, p, p]
         L.fqo_mx_gemm.restype = ctypes.c_int
         _lib = L
@@ -308,3 +310,19 @@ def mx_gemm(a: np.ndarray, a_e8: np.ndarray, w: np.ndarray, w_e8: np.ndarray, H:
     if st != 0:
         raise ValueError(f"fqo_mx_gemm rejected the arguments ({st})")
     return c, cabs
+
+
+def int4_gemm(a: np.ndarray, sa: np.ndarray, w: np.ndarray, sw: np.ndarray, H: int) -> np.ndarray:
+    """C [T, O] fp32 = fl32(fl32(acc) * fl32(sa[t] * sw[o])), acc the exact int4 dot product
+    (see fqo_int4_gemm).  a [T, H/2], w [O, H/2] int4 code bytes (low nibble first); sa [T],
+    sw [O] fp32."""
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    sa = np.ascontiguousarray(sa, dtype=np.float32)
+    sw = np.ascontiguousarray(sw, dtype=np.float32)
+    T, O = a.shape[0], w.shape[0]
+    c = np.empty((T, O), np.float32)
+    st = lib().fqo_int4_gemm(T, O, H, a.ctypes.data, sa.ctypes.data, w.ctypes.data, sw.ctypes.data, c.ctypes.data)
+    if st != 0:
+        raise ValueError(f"fqo_int4_gemm rejected the arguments ({st})")
+    return c

@@ -787,6 +787,29 @@ int fqo_dequant(int dtype, int mode, int64_t S, int64_t M, int64_t N, const uint
  * below H 2^-53 sum|terms|); `c` receives the sums, `cabs` (if non-NULL) sum|terms|, from
  * which the comparison derives the bound any fp32 accumulation order can reach.  e8m0
  * bytes 0xFF are outside this function's domain (the quantizer never writes them). */
+/* int4 consumer GEMM (the per-token int4 codes as A, per-output-channel int4 weights as W):
+ *   acc[t,o] = sum_h qa[t,h] * qw[o,h]          exact (an int64 sum of int4 products)
+ *   C[t,o]   = fl32( fl32(acc) * fl32(sa[t] * sw[o]) )
+ * reading: the integer dot product is exact (any implementation accumulating in int32 reaches
+ * it, |acc| <= 64 H), the two scales are multiplied first, then the product with acc; both in
+ * IEEE fp32 ([APT] 2.1: the symmetric integer format dequantizes as q * scale, so the product
+ * of two such values is qa qw sa sw).  Codes two a byte, low nibble first, two's complement. */
+int fqo_int4_gemm(int64_t T, int64_t O, int64_t H, const uint8_t* a, const float* sa, const uint8_t* w,
+                  const float* sw, float* c) {
+  if (T < 1 || O < 1 || H < 2 || H % 2) return -1;
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t o = 0; o < O; ++o) {
+      int64_t acc = 0;
+      for (int64_t h = 0; h < H; ++h) {
+        const int na = (a[t * (H / 2) + h / 2] >> (4 * (h & 1))) & 15, nw = (w[o * (H / 2) + h / 2] >> (4 * (h & 1))) & 15;
+        acc += (int64_t)(na >= 8 ? na - 16 : na) * (int64_t)(nw >= 8 ? nw - 16 : nw);
+      }
+      const float s = sa[t] * sw[o];
+      c[t * O + o] = (float)acc * s;
+    }
+  return 0;
+}
+
 int fqo_mx_gemm(int64_t T, int64_t O, int64_t H, const uint8_t* a, const uint8_t* a_e8, const uint8_t* w,
                 const uint8_t* w_e8, double* c, double* cabs) {
   if (T < 1 || O < 1 || H < 2 || H % 32 != 0) return -1;

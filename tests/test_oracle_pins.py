@@ -700,3 +700,46 @@ def test_dequant_8bit_round_trip_within_half_a_step(mode):
         step = table[idx] - table[idx - 1]
     bound = 0.5 * step * s * (1 + 1e-5) + np.abs(v) * 2.0 ** -8 + 1e-30
     assert np.all(np.abs(v - y) <= bound)
+
+
+# ---------------------------------------------------------------- int4 consumer GEMM
+
+def _int4_values(codes: np.ndarray) -> np.ndarray:
+    lo, hi = (codes & 15).astype(np.int64), (codes >> 4).astype(np.int64)
+    v = np.empty((codes.shape[0], codes.shape[1] * 2), np.int64)
+    v[:, 0::2], v[:, 1::2] = np.where(lo >= 8, lo - 16, lo), np.where(hi >= 8, hi - 16, hi)
+    return v
+
+
+def test_int4_gemm_integer_part_against_numpy_matmul():
+    """With unit scales C is fl32 of the exact integer dot product: numpy's int64 matmul of
+    the decoded codes (|acc| < 2^24, so the fp32 value is exact)."""
+    rng = np.random.default_rng(31)
+    T, O, H = 19, 23, 384
+    a = rng.integers(0, 256, (T, H // 2), dtype=np.uint8)
+    w = rng.integers(0, 256, (O, H // 2), dtype=np.uint8)
+    c = oracle.int4_gemm(a, np.ones(T, np.float32), w, np.ones(O, np.float32), H)
+    ref = _int4_values(a) @ _int4_values(w).T
+    assert np.array_equal(c.astype(np.int64), ref)
+    # the extremes: every product -8 * -8 = 64
+    full = np.full((1, H // 2), 0x88, np.uint8)
+    assert oracle.int4_gemm(full, np.ones(1, np.float32), full, np.ones(1, np.float32), H)[0, 0] == 64 * H
+
+
+def test_int4_gemm_scales_apply_as_one_fp32_factor():
+    """Power-of-two scales are exact: C = acc * sa * sw exactly; with general scales C is
+    fl32(acc * fl32(sa * sw)) (numpy's fp32 arithmetic on the same operands)."""
+    rng = np.random.default_rng(32)
+    T, O, H = 7, 9, 256
+    a = rng.integers(0, 256, (T, H // 2), dtype=np.uint8)
+    w = rng.integers(0, 256, (O, H // 2), dtype=np.uint8)
+    acc = _int4_values(a) @ _int4_values(w).T
+    sa = np.float32(2.0) ** rng.integers(-20, 20, T).astype(np.float32)
+    sw = np.float32(2.0) ** rng.integers(-20, 20, O).astype(np.float32)
+    c = oracle.int4_gemm(a, sa, w, sw, H)
+    assert np.array_equal(c.astype(np.float64), acc * sa[:, None].astype(np.float64) * sw[None, :])
+    sa = np.abs(rng.standard_normal(T)).astype(np.float32)
+    sw = np.abs(rng.standard_normal(O)).astype(np.float32)
+    c = oracle.int4_gemm(a, sa, w, sw, H)
+    want = acc.astype(np.float32) * (sa[:, None] * sw[None, :])
+    assert np.array_equal(c, want)
