@@ -86,6 +86,8 @@ def _load():
     L.fq_v1_get_workspace_size.restype = ctypes.c_int32
     L.fq_mx_gemm.argtypes = [P, P, P, P, P, vp]
     L.fq_mx_gemm.restype = ctypes.c_int32
+    L.fq_int4_gemm.argtypes = [P, P, P, P, P, vp]
+    L.fq_int4_gemm.restype = ctypes.c_int32
     L.fq_dequant.argtypes = [P, P, P, vp]
     L.fq_dequant.restype = ctypes.c_int32
     return L
@@ -93,7 +95,8 @@ def _load():
 
 lib = _load()
 EXPORTS = ("fq_get_workspace_size", "fq_run", "fq_executor_destroy", "fq_executor_set_repeatable",
-           "fq_executor_set_kernel", "fq_executor_kernel", "fq_status_string", "fq_last_error", "fq_dequant", "fq_v1_get_workspace_size", "fq_mx_gemm")
+           "fq_executor_set_kernel", "fq_executor_kernel", "fq_status_string", "fq_last_error", "fq_dequant", "fq_v1_get_workspace_size", "fq_mx_gemm",
+           "fq_int4_gemm")
 
 
 def status_string(status: int) -> str:
@@ -167,6 +170,11 @@ def fq_status_string(status: int) -> str:
 
 def fq_last_error() -> str:
     return lib.fq_last_error().decode()
+
+
+def fq_int4_gemm(a: FqTensor, a_scale: FqTensor, w: FqTensor, w_scale: FqTensor, c: FqTensor, stream_ptr: int) -> int:
+    ref = lambda t: ctypes.byref(t) if t is not None else None  # noqa: E731
+    return lib.fq_int4_gemm(ref(a), ref(a_scale), ref(w), ref(w_scale), ref(c), stream_ptr or None)
 
 
 def fq_mx_gemm(a: FqTensor, a_scale: FqTensor, w: FqTensor, w_scale: FqTensor, c: FqTensor, stream_ptr: int) -> int:
@@ -333,4 +341,27 @@ def mx_gemm(a_codes, a_scale, w_codes, w_scale, H: int, out_dtype=None, out=None
                     (stream if stream is not None else torch.cuda.current_stream(a_codes.device)).cuda_stream)
     if st != FQ_SUCCESS:
         raise FqError(st, "fq_mx_gemm")
+    return out
+
+
+def int4_gemm(a_codes, a_scale, w_codes, w_scale, H: int, out_dtype=None, out=None, stream=None):
+    """C [T, O] = a_scale[t] w_scale[o] (A . W^T) for int4 codes in the quantizer's per-token
+    storage: codes uint8 [rows, H/2] (the int4 / int32 out of ``empty_outputs`` viewed as
+    bytes), scales float32 [rows].  C is torch.bfloat16 (default) or torch.float32."""
+    torch = _torch()
+    for t in (a_codes, a_scale, w_codes, w_scale):
+        if not t.is_contiguous():
+            raise ValueError("int4_gemm operands must be contiguous")
+    T, O = a_codes.shape[0], w_codes.shape[0]
+    if out is None:
+        out = torch.empty((T, O), dtype=out_dtype or torch.bfloat16, device=a_codes.device)
+    cdt = {torch.bfloat16: DT_BFLOAT16, torch.float32: DT_FLOAT32}.get(out.dtype, -1)
+    st = fq_int4_gemm(make_tensor(a_codes.data_ptr(), DT_INT4, (T, H)),
+                      make_tensor(a_scale.data_ptr(), DT_FLOAT32, (T,)),
+                      make_tensor(w_codes.data_ptr(), DT_INT4, (O, H)),
+                      make_tensor(w_scale.data_ptr(), DT_FLOAT32, (O,)),
+                      make_tensor(out.data_ptr(), cdt, out.shape, out.stride()),
+                      (stream if stream is not None else torch.cuda.current_stream(a_codes.device)).cuda_stream)
+    if st != FQ_SUCCESS:
+        raise FqError(st, "fq_int4_gemm")
     return out

@@ -424,6 +424,37 @@ fq_status fq_dequant(const fq_tensor* codes, const fq_tensor* scale, const fq_te
   return FQ_SUCCESS;
 }
 
+fq_status fq_int4_gemm(const fq_tensor* a, const fq_tensor* a_scale, const fq_tensor* w, const fq_tensor* w_scale,
+                       const fq_tensor* c, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  for (const fq_tensor* t : {a, a_scale, w, w_scale, c})
+    if (!t || !t->data) return FQ_ERR_PARAM_NULLPTR;
+  for (const fq_tensor* t : {a, a_scale, w, w_scale, c})
+    if (!strides_ok(*t) || !is_contiguous(*t)) return FQ_ERR_PARAM_INVALID;
+  if (a->dtype != FQ_DT_INT4 || w->dtype != FQ_DT_INT4 || a->ndim != 2 || w->ndim != 2) return FQ_ERR_PARAM_INVALID;
+  const int64_t T = a->shape[0], H = a->shape[1], O = w->shape[0];
+  if (T < 1 || O < 1 || H < 128 || H % 128 != 0 || w->shape[1] != H) return FQ_ERR_PARAM_INVALID;
+  if (a_scale->dtype != FQ_DT_FLOAT32 || !shape_is(*a_scale, 1, T)) return FQ_ERR_PARAM_INVALID;
+  if (w_scale->dtype != FQ_DT_FLOAT32 || !shape_is(*w_scale, 1, O)) return FQ_ERR_PARAM_INVALID;
+  if ((c->dtype != FQ_DT_BFLOAT16 && c->dtype != FQ_DT_FLOAT32) || !shape_is(*c, 2, T, O)) return FQ_ERR_PARAM_INVALID;
+  // 32-bit buffer offsets, with a tile's worth of rows past the end
+  const int64_t lim = int64_t(1) << 31;
+  if ((T + 256) * (H / 2) >= lim || (O + 256) * (H / 2) >= lim || (T + 256) * 4 >= lim || (O + 256) * 4 >= lim)
+    return FQ_ERR_PARAM_INVALID;
+  auto al = [](const void* p, uintptr_t n) { return reinterpret_cast<uintptr_t>(p) % n == 0; };
+  if (!al(a->data, 16) || !al(w->data, 16) || !al(a_scale->data, 4) || !al(w_scale->data, 4) ||
+      !al(c->data, c->dtype == FQ_DT_FLOAT32 ? 4 : 2))
+    return FQ_ERR_PARAM_INVALID;
+  if (!device_is_gfx950()) return fail_runtime("the current device is not gfx950", hipSuccess);
+  const hipError_t err = fq::launch_int4_gemm(T, O, H, static_cast<const uint8_t*>(a->data),
+                                              static_cast<const float*>(a_scale->data),
+                                              static_cast<const uint8_t*>(w->data),
+                                              static_cast<const float*>(w_scale->data), c->data,
+                                              c->dtype == FQ_DT_FLOAT32, stream);
+  if (err != hipSuccess) return fail_runtime("int4 GEMM kernel launch", err);
+  return FQ_SUCCESS;
+}
+
 fq_status fq_mx_gemm(const fq_tensor* a, const fq_tensor* a_scale, const fq_tensor* w, const fq_tensor* w_scale,
                      const fq_tensor* c, hipStream_t stream) {
   g_last_error[0] = '\0';

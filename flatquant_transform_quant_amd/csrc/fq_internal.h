@@ -66,6 +66,10 @@ hipError_t launch_dequant(int32_t dtype, bool per_group, int64_t K, int64_t M, i
 hipError_t launch_dequant8(int32_t dtype, int32_t mode, int64_t K, int64_t M, int64_t N, const uint8_t* codes,
                            const float* scale, uint16_t* out, hipStream_t s);
 
+// int4 consumer GEMM over contiguous operands: C[T, O] = sa[t] sw[o] . A[T, H] . W[O, H]^T.
+hipError_t launch_int4_gemm(int64_t T, int64_t O, int64_t H, const uint8_t* a, const float* sa, const uint8_t* w,
+                            const float* sw, void* c, bool f32_out, hipStream_t s);
+
 // MXFP4 consumer GEMM over contiguous operands: C[T, O] = A[T, H] . W[O, H]^T (bf16 or fp32 C).
 hipError_t launch_mx_gemm(int64_t T, int64_t O, int64_t H, const uint8_t* a, const uint8_t* a_e8, const uint8_t* w,
                           const uint8_t* w_e8, void* c, bool f32_out, hipStream_t s);

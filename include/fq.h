@@ -166,6 +166,28 @@ fq_status fq_run(void* workspace, uint64_t workspaceSize, fq_executor* executor,
  * call); not a gfx950 device, or a launch failure -> FQ_ERR_RUNTIME. */
 fq_status fq_dequant(const fq_tensor* codes, const fq_tensor* scale, const fq_tensor* out, hipStream_t stream);
 
+/* ---- int4 consumer GEMM ------------------------------------------------------------
+ * The product that follows the per-token int4 quantizer in a FlatQuant linear layer:
+ *     C[t, o] = fl32( fl32(acc[t, o]) * fl32(a_scale[t] * w_scale[o]) ),
+ *     acc[t, o] = sum_h qa[t, h] * qw[o, h]   (exact: int32 accumulation, |acc| <= 64 H)
+ * with qa the int4 codes fq_run writes per token ([FQV2] 第3步 pertoken; its INT32 and INT4
+ * outputs are the same bytes, so out viewed as INT4 [K, M*N] is a with T = K, H = M*N) and its
+ * FLOAT32 [K] quantScale as a_scale; W int4 weights with one fp32 scale per output channel.
+ * The symmetric integer format dequantizes as q * scale (the APT-LLM page, section 2.1).
+ *   a        INT4    [T, H]     two's complement, 2 codes per byte, low nibble first; H % 128 == 0
+ *   a_scale  FLOAT32 [T]
+ *   w        INT4    [O, H]
+ *   w_scale  FLOAT32 [O]
+ *   c        BFLOAT16 | FLOAT32 [T, O]   (a bf16 C is the fp32 value rounded to nearest even)
+ * All tensors contiguous device memory owned by the caller; a and w 16-byte aligned, the
+ * scales 4-byte aligned; (T + 256) * H / 2 and (O + 256) * H / 2 below 2^31.  Enqueued on
+ * `stream` without synchronizing; no workspace.  Errors: a NULL tensor or data pointer ->
+ * FQ_ERR_PARAM_NULLPTR; any shape, dtype, stride, size or alignment mismatch ->
+ * FQ_ERR_PARAM_INVALID (no HIP call is made before these checks); not a gfx950 device, or a
+ * launch failure -> FQ_ERR_RUNTIME. */
+fq_status fq_int4_gemm(const fq_tensor* a, const fq_tensor* a_scale, const fq_tensor* w, const fq_tensor* w_scale,
+                       const fq_tensor* c, hipStream_t stream);
+
 /* ---- MXFP4 consumer GEMM ----------------------------------------------------------------
  * The product that follows the quantizer in a FlatQuant linear layer:
  *     C[t, o] = sum_h value(a[t, h]) * value(w[o, h])

@@ -466,3 +466,30 @@ def test_dequant_8bit_codes_arguments(mode):
     assert fq.fq_dequant(tens(dt, (4, 16, 16)), tens(fq.DT_FLOAT32, (3,)), o, 0) == INVAL
     assert fq.fq_dequant(tens(dt, (4, 16, 16), (512, 32, 1)), s, o, 0) == INVAL  # contiguous only
     assert fq.fq_dequant(None, s, o, 0) == NULLP
+
+
+# ---------------------------------------------------------------- fq_int4_gemm arguments
+
+def i4_args(T=32, O=16, H=256, cdt=fq.DT_BFLOAT16):
+    return (tens(fq.DT_INT4, (T, H)), tens(fq.DT_FLOAT32, (T,)), tens(fq.DT_INT4, (O, H)),
+            tens(fq.DT_FLOAT32, (O,)), tens(cdt, (T, O)))
+
+
+def test_int4_gemm_arguments():
+    """Rejected before any HIP call: NULLs, H not a multiple of 128, mismatched H, wrong
+    scale shapes or dtypes, a C of another shape or dtype, e2m1 codes, strided operands."""
+    a, sa, w, sw, c = i4_args()
+    assert fq.fq_int4_gemm(None, sa, w, sw, c, 0) == NULLP
+    assert fq.fq_int4_gemm(a, sa, w, sw, tens(fq.DT_BFLOAT16, (32, 16), data=0), 0) == NULLP
+    bad = [
+        (tens(fq.DT_INT4, (32, 192)), sa, tens(fq.DT_INT4, (16, 192)), sw, c),        # H % 128
+        (a, sa, tens(fq.DT_INT4, (16, 384)), sw, c),                                   # H differs
+        (a, tens(fq.DT_FLOAT32, (31,)), w, sw, c),                                     # scale count
+        (a, sa, w, tens(fq.DT_FLOAT8_E8M0, (16,)), c),                                 # scale dtype
+        (a, sa, w, sw, tens(fq.DT_FLOAT16, (32, 16))),                                 # C dtype
+        (a, sa, w, sw, tens(fq.DT_BFLOAT16, (16, 32))),                                # C shape
+        (tens(fq.DT_FLOAT4_E2M1, (32, 256)), sa, w, sw, c),                            # codes dtype
+        (tens(fq.DT_INT4, (32, 256), (512, 1)), sa, w, sw, c),                         # strided
+    ]
+    for args in bad:
+        assert fq.fq_int4_gemm(*args, 0) == INVAL
