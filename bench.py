@@ -26,6 +26,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16/fp16 MFMA, TFLOP/s
 MFMA_FP4_PEAK_TFS = 10100.0    # MI355X dense fp4 MFMA, TFLOP/s
+MFMA_INT8_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA, TOP/s
 
 
 def algorithmic_bytes(w, K=None) -> int:
@@ -152,7 +153,7 @@ def main() -> int:
     ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 generic, 2 mfma-small, 3 mfma-wide")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
-    ap.add_argument("--op", default="quantize", choices=["quantize", "dequant", "mxgemm"],
+    ap.add_argument("--op", default="quantize", choices=["quantize", "dequant", "mxgemm", "i4gemm"],
                     help="quantize (the fused operator, default), dequant (codes + scales -> values) or "
                          "mxgemm (the MXFP4 GEMM consuming a per-group workload's output)")
     ap.add_argument("--gemm-out", type=int, default=8192, help="mxgemm: output features O")
@@ -181,6 +182,8 @@ def main() -> int:
         return bench_dequant(args, w, x_host, p1, p2, to_dev, dev, tdt)
     if args.op == "mxgemm":
         return bench_mx_gemm(args, w, x_host, p1, p2, to_dev, dev)
+    if args.op == "i4gemm":
+        return bench_int4_gemm(args, w, x_host, p1, p2, to_dev, dev)
     # rotate input/output sets so one lap touches > 2x the 256 MB last-level cache
     per_set = algorithmic_bytes(w)
     nsets = int(max(1, min(8, -(-(600 * 2 ** 20) // per_set))))
@@ -406,6 +409,80 @@ def bench_mx_gemm(args, w, x_host, p1, p2, to_dev, dev):
         "dtype": "fp4",
         "data": "synthetic",
         "config": {"workload": w.name, "op": "mxgemm", "T": T, "H": H, "O": O, "c": "bf16", "parallelism": "none"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def bench_int4_gemm(args, w, x_host, p1, p2, to_dev, dev):
+    """Times fq_int4_gemm with A = the workload's per-token int4 quantizer output (T = K
+    tokens, H = M*N) and its scales, and synthetic int4 weights W [O, H] with per-channel fp32
+    scales (seeded)."""
+    import numpy as np
+    import torch
+
+    import flatquant_transform_quant_amd as fq
+
+    if w.mode not in ("int32", "int4"):
+        print("--op i4gemm needs a per-token int4 workload", file=sys.stderr)
+        return 2
+    T, H, O = w.K, w.M * w.N, args.gemm_out
+    x = to_dev(x_host)
+    a, a_sc = fq.empty_outputs(T, w.M, w.N, "int4", dev)
+    fq.quantize(x, to_dev(p1), to_dev(p2), a, a_sc, "int4", w.clip_ratio, w.dst_type_max)
+    del x
+    a = a.reshape(T, H // 2)
+    rng = np.random.default_rng(1235)
+    wc = torch.from_numpy(rng.integers(0, 256, (O, H // 2), dtype=np.uint8)).to(dev)
+    ws = torch.from_numpy(np.abs(rng.standard_normal(O)).astype(np.float32) * np.float32(0.01)).to(dev)
+    c = torch.empty((T, O), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.Stream(dev)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        fq.int4_gemm(a, a_sc, wc, ws, H, out=c, stream=stream)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        fq.int4_gemm(a, a_sc, wc, ws, H, out=c, stream=stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms = total_ms / args.steps
+    ops = 2 * T * O * H
+    tops = ops / (ms / 1e3) / 1e12
+    bytes_ = T * H // 2 + O * H // 2 + 4 * (T + O) + 2 * T * O
+    roof = {"bound": "mfma", "achieved": round(tops, 1), "peak": MFMA_INT8_PEAK_TOPS, "unit": "TOP/s",
+            "frac": round(tops / MFMA_INT8_PEAK_TOPS, 4), "traffic": None, "kernel": "int4_gemm_kernel",
+            "avg_launch_us": round(ms * 1e3, 3), "algorithmic_ops": ops, "algorithmic_bytes": bytes_,
+            "other_frac": round(bytes_ / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+
+        rows = 4
+        t = time.perf_counter()
+        oracle.int4_gemm(a[:rows].cpu().numpy(), a_sc[:rows].cpu().numpy(), wc.cpu().numpy(), ws.cpu().numpy(), H)
+        dt = time.perf_counter() - t
+        cpu = {"value": 2 * rows * O * H / dt / 1e12, "unit": "TOP/s", "cores": 1, "kind": "oracle",
+               "sample": f"{rows} of {T} rows of C ({rows * O} outputs, H = {H}), {dt:.2f} s wall on 1 thread"}
+    line = {
+        "metric": "TOP/s of the int4 GEMM consuming the quantizer output + % of the int8 MFMA roofline, 1 MI355X",
+        "value": round(tops, 1),
+        "unit": "TOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4",
+        "data": "synthetic",
+        "config": {"workload": w.name, "op": "i4gemm", "T": T, "H": H, "O": O, "c": "bf16", "parallelism": "none"},
         "roofline": roof,
         "cpu_baseline": cpu,
     }
