@@ -52,14 +52,15 @@ __global__ __launch_bounds__(kGenericThreads) void generic_kernel(Problem pb, Bu
   const int M = static_cast<int>(pb.M), N = static_cast<int>(pb.N), MN = M * N;
   const int tid = threadIdx.x;
   for (int64_t k = blockIdx.x; k < pb.K; k += gridDim.x) {
-    const uint16_t* xk = b.x + k * MN;
+    const uint16_t* xk = b.x + k * pb.xs_k;  // row m of the slice at xk + m * xs_m
+    const int64_t xs_m = pb.xs_m;
     // [FQV2] 第1步: T = x_k . P2, rounded to the dtype; skipped for an empty P2.
     for (int e = tid; e < MN; e += kGenericThreads) {
       if (pb.two_sided) {
         const int m = e / N, n = e % N;
         double acc = 0.0;
         for (int j = 0; j < N; ++j)
-          acc = __builtin_fma(static_cast<double>(load16<DT>(xk[m * N + j])),
+          acc = __builtin_fma(static_cast<double>(load16<DT>(xk[m * xs_m + j])),
                               static_cast<double>(load16<DT>(b.p2[j * N + n])), acc);
         // T is the fp32 value rounded to the dtype: two roundings.  The register barrier
         // keeps the compiler from merging them into one fp64 -> dtype rounding, which
@@ -68,7 +69,7 @@ __global__ __launch_bounds__(kGenericThreads) void generic_kernel(Problem pb, Bu
         asm volatile("" : "+v"(t32));
         Ts[e] = round16<DT>(t32);
       } else {
-        Ts[e] = xk[e];
+        Ts[e] = xk[(e / N) * xs_m + e % N];
       }
     }
     __syncthreads();

@@ -36,6 +36,7 @@ struct fq_executor {
   int32_t repeatable;
   fq_tensor x, p1, p2, out, scale;
   bool stage_x, stage_p1, stage_p2, stage_out, stage_scale;
+  bool x_direct;  // a non-contiguous x read in place through its strides (no gather)
   uint64_t off_x, off_p1, off_p2, off_out, off_scale, ws_size;
 };
 
@@ -123,7 +124,7 @@ bool kernel_supports(int32_t k, const fq_executor* e) {
   switch (k) {
     case fq::kGeneric: return true;
     case fq::kMfmaSmall: return vector_aligned(e) && fq::mfma_small_supports(e->pb);
-    case fq::kMfmaWide: return vector_aligned(e) && fq::mfma_wide_supports(e->pb);
+    case fq::kMfmaWide: return !e->x_direct && vector_aligned(e) && fq::mfma_wide_supports(e->pb);
     default: return false;
   }
 }
@@ -236,6 +237,9 @@ fq_status fq_get_workspace_size(const fq_tensor* x, const fq_tensor* kroneckerP1
   e->out = *out;
   e->scale = *quantScale;
   e->stage_x = !is_contiguous(*x);
+  e->x_direct = false;
+  e->pb.xs_k = MN;
+  e->pb.xs_m = N;
   e->stage_p1 = !is_contiguous(*kroneckerP1);
   e->stage_p2 = !p2_empty && !is_contiguous(*kroneckerP2);
   e->stage_out = !is_contiguous(*out);
@@ -247,6 +251,21 @@ fq_status fq_get_workspace_size(const fq_tensor* x, const fq_tensor* kroneckerP1
     off = align256(off + bytes);
     return at;
   };
+  if (e->stage_x) {
+    // Strided-input fast path: with a unit innermost stride and slice / row strides of whole
+    // 16-byte units the generic and one-wave-per-slice kernels read x in place (no gather
+    // into the workspace); the 256-class kernels keep the gather.
+    const int64_t sk = x->strides[0], sm = x->strides[1], sn = x->strides[2];
+    const bool ok = (sn == 1 || N == 1) && (sk % 8 == 0 || K == 1) && (sm % 8 == 0 || M == 1) &&
+                    reinterpret_cast<uintptr_t>(x->data) % 16 == 0 && (M - 1) * sm + N < (int64_t(1) << 30) &&
+                    (K - 1) * sk + (M - 1) * sm + N < (int64_t(1) << 62);
+    if (ok && auto_kernel(e) != fq::kMfmaWide) {
+      e->stage_x = false;
+      e->x_direct = true;
+      e->pb.xs_k = K == 1 ? MN : sk;
+      e->pb.xs_m = M == 1 ? N : sm;
+    }
+  }
   e->off_x = take(e->stage_x, uint64_t(K * MN) * 2);
   e->off_p1 = take(e->stage_p1, uint64_t(M * M) * 2);
   e->off_p2 = take(e->stage_p2, uint64_t(N * N) * 2);

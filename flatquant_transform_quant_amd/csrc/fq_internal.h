@@ -29,6 +29,9 @@ struct Problem {
   float d;            // fl32(max_val / clipRatio), the per-token divisor (max_val 7, 127, 448, 57344)
   float dmax;         // fl32(dstTypeMax); 0 selects V1
   float dmax_inv;     // 1/dmax when dmax is a power of two (then exact), else 0
+  int64_t xs_k, xs_m; // x's slice and row strides in elements (M*N and N when contiguous);
+                      // the innermost stride is 1; only the generic and small kernels take
+                      // other values (x read in place)
 };
 
 // Device buffers of one launch, in the packed contiguous layouts:

@@ -94,18 +94,21 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()), (small_waves<M, N, 
   // buffer cover that buffer's loads only and not the ones issued after them.
   constexpr int PF = prefetch_depth<M, N, PG>();
   u32x4_t xa[PF][MT][KS1];
+  // x's slice and row strides (M*N and N for a contiguous x; a strided x is read in place)
+  const int64_t xs_k = pb.xs_k;
+  const int xs_m = static_cast<int>(pb.xs_m);
+  const int x_span = ((M - 1) * xs_m + N) * 2;  // bytes a slice spans
   auto load_x = [&](int buf, int64_t slice) {
     const bool in = slice < pb.K;
-    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(b.x + (in ? slice : 0) * MN),
-                                                        static_cast<int16_t>(0), in ? MN * 2 : 0,
-                                                        kBufferWord3);
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(b.x + (in ? slice : 0) * xs_k),
+                                                        static_cast<int16_t>(0), in ? x_span : 0, kBufferWord3);
     // row tile in the scalar offset, k-step in the immediate: one address register
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int ks = 0; ks < KS1; ++ks)
-        xa[buf][mt][ks] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (c * N + 32 * ks + 8 * g) * 2,
-                                                                16 * mt * N * 2, 0);
+        xa[buf][mt][ks] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (c * xs_m + 32 * ks + 8 * g) * 2,
+                                                                16 * mt * xs_m * 2, 0);
   };
   // ---- stage P2 / P1 fragments (once per workgroup) ----
   // The P loads go first and the x loads of the first slices right after them, so the

@@ -203,10 +203,22 @@ def test_dst_type_max_values(dmax, ok):
 
 
 def test_strided_inputs_get_a_workspace():
+    # x with a unit innermost stride and 16-byte slice / row strides is read in place
     p = problem()
     p["x"] = tens(fq.DT_BFLOAT16, (4, 16, 16), (16, 64 * 16, 1))  # K and M axes swapped
+    assert plan(p) == (OK, 0)
+    p["x"] = tens(fq.DT_BFLOAT16, (4, 16, 16), (16 * 24, 24, 1))  # padded rows
+    assert plan(p) == (OK, 0)
+    # otherwise it is gathered into the workspace
+    for strides in [(512, 32, 2), (16 * 17, 17, 1), (16 * 16 + 4, 16, 1)]:
+        p["x"] = tens(fq.DT_BFLOAT16, (4, 16, 16), strides)
+        st, ws = plan(p)
+        assert st == OK and ws >= 4 * 16 * 16 * 2, strides
+    # the 256-class kernel always reads a gathered x
+    p = problem(K=2, M=256, N=256, mode="int4")
+    p["x"] = tens(fq.DT_BFLOAT16, (2, 256, 256), (256 * 264, 264, 1))
     st, ws = plan(p)
-    assert st == OK and ws >= 4 * 16 * 16 * 2
+    assert st == OK and ws >= 2 * 256 * 256 * 2
     p = problem()
     p["p2"] = tens(fq.DT_BFLOAT16, (16, 16), (1, 16))  # transposed view
     st, ws = plan(p)
@@ -237,7 +249,7 @@ def test_run_argument_checks_without_device():
     assert fq.fq_run(0, 0, 0, 0) == NULLP  # NULL executor
     # a strided problem needs its workspace
     p2 = problem()
-    p2["x"] = tens(fq.DT_BFLOAT16, (4, 16, 16), (16, 64 * 16, 1))
+    p2["x"] = tens(fq.DT_BFLOAT16, (4, 16, 16), (512, 32, 2))
     st, ws2, ex2 = fq.fq_get_workspace_size(p2["x"], p2["p1"], p2["p2"], 1.0, 0.0, p2["out"], p2["sc"])
     assert st == OK and ws2 > 0
     assert fq.fq_executor_set_repeatable(ex2, True) == OK

@@ -225,3 +225,33 @@ def test_v1_form_runs_like_v2_with_dst_type_max_zero(key):
     torch.cuda.synchronize()
     got = fetch(out, sc, w.mode, K)
     assert np.array_equal(ref[0], got[0]) and np.array_equal(ref[1], got[1])
+
+
+@pytest.mark.parametrize("M,N,mode", [(64, 64, "int4"), (33, 40, "int32"), (64, 128, "fp4"), (256, 256, "int4"),
+                                      (64, 64, "e4m3")])
+def test_strided_x_in_place_or_gathered(M, N, mode):
+    """x as a view with padded rows and padded slices (read in place by the generic and
+    one-wave-per-slice kernels, gathered for the 256-class kernel), and with a non-unit
+    innermost stride (always gathered): the codes and scales equal those of a contiguous x."""
+    dt = "bf16"
+    K = 9
+    x, p1, p2 = _inputs(M, N, dt, K, seed=M * 7 + N)
+    if mode == "int32" and N % 8:
+        pytest.skip("INT32 needs N % 8 == 0")
+    xd, p1d, p2d = to_dev(x, dt), to_dev(p1, dt), to_dev(p2, dt)
+    ref = fetch(*run_lib(xd, p1d, p2d, mode, 0.9, 0.0), mode, K)
+    big = torch.zeros((K + 1, M + 3, N + 8), dtype=xd.dtype, device=DEV)
+    big[:K, :M, :N] = xd
+    views = {"padded": big[:K, :M, :N],
+             "innermost stride 2": torch.zeros((K, M, 2 * N), dtype=xd.dtype, device=DEV)}
+    views["innermost stride 2"][:, :, 0::2] = xd
+    views["innermost stride 2"] = views["innermost stride 2"][:, :, 0::2]
+    for name, xv in views.items():
+        assert not xv.is_contiguous()
+        out, sc = fq.empty_outputs(K, M, N, mode, DEV)
+        ex = fq.Executor(xv, p1d, p2d, out, sc, mode, 0.9, 0.0, repeatable=False)
+        say(f"[gpu] strided x ({name}) {M}x{N} {mode}: kernel {ex.kernel}, workspace {ex.workspace_size}")
+        ex.run()
+        torch.cuda.synchronize()
+        got = fetch(out, sc, mode, K)
+        assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1]), name
