@@ -79,7 +79,9 @@ typedef int32_t fq_status;
  * elements).  Inputs may have any non-negative strides.  Outputs may be strided too,
  * but the innermost dimension of INT4 / FLOAT4_E2M1 must have stride 1 and their other
  * strides must be even (whole bytes).  Non-contiguous tensors are staged through the
- * workspace.  The caller owns all tensor memory; it must stay valid until the work
+ * workspace, except an x whose innermost stride is 1 and whose other strides are multiples
+ * of 8 elements (16-byte aligned data): the generic and one-wave-per-slice kernels read such
+ * an x in place.  The caller owns all tensor memory; it must stay valid until the work
  * enqueued by fq_run has completed on the stream. */
 typedef enum {
   FQ_DT_FLOAT16 = 1,
