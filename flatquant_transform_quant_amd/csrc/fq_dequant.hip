@@ -82,7 +82,7 @@ __global__ __launch_bounds__(kDqThreads) void dequant32_kernel(const uint8_t* __
 #pragma unroll
     for (int p = 0; p < 4; ++p)
       o[p] = round16x2<DT>(dq_value<PG>((c >> (8 * p)) & 15u, sc, e8), dq_value<PG>((c >> (8 * p + 4)) & 15u, sc, e8));
-    reinterpret_cast<u32x4_t*>(out)[r] = o;
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(out) + r);  // written once
   }
 }
 
@@ -140,8 +140,9 @@ __global__ __launch_bounds__(kDqThreads) void dequant8_kernel(const uint8_t* __r
     const float sc = scale[r / runs_per_slice];
     const float2 q0 = q8x2<MODE, false>(c[0]), q1 = q8x2<MODE, true>(c[0]);
     const float2 q2 = q8x2<MODE, false>(c[1]), q3 = q8x2<MODE, true>(c[1]);
-    reinterpret_cast<u32x4_t*>(out)[r] = u32x4_t{round16x2<DT>(q0.x * sc, q0.y * sc), round16x2<DT>(q1.x * sc, q1.y * sc),
-                                                 round16x2<DT>(q2.x * sc, q2.y * sc), round16x2<DT>(q3.x * sc, q3.y * sc)};
+    __builtin_nontemporal_store(u32x4_t{round16x2<DT>(q0.x * sc, q0.y * sc), round16x2<DT>(q1.x * sc, q1.y * sc),
+                                        round16x2<DT>(q2.x * sc, q2.y * sc), round16x2<DT>(q3.x * sc, q3.y * sc)},
+                                reinterpret_cast<u32x4_t*>(out) + r);  // written once
   }
 }
 

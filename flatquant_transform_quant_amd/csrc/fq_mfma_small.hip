@@ -147,16 +147,17 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()), (small_waves<M, N, 
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     u32x4_t* gcodes = reinterpret_cast<u32x4_t*>(b.codes + slice * CODE_BYTES);
 #pragma unroll
-    for (int q = 0; q < CODE_BYTES / 16 / 64; ++q) gcodes[q * 64 + lane] = stage[wave][q * 64 + lane];
+    // the codes are written once and not read back by this kernel: non-temporal stores
+    for (int q = 0; q < CODE_BYTES / 16 / 64; ++q) __builtin_nontemporal_store(stage[wave][q * 64 + lane], &gcodes[q * 64 + lane]);
     if constexpr ((CODE_BYTES / 16) % 64 != 0) {
       constexpr int q = CODE_BYTES / 16 / 64;
-      if (q * 64 + lane < CODE_BYTES / 16) gcodes[q * 64 + lane] = stage[wave][q * 64 + lane];
+      if (q * 64 + lane < CODE_BYTES / 16) __builtin_nontemporal_store(stage[wave][q * 64 + lane], &gcodes[q * 64 + lane]);
     }
     if constexpr (PG) {
       const uint32_t* se = reinterpret_cast<const uint32_t*>(st + CODE_BYTES);
       uint32_t* ge = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(b.scale) +
                                                  slice * e8m0_bytes_per_slice(MN));
-      for (int q = lane; q < E8_BYTES / 4; q += 64) ge[q] = se[q];
+      for (int q = lane; q < E8_BYTES / 4; q += 64) __builtin_nontemporal_store(se[q], &ge[q]);
     }
     // the staging buffer is reused by the next slice
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

@@ -31,6 +31,8 @@ constexpr int kW = 256;       // M = N
 constexpr int kChunk = 32;    // rows of x per chunk
 constexpr int kNChunk = kW / kChunk;
 constexpr int kIT = kW / 16;  // 16-row tiles of y
+// cache policy of the code stores: non-temporal (written once, not read back here)
+constexpr int kStoreNT = 2;
 
 // CLAMP (per token): the int4 clamp is compiled in.  SV (per group): the e8m0 rule.  Q (per
 // token): 0 for int4 codes, else the 8-bit mode (kPerTokenInt8 / E4M3 / E5M2), one byte a code.
@@ -277,7 +279,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb,
             const int r0 = 16 * it + i;  // row - 4g
             const uint32_t v = code8x2<Q>(y[it][0][i] * inv, y[it][1][i] * inv) |
                                (code8x2<Q>(y[it][2][i] * inv, y[it][3][i] * inv) << 16);
-            __builtin_amdgcn_raw_buffer_store_b32(v, rs_codes, code_off, r0 * kW, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(v, rs_codes, code_off, r0 * kW, kStoreNT);
             if (i == 3) __builtin_amdgcn_sched_barrier(0);
           }
       } else {
@@ -289,7 +291,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb,
           const uint32_t b0 = pair_byte(int4_biased<CLAMP>(y[it][0][i], inv), int4_biased<CLAMP>(y[it][1][i], inv));
           const uint32_t b1 = pair_byte(int4_biased<CLAMP>(y[it][2][i], inv), int4_biased<CLAMP>(y[it][3][i], inv));
           __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(unbias(__builtin_amdgcn_perm(b1, b0, 0x0C0C0400u))),
-                                                rs_codes, code_off, r0 * (kW / 2), 0);
+                                                rs_codes, code_off, r0 * (kW / 2), kStoreNT);
           if (i == 3) __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -312,7 +314,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb,
           const float sc = e8m0_to_float(code);
           uint32_t packed = fp4x2<0>(0u, y[it][0][i], y[it][1][i], sc);
           packed = fp4x2<1>(packed, y[it][2][i], y[it][3][i], sc);
-          __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(packed), rs_codes, code_off, r0 * (kW / 2), 0);
+          __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(packed), rs_codes, code_off, r0 * (kW / 2), kStoreNT);
           // the 8 lanes of a group hold the same code and all store it (no branch)
           __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(code), rs_e8, e8_off, r0 * (kW / 32), 0);
         }
@@ -488,7 +490,7 @@ __global__ __launch_bounds__(kLeftThreads, 1) void mfma_wide1_kernel(Problem pb,
         packed = fp4x2<1>(packed, y[it][2][i], y[it][3][i], scf);
         packed = fp4x2<2>(packed, y[it][4][i], y[it][5][i], scf);
         packed = fp4x2<3>(packed, y[it][6][i], y[it][7][i], scf);
-        __builtin_amdgcn_raw_buffer_store_b32(packed, rs_codes, code_off, r0 * (kW / 2), 0);
+        __builtin_amdgcn_raw_buffer_store_b32(packed, rs_codes, code_off, r0 * (kW / 2), kStoreNT);
       }
       // lane (k, j) takes row 4g + j's code of group k, places it at byte k, and ORs in
       // the other three quads' bytes (rotations by 4, 8, 12 lanes reach all of them)
