@@ -62,15 +62,23 @@ def algorithmic_flops(w, K=None) -> int:
     return K * f
 
 
-def kernel_source_hash() -> str:
-    """Hash of the device code (the HIP sources and the headers they include, not the host
-    code); the profile summaries record it beside their counters."""
+# the source file of each profiled kernel
+KERNEL_SOURCES = {"generic": "fq_generic.hip", "mfma_small": "fq_mfma_small.hip", "mfma_wide1": "fq_mfma_wide.hip",
+                  "mfma_wide2": "fq_mfma_wide.hip", "dequant": "fq_dequant.hip"}
+
+
+def kernel_source_hash(kernel: str | None = None) -> str:
+    """Hash of a kernel's device code: its HIP source and every device header (not the host
+    code); all HIP sources when no kernel is named.  The profile summaries record it beside
+    their counters."""
     import glob
     import hashlib
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "flatquant_transform_quant_amd", "csrc")
-    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
+    hips = ([os.path.join(csrc, KERNEL_SOURCES[kernel])] if kernel in KERNEL_SOURCES
+            else glob.glob(os.path.join(csrc, "*.hip")))
+    for f in sorted(hips + glob.glob(os.path.join(csrc, "*.h"))):
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:
             h.update(fh.read())
@@ -90,7 +98,7 @@ def profiled_traffic(w, op="quantize"):
             for line in fh:
                 if line.startswith("machine-readable:"):
                     info = json.loads(line.split(":", 1)[1])
-                    if info.get("source_hash") == kernel_source_hash():
+                    if info.get("source_hash") == kernel_source_hash(info.get("kernel")):
                         return info.get("traffic_bytes_per_dispatch")
     return None
 

@@ -31,7 +31,10 @@ constexpr int kW = 256;       // M = N
 constexpr int kChunk = 32;    // rows of x per chunk
 constexpr int kNChunk = kW / kChunk;
 constexpr int kIT = kW / 16;  // 16-row tiles of y
-// cache policy of the code stores: non-temporal (written once, not read back here)
+// cache policy of the two-sided kernel's per-token code stores: non-temporal (written once, not
+// read back here).  The per-group code stores leave short runs per group of lanes, which
+// non-temporal stores turn into partial-line writes (17% more HBM writes measured on the
+// left-only kernel), so those stay cached.
 constexpr int kStoreNT = 2;
 
 // CLAMP (per token): the int4 clamp is compiled in.  SV (per group): the e8m0 rule.  Q (per
@@ -314,7 +317,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb,
           const float sc = e8m0_to_float(code);
           uint32_t packed = fp4x2<0>(0u, y[it][0][i], y[it][1][i], sc);
           packed = fp4x2<1>(packed, y[it][2][i], y[it][3][i], sc);
-          __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(packed), rs_codes, code_off, r0 * (kW / 2), kStoreNT);
+          __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(packed), rs_codes, code_off, r0 * (kW / 2), 0);
           // the 8 lanes of a group hold the same code and all store it (no branch)
           __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(code), rs_e8, e8_off, r0 * (kW / 32), 0);
         }
@@ -490,7 +493,7 @@ __global__ __launch_bounds__(kLeftThreads, 1) void mfma_wide1_kernel(Problem pb,
         packed = fp4x2<1>(packed, y[it][2][i], y[it][3][i], scf);
         packed = fp4x2<2>(packed, y[it][4][i], y[it][5][i], scf);
         packed = fp4x2<3>(packed, y[it][6][i], y[it][7][i], scf);
-        __builtin_amdgcn_raw_buffer_store_b32(packed, rs_codes, code_off, r0 * (kW / 2), kStoreNT);
+        __builtin_amdgcn_raw_buffer_store_b32(packed, rs_codes, code_off, r0 * (kW / 2), 0);  // cached: 32-byte runs
       }
       // lane (k, j) takes row 4g + j's code of group k, places it at byte k, and ORs in
       // the other three quads' bytes (rotations by 4, 8, 12 lanes reach all of them)
