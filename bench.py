@@ -78,6 +78,7 @@ def kernel_source_hash(kernel: str | None = None) -> str:
     csrc = os.path.join(ROOT, "flatquant_transform_quant_amd", "csrc")
     hips = ([os.path.join(csrc, KERNEL_SOURCES[kernel])] if kernel in KERNEL_SOURCES
             else glob.glob(os.path.join(csrc, "*.hip")))
+    hips = [f for f in hips if os.path.exists(f)]  # no sources beside the library: no match
     for f in sorted(hips + glob.glob(os.path.join(csrc, "*.h"))):
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:
