@@ -743,3 +743,20 @@ def test_int4_gemm_scales_apply_as_one_fp32_factor():
     c = oracle.int4_gemm(a, sa, w, sw, H)
     want = acc.astype(np.float32) * (sa[:, None] * sw[None, :])
     assert np.array_equal(c, want)
+
+
+@pytest.mark.parametrize("mode", ["int8", "e4m3", "e5m2"])
+def test_worked_8bit_examples(mode):
+    """The hand-worked codes of tests/golden/worked_8bit.txt (scale exactly 1)."""
+    k = keyed("worked_8bit.txt")
+    M, N = (int(v) for v in k[f"{mode}_shape"])
+    xv = np.array([float(v) for v in k[f"{mode}_x"]])
+    x = bf16(xv).reshape(1, M, N)
+    assert np.array_equal(oracle.dt_to_float(x, "bf16").reshape(-1), xv)  # exact in bf16
+    r = oracle.run(x, bf16(np.eye(M)), bf16(np.eye(N)), "bf16", mode, 1.0)
+    assert r["scale"][0] == 1.0
+    if mode == "int8":
+        want = np.array([int(v) for v in k["int8_codes"]]).astype(np.int8).view(np.uint8)
+    else:
+        want = np.array([int(v, 16) for v in k[f"{mode}_codes"]], np.uint8)
+    assert r["packed"][0].tolist() == want.tolist()
