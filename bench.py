@@ -64,7 +64,8 @@ def algorithmic_flops(w, K=None) -> int:
 
 # the source file of each profiled kernel
 KERNEL_SOURCES = {"generic": "fq_generic.hip", "mfma_small": "fq_mfma_small.hip", "mfma_wide1": "fq_mfma_wide.hip",
-                  "mfma_wide2": "fq_mfma_wide.hip", "dequant": "fq_dequant.hip"}
+                  "mfma_wide2": "fq_mfma_wide.hip", "dequant": "fq_dequant.hip", "mx_gemm_kernel": "fq_mx_gemm.hip",
+                  "int4_gemm_kernel": "fq_int4_gemm.hip"}
 
 
 def kernel_source_hash(kernel: str | None = None) -> str:
@@ -100,6 +101,21 @@ def profiled_traffic(w, op="quantize"):
                 if line.startswith("machine-readable:"):
                     info = json.loads(line.split(":", 1)[1])
                     if info.get("source_hash") == kernel_source_hash(info.get("kernel")):
+                        return info.get("traffic_bytes_per_dispatch")
+    return None
+
+
+def profiled_gemm_traffic(kernel: str, product: str):
+    """Bytes beyond L2 per launch of a GEMM (2 x FETCH_SIZE + WRITE_SIZE) from its committed
+    profile summary for this T x O x H product, or None (no summary, or the kernel changed)."""
+    import glob
+
+    for f in glob.glob(os.path.join(ROOT, "profiles", f"{kernel.replace('_kernel', '')}_*.md")):
+        with open(f, encoding="utf-8") as fh:
+            for line in fh:
+                if line.startswith("machine-readable:"):
+                    info = json.loads(line.split(":", 1)[1])
+                    if info.get("product") == product and info.get("source_hash") == kernel_source_hash(kernel):
                         return info.get("traffic_bytes_per_dispatch")
     return None
 
@@ -389,7 +405,8 @@ def bench_mx_gemm(args, w, x_host, p1, p2, to_dev, dev):
     tfs = flops / (ms / 1e3) / 1e12
     bytes_ = T * H // 2 + O * H // 2 + (T + O) * 2 * (-(-H // 64)) + 2 * T * O
     roof = {"bound": "mfma", "achieved": round(tfs, 1), "peak": MFMA_FP4_PEAK_TFS, "unit": "TFLOP/s",
-            "frac": round(tfs / MFMA_FP4_PEAK_TFS, 4), "traffic": None, "kernel": "mx_gemm_kernel",
+            "frac": round(tfs / MFMA_FP4_PEAK_TFS, 4), "traffic": profiled_gemm_traffic("mx_gemm_kernel", f"{T}x{O}x{H}"),
+            "kernel": "mx_gemm_kernel",
             "avg_launch_us": round(ms * 1e3, 3), "algorithmic_flops": flops, "algorithmic_bytes": bytes_,
             "other_frac": round(bytes_ / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
     cpu = None
@@ -465,7 +482,8 @@ def bench_int4_gemm(args, w, x_host, p1, p2, to_dev, dev):
     tops = ops / (ms / 1e3) / 1e12
     bytes_ = T * H // 2 + O * H // 2 + 4 * (T + O) + 2 * T * O
     roof = {"bound": "mfma", "achieved": round(tops, 1), "peak": MFMA_INT8_PEAK_TOPS, "unit": "TOP/s",
-            "frac": round(tops / MFMA_INT8_PEAK_TOPS, 4), "traffic": None, "kernel": "int4_gemm_kernel",
+            "frac": round(tops / MFMA_INT8_PEAK_TOPS, 4),
+            "traffic": profiled_gemm_traffic("int4_gemm_kernel", f"{T}x{O}x{H}"), "kernel": "int4_gemm_kernel",
             "avg_launch_us": round(ms * 1e3, 3), "algorithmic_ops": ops, "algorithmic_bytes": bytes_,
             "other_frac": round(bytes_ / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
     cpu = None
