@@ -56,6 +56,20 @@ __device__ __forceinline__ void widen(const u32x4_t raw, i32x4_t& lo, i32x4_t& h
   hi = i32x4_t{static_cast<int>(v[4]), static_cast<int>(v[5]), static_cast<int>(v[6]), static_cast<int>(v[7])};
 }
 
+// 32 int4 codes -> two operands of their values plus 8 (0 .. 15: the nibble with bit 3 flipped,
+// no sign extension), in the byte order of widen().
+__device__ __forceinline__ void widen_biased(const u32x4_t raw, i32x4_t& lo, i32x4_t& hi) {
+  uint32_t v[8];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t x = raw[p] ^ 0x88888888u;
+    v[2 * p] = x & 0x0F0F0F0Fu;
+    v[2 * p + 1] = (x >> 4) & 0x0F0F0F0Fu;
+  }
+  lo = i32x4_t{static_cast<int>(v[0]), static_cast<int>(v[1]), static_cast<int>(v[2]), static_cast<int>(v[3])};
+  hi = i32x4_t{static_cast<int>(v[4]), static_cast<int>(v[5]), static_cast<int>(v[6]), static_cast<int>(v[7])};
+}
+
 template <bool F32OUT>
 __global__ __launch_bounds__(kThreads) void int4_gemm_kernel(const uint8_t* __restrict__ a, const float* __restrict__ sa,
                                                               const uint8_t* __restrict__ w, const float* __restrict__ sw,
@@ -101,7 +115,13 @@ __global__ __launch_bounds__(kThreads) void int4_gemm_kernel(const uint8_t* __re
   // products: this wave's rows of A are 128 wm + 16 i + lane%16, of W 64 wn + 16 j + lane%16
   const int wm = wv >> 2, wn = wv & 3;
   const int r16 = lane & 15, kb = lane >> 4, sw8 = swz(r16);
-  i32x4_t acc[8][4];
+  // A's codes enter the products as qa + 8 (widening without sign extension, half the work of
+  // W's), so acc[i][j] sums (qa + 8) qw; wsum[j] accumulates sum_h qw for the same rows o of W
+  // (products with an all-ones operand), and the exact sum is acc - 8 wsum.
+  i32x4_t acc[8][4], wsum[4];
+  const i32x4_t ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) wsum[j] = i32x4_t{0, 0, 0, 0};
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -113,8 +133,11 @@ __global__ __launch_bounds__(kThreads) void int4_gemm_kernel(const uint8_t* __re
     const int pos = 16 * ((4 * h + kb) ^ sw8);
     i32x4_t wlo[4], whi[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j) {
       widen(*reinterpret_cast<const u32x4_t*>(st + kCodeB + (64 * wn + 16 * j + r16) * kRowB + pos), wlo[j], whi[j]);
+      wsum[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wlo[j], ones, wsum[j], 0, 0, 0);
+      wsum[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(whi[j], ones, wsum[j], 0, 0, 0);
+    }
     auto read_a = [&](int i) __attribute__((always_inline)) {
       return *reinterpret_cast<const u32x4_t*>(st + (128 * wm + 16 * i + r16) * kRowB + pos);
     };
@@ -125,7 +148,7 @@ __global__ __launch_bounds__(kThreads) void int4_gemm_kernel(const uint8_t* __re
       if (i < 7) afn = read_a(i + 1);
       __builtin_amdgcn_sched_barrier(0);
       i32x4_t alo, ahi;
-      widen(af, alo, ahi);
+      widen_biased(af, alo, ahi);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wlo[j], alo, acc[i][j], 0, 0, 0);
@@ -174,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void int4_gemm_kernel(const uint8_t* __re
       const int64_t idx = static_cast<int64_t>(t) * O + o;
       f32x4_t v;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = static_cast<float>(acc[i][j][e]) * (sat * swv[j][e]);
+      for (int e = 0; e < 4; ++e) v[e] = static_cast<float>(acc[i][j][e] - 8 * wsum[j][e]) * (sat * swv[j][e]);
       if (vec_out && o + 4 <= O) {
         if constexpr (F32OUT)
           *reinterpret_cast<f32x4_t*>(static_cast<float*>(c) + idx) = v;
