@@ -26,29 +26,23 @@
 namespace fq {
 namespace {
 
-// Slices of x kept in flight per wave: two for small slices (the loads of the slice two
-// ahead are issued as soon as the current one's first product has consumed its
-// registers), one where registers are short.  (Three measured slower: the extra slice
-// every wave queues at the start delays every wave's first slice.)
+// Slices of x kept in flight per wave: two for slices under 4096 elements (the loads of
+// the slice two ahead are issued as soon as the current one's first product has consumed
+// its registers), one from 4096 up.  At 4096 elements one slice in flight in each of two
+// waves per SIMD beats two slices in flight in one wave per SIMD by 4-5% (while one wave
+// waits for its x the other computes); three slices in flight measured slower still (the
+// extra slice every wave queues at the start delays every wave's first slice).
 template <int M, int N, bool PG>
 constexpr int prefetch_depth() {
-  return (M * N <= 4096) ? 2 : 1;
+  return (M * N < 4096) ? 2 : 1;
 }
 
-// Waves per workgroup: 8 for the large slices (one workgroup per CU, so the CU stages its
-// 40 KB or more of P fragments once: 6-9% faster at M=64, N=128), 4 for the small ones.
+// Waves per workgroup: 8 from 4096 elements up (one workgroup per CU, so the CU stages
+// its P fragments once: 6-9% faster at M=64, N=128 than two 4-wave workgroups), 4 for the
+// small slices, which fill the CU with as many workgroups as fit.
 template <int M, int N, bool PG>
 constexpr int small_waves() {
   return prefetch_depth<M, N, PG>() == 1 ? 8 : 4;
-}
-
-// Workgroups per CU: for 4096-element slices with two in flight, one (a wave per SIMD, 8
-// slices each at K = 8192) -- 4-6% faster than the two that fit, which double the x
-// requested at the start and the P staging; smaller slices fill the CU (more waves hide
-// their shorter latency chains).  0 = as many as fit.
-template <int M, int N, bool PG>
-constexpr int small_workgroups_per_cu() {
-  return (M * N >= 4096 && prefetch_depth<M, N, PG>() == 2) ? 1 : 0;
 }
 
 // CLAMP (per token): the int4 clamp is compiled in.  SV (per group): the e8m0 rule.  Q (per
@@ -128,8 +122,9 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()), (small_waves<M, N, 
       }
       ps.scatter(pb, frag2, frag1, tid);
     } else {
-      // Large slices: registers are short, so P2 and P1 are staged one after the other
-      // and the first x load waits for the slice loop.
+      // One slice in flight: P2 and P1 are staged one after the other and the first x
+      // load waits for the slice loop (issuing it before the staging measured 4% slower
+      // at 4096 elements: the staging then waits behind it).
       ps.issue_p2(pb, b, tid);
       ps.scatter_p2(pb, frag2, tid);
       ps.issue_p1(b, tid);
@@ -346,8 +341,7 @@ hipError_t launch_one(const Problem& pb, const Buffers& b, hipStream_t s) {
       e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_small_kernel<DT, M, N, PG, CLAMP, SV, Q>,
                                                        kThreads, 0);
     if (e != hipSuccess) return e;
-    constexpr int wg = small_workgroups_per_cu<M, N, PG>();
-    grid_cap = cus * (wg > 0 ? wg : (per_cu > 0 ? per_cu : 1));
+    grid_cap = cus * (per_cu > 0 ? per_cu : 1);
   }
   const int64_t need = (pb.K + kWaves - 1) / kWaves;
   const int grid = static_cast<int>(need < grid_cap ? need : grid_cap);
