@@ -61,11 +61,19 @@ __device__ __forceinline__ uint32_t int4_nibble(float q) {
 // quantization, clamp(round(q), -max_val, max_val) with max_val 127 for INT8, 448 for FP8
 // E4M3FN and 57344 for FP8 E5M2; round half to even, section 6.1).
 //
-// INT8: the two's-complement byte of clamp(RNE(q), -127, 127).
-__device__ __forceinline__ uint32_t int8_code(float q) {
-  float r = __builtin_rintf(q);
-  r = fminf(fmaxf(r, -127.0f), 127.0f);
-  return static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xFFu;
+// INT8: clamp(RNE(q), -127, 127) in the low byte of a dword.  q is clamped first, then
+// 1.5 * 2^23 is added: fp32 numbers of that size are spaced 1 apart, so the sum is q rounded
+// to the nearest integer, ties to even (1.5 * 2^23 is even), and its bit pattern is that of
+// 1.5 * 2^23 (low byte 0) plus the integer, whose two's-complement byte is therefore the low
+// byte.  (Clamping before rounding gives the same integer: the bounds are integers.)
+__device__ __forceinline__ uint32_t int8_bits(float q) {
+  return __float_as_uint(__builtin_amdgcn_fmed3f(q, -127.0f, 127.0f) + 12582912.0f);
+}
+__device__ __forceinline__ uint32_t int8_code(float q) { return int8_bits(q) & 0xFFu; }
+
+// Low bytes of a, b -> bytes 0, 1 (bytes 2, 3 zero).
+__device__ __forceinline__ uint32_t low_bytes2(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x0C0C0400u);
 }
 
 // FP8 (OCP encodings: E4M3FN = sign, 4 exponent bits with bias 7, 3 mantissa bits, no
@@ -74,26 +82,66 @@ __device__ __forceinline__ uint32_t int8_code(float q) {
 // conversions to the OCP formats round to nearest even; with the clamp applied first they
 // never overflow, and over every fp32 input in [-max_val, max_val] they equal the rounding
 // of the fp32 mantissa to the format's bits (checked exhaustively against a bitwise encoder).
-// Two codes per call, in bytes 0 and 1.
-__device__ __forceinline__ uint32_t e4m3x2(float a, float b) {
-  const float ca = fminf(fmaxf(a, -448.0f), 448.0f), cb = fminf(fmaxf(b, -448.0f), 448.0f);
-  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false)) & 0xFFFFu;
+// Two codes per call; `old` keeps the other word (HI = false: codes in bytes 0, 1; HI =
+// true: bytes 2, 3).
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2(float a, float b, uint32_t old) {
+  const float ca = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f), cb = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, static_cast<int>(old), HI));
 }
-__device__ __forceinline__ uint32_t e5m2x2(float a, float b) {
-  const float ca = fminf(fmaxf(a, -57344.0f), 57344.0f), cb = fminf(fmaxf(b, -57344.0f), 57344.0f);
-  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_bf8_f32(ca, cb, 0, false)) & 0xFFFFu;
+template <bool HI>
+__device__ __forceinline__ uint32_t e5m2x2(float a, float b, uint32_t old) {
+  const float ca = __builtin_amdgcn_fmed3f(a, -57344.0f, 57344.0f);
+  const float cb = __builtin_amdgcn_fmed3f(b, -57344.0f, 57344.0f);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_bf8_f32(ca, cb, static_cast<int>(old), HI));
 }
+__device__ __forceinline__ uint32_t e4m3x2(float a, float b) { return e4m3x2<false>(a, b, 0u); }
+__device__ __forceinline__ uint32_t e5m2x2(float a, float b) { return e5m2x2<false>(a, b, 0u); }
 
 // Two bytes of a per-token 8-bit mode (byte 0 = a) for q = y / scale (y * (1 / scale) in the
 // MFMA kernels).
 template <int MODE>
 __device__ __forceinline__ uint32_t code8x2(float a, float b) {
   if constexpr (MODE == kPerTokenInt8)
-    return int8_code(a) | (int8_code(b) << 8);
+    return low_bytes2(int8_bits(a), int8_bits(b));
   else if constexpr (MODE == kPerTokenE4M3)
     return e4m3x2(a, b);
   else
     return e5m2x2(a, b);
+}
+
+// INT8 without the clamp, for q = y * inv where |y * inv| stays below 127.5 (the scale is
+// max|y| / (127 / clipRatio), so this holds while 127 / clipRatio, with the few ulp the scale
+// and its reciprocal add, stays below 127.5): one fused multiply-add rounds y * inv to the
+// nearest integer as int8_bits does (one rounding of the exact product instead of rounding
+// the product to fp32 first; either integer is within the product's rounding interval).
+__device__ __forceinline__ uint32_t int8_bits_fma(float y, float inv) {
+  return __float_as_uint(__builtin_fmaf(y, inv, 12582912.0f));
+}
+
+// Four bytes (byte 0 = a).
+template <int MODE>
+__device__ __forceinline__ uint32_t code8x4(float a, float b, float c, float d) {
+  if constexpr (MODE == kPerTokenInt8) {
+    const uint32_t lo = low_bytes2(int8_bits(a), int8_bits(b)), hi = low_bytes2(int8_bits(c), int8_bits(d));
+    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);  // [lo.b0, lo.b1, hi.b0, hi.b1]
+  } else if constexpr (MODE == kPerTokenE4M3) {
+    return e4m3x2<true>(c, d, e4m3x2<false>(a, b, 0u));
+  } else {
+    return e5m2x2<true>(c, d, e5m2x2<false>(a, b, 0u));
+  }
+}
+
+// The same four codes of y0..y3 * inv; CLAMP = false: the INT8 clamp is known not to bite.
+template <int MODE, bool CLAMP>
+__device__ __forceinline__ uint32_t code8x4(float y0, float y1, float y2, float y3, float inv) {
+  if constexpr (MODE == kPerTokenInt8 && !CLAMP) {
+    const uint32_t lo = low_bytes2(int8_bits_fma(y0, inv), int8_bits_fma(y1, inv));
+    const uint32_t hi = low_bytes2(int8_bits_fma(y2, inv), int8_bits_fma(y3, inv));
+    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+  } else {
+    return code8x4<MODE>(y0 * inv, y1 * inv, y2 * inv, y3 * inv);
+  }
 }
 
 // E2M1 code (sign << 3 | magnitude index) by counting the decision points passed.

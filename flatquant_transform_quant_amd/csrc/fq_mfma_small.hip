@@ -45,7 +45,7 @@ constexpr int small_waves() {
   return prefetch_depth<M, N, PG>() == 1 ? 8 : 4;
 }
 
-// CLAMP (per token): the int4 clamp is compiled in.  SV (per group): the e8m0 rule.  Q (per
+// CLAMP (per token): the int4 or INT8 clamp is compiled in.  SV (per group): the e8m0 rule.  Q (per
 // token): 0 for int4 codes, else the 8-bit mode (kPerTokenInt8 / E4M3 / E5M2), one byte a code.
 template <int DT, int M, int N, bool PG, bool CLAMP, int SV, int Q>
 // (The second launch bound is HIP's minimum of waves per SIMD: 2 keeps the 4-wave variants
@@ -236,10 +236,15 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()), (small_waves<M, N, 
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r0 = 16 * it + i;  // row - 4g
-            uint32_t w[(R + 3) / 4] = {};
+            uint32_t w[(R + 3) / 4];
+            if constexpr (R == 2) {
+              w[0] = code8x2<Q>(y[it][0][i] * inv, y[it][1][i] * inv);
+            } else {
 #pragma unroll
-            for (int nt = 0; nt < R; nt += 2)
-              w[nt / 4] |= code8x2<Q>(y[it][nt][i] * inv, y[it][nt + 1][i] * inv) << (8 * (nt % 4));
+              for (int q = 0; q < R / 4; ++q)
+                w[q] = code8x4<Q, CLAMP>(y[it][4 * q][i], y[it][4 * q + 1][i], y[it][4 * q + 2][i],
+                                         y[it][4 * q + 3][i], inv);
+            }
             uint8_t* dst = st + code_off + r0 * N;
             if constexpr (R == 2) {
               *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(w[0]);
@@ -359,7 +364,10 @@ hipError_t dispatch_clamp(const Problem& pb, const Buffers& b, hipStream_t s) {
     }
   } else {
     switch (pb.mode) {
-      case kPerTokenInt8: return launch_one<DT, M, N, false, false, kE8V1, kPerTokenInt8>(pb, b, s);
+      case kPerTokenInt8:
+        // The INT8 clamp can only bite when (127/clipRatio) * (1 + 4 ulp) reaches 127.5.
+        if (pb.d >= 127.4999f) return launch_one<DT, M, N, false, true, kE8V1, kPerTokenInt8>(pb, b, s);
+        return launch_one<DT, M, N, false, false, kE8V1, kPerTokenInt8>(pb, b, s);
       case kPerTokenE4M3: return launch_one<DT, M, N, false, false, kE8V1, kPerTokenE4M3>(pb, b, s);
       case kPerTokenE5M2: return launch_one<DT, M, N, false, false, kE8V1, kPerTokenE5M2>(pb, b, s);
       default: break;

@@ -37,7 +37,7 @@ constexpr int kIT = kW / 16;  // 16-row tiles of y
 // left-only kernel), so those stay cached.
 constexpr int kStoreNT = 2;
 
-// CLAMP (per token): the int4 clamp is compiled in.  SV (per group): the e8m0 rule.  Q (per
+// CLAMP (per token): the int4 or INT8 clamp is compiled in.  SV (per group): the e8m0 rule.  Q (per
 // token): 0 for int4 codes, else the 8-bit mode (kPerTokenInt8 / E4M3 / E5M2), one byte a code.
 template <int DT, bool PG, bool CLAMP, int SV, int Q>
 __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb, Buffers b) {
@@ -280,8 +280,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb,
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r0 = 16 * it + i;  // row - 4g
-            const uint32_t v = code8x2<Q>(y[it][0][i] * inv, y[it][1][i] * inv) |
-                               (code8x2<Q>(y[it][2][i] * inv, y[it][3][i] * inv) << 16);
+            const uint32_t v = code8x4<Q, CLAMP>(y[it][0][i], y[it][1][i], y[it][2][i], y[it][3][i], inv);
             __builtin_amdgcn_raw_buffer_store_b32(v, rs_codes, code_off, r0 * kW, kStoreNT);
             if (i == 3) __builtin_amdgcn_sched_barrier(0);
           }
@@ -575,7 +574,10 @@ hipError_t dispatch_w2(const Problem& pb, const Buffers& b, hipStream_t s) {
     }
   }
   switch (pb.mode) {
-    case kPerTokenInt8: return launch_w2<DT, false, false, kE8V1, kPerTokenInt8>(pb, b, s);
+    case kPerTokenInt8:
+      // The INT8 clamp can only bite when (127/clipRatio) * (1 + 4 ulp) reaches 127.5.
+      if (pb.d >= 127.4999f) return launch_w2<DT, false, true, kE8V1, kPerTokenInt8>(pb, b, s);
+      return launch_w2<DT, false, false, kE8V1, kPerTokenInt8>(pb, b, s);
     case kPerTokenE4M3: return launch_w2<DT, false, false, kE8V1, kPerTokenE4M3>(pb, b, s);
     case kPerTokenE5M2: return launch_w2<DT, false, false, kE8V1, kPerTokenE5M2>(pb, b, s);
     default: break;

@@ -40,6 +40,19 @@ def test_8bit_shapes_every_kernel(mode, dt):
             assert rep["ok"], rep["errors"]
 
 
+@pytest.mark.parametrize("clip", [127.0 / 127.4998, 127.0 / 127.5002, 0.5])
+def test_int8_clamp_threshold_every_kernel(clip):
+    """INT8 codes where 127/clipRatio sits just below 127.5 (the kernels then round without
+    the clamp, so the largest |y / scale| must still give 127), just above it, and well
+    above it (the clamp then bites on every slice's largest elements)."""
+    for M, N in [(64, 64), (64, 128), (256, 256)]:
+        x, p1, p2 = _inputs(M, N, "bf16", 5, seed=M + N)
+        xd, p1d, p2d = to_dev(x, "bf16"), to_dev(p1, "bf16"), to_dev(p2, "bf16")
+        for k in supported_kernels(xd, p1d, p2d, "int8", clip, 0.0):
+            rep = check(x, p1, p2, "bf16", "int8", clip, 0.0, kernel=k, label=f"int8 clip {clip:.7f} {M}x{N}")
+            assert rep["ok"], rep["errors"]
+
+
 @pytest.mark.parametrize("mode", MODES)
 def test_8bit_ragged_k(mode):
     w = synth.WORKLOADS["c2i8"]
