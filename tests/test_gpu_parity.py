@@ -88,6 +88,22 @@ def test_k_not_a_multiple_of_the_grid():
         assert rep["ok"], rep["errors"]
 
 
+@pytest.mark.parametrize("M,N,mode,kernel", [(16, 32, "int32", fq.KERNEL_MFMA_SMALL),
+                                            (16, 32, "fp4", fq.KERNEL_MFMA_SMALL),
+                                            (1, 8, "int4", fq.KERNEL_GENERIC)])
+def test_largest_k(M, N, mode, kernel):
+    """K at the library's limit (262144 slices): the persistent kernel's walk over slices and
+    the per-slice offsets of codes and scales at the far end, compared with the oracle on
+    sampled slices that include the first and the last."""
+    K = 262144
+    x = synth.gen_x(M, N, "bf16", "gauss", 0.01, 20.0, seed=5, k0=0, k1=K)
+    p1, p2 = synth.gen_orthogonal(M, "bf16", 5, 2), synth.gen_orthogonal(N, "bf16", 5, 3)
+    rng = np.random.default_rng(5)
+    slices = sorted({0, 1, K // 2 - 1, K // 2, K - 2, K - 1, *rng.integers(0, K, 26).tolist()})
+    rep = check(x, p1, p2, "bf16", mode, 1.0, 0.0, kernel=kernel, label="largest K", slices=slices)
+    assert rep["ok"], rep["errors"]
+
+
 @pytest.mark.parametrize("key", ["c4", "c5"])
 def test_k_ragged_whole_workgroup_kernels(key):
     """M = N = 256 with K leaving some CUs two or three slices and others one: the slice
