@@ -185,7 +185,7 @@ def main() -> int:
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this operator shards over K with no communication, and "
-              "this build runs and reports a single MI355X only (--gpus 1).", file=sys.stderr)
+              "the benchmark runs and reports a single MI355X only (--gpus 1).", file=sys.stderr)
         return 2
 
     import numpy as np
