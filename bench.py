@@ -1,15 +1,24 @@
 """Throughput benchmark of the fused transform + dynamic quantization operator on one GPU.
 
-A step is one fq_run over the whole workload: every slice x_k of x[K, M, N] is
-transformed (P1 . x_k . P2) and quantized, codes and scales written to HBM.  The
-default workload is K=8192, M=N=64 (hidden 4096), bf16 activations N(0,1) with 1% of
-the channels x20, random orthogonal P1/P2, per-token int4 packed in INT32, clipRatio
-0.9.  Inputs are resident in HBM before the timed region; several input/output sets are
-rotated so the 256 MB last-level cache cannot serve the reads.
+A step is one fq_run over a whole workload: every slice x_k of x[K, M, N] is transformed
+(P1 . x_k . P2) and quantized, codes and scales written to HBM.  The headline workload is
+the largest one, K=32768, M=N=256 (hidden 65536), bf16 activations N(0,1) with 1% of the
+channels x20, random orthogonal P1/P2, per-token int4 (2 codes a byte), clipRatio 0.95 --
+bound by the bf16 matrix cores.  The other four workloads (K=64 M=N=16; K=8192 M=N=64
+per-token INT32 clip 0.9; K=16384 M=64 N=128 fp16 MXFP4; K=16384 M=N=256 left-only MXFP4
+V2) are measured the same way and reported as sub-records of the same line.  Inputs are
+resident in HBM before the timed region; for the small workloads several input/output sets
+are rotated so the 256 MB last-level cache cannot serve the reads.
 
-Prints one JSON line with the metric (Gelem/s of x), the roofline record of the fused
-kernel (its average launch time measured with HIP events on its own stream) and the
-CPU oracle's throughput on a bounded sample of the same workload.
+Per workload: `steps` launches back to back on one stream, bracketed by HIP events on that
+stream (the step time), then `steps` more launches each bracketed by its own event pair (the
+launch-duration distribution: mean, median, p10, p90).  The roofline record divides the
+algorithmic bytes (HBM-bound workloads) or flops (the 256 x 256 two-sided one) by the mean
+launch duration.  HBM traffic, MFMA busy and the shader clock come from the committed
+rocprofv3 summaries under profiles/ when their kernel source hash matches the build.  The
+CPU baseline is the oracle on the host cores on a bounded sample of the workload; the same
+leg compares a sample of the timed run's outputs with the oracle (the bit-exact rule with
+its tie tolerance) and reports the result.
 """
 from __future__ import annotations
 
@@ -87,13 +96,13 @@ def kernel_source_hash(kernel: str | None = None) -> str:
     return h.hexdigest()[:16]
 
 
-def profiled_traffic(w, op="quantize"):
-    """HBM bytes per launch from the committed rocprofv3 counter summary of this workload
-    (FETCH_SIZE and WRITE_SIZE, each scaled against a copy kernel of known size), or None
-    when there is none or the kernels have changed since the counters were taken."""
+def profile_info(w, op="quantize"):
+    """The machine-readable record of the committed rocprofv3 summary of this workload's
+    kernel (profiles/<kernel>_<workload>.md), or None when there is none or the kernel's
+    device code has changed since it was taken."""
     import glob
 
-    for f in glob.glob(os.path.join(ROOT, "profiles", f"*_{w.name}.md")):
+    for f in sorted(glob.glob(os.path.join(ROOT, "profiles", f"*_{w.name}.md"))):
         if os.path.basename(f).startswith("dequant_") != (op == "dequant"):
             continue
         with open(f, encoding="utf-8") as fh:
@@ -101,8 +110,15 @@ def profiled_traffic(w, op="quantize"):
                 if line.startswith("machine-readable:"):
                     info = json.loads(line.split(":", 1)[1])
                     if info.get("source_hash") == kernel_source_hash(info.get("kernel")):
-                        return info.get("traffic_bytes_per_dispatch")
+                        return info
     return None
+
+
+def profiled_traffic(w, op="quantize"):
+    """HBM bytes per launch from the committed counter summary (FETCH_SIZE and WRITE_SIZE,
+    each scaled against a copy kernel of known size), or None."""
+    info = profile_info(w, op)
+    return info.get("traffic_bytes_per_dispatch") if info else None
 
 
 def profiled_gemm_traffic(kernel: str, product: str):
@@ -120,9 +136,22 @@ def profiled_gemm_traffic(kernel: str, product: str):
     return None
 
 
-def cpu_baseline(w, x_host, p1, p2, budget_s: float = 10.0):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, x_host, p1, p2, budget_s: float = 10.0, gpu_slices=None):
     """The oracle (codes and scales only) on the host cores, on a bounded sample of
-    slices of the same workload, scaled to Gelem/s."""
+    slices of the same workload, scaled to Gelem/s.  With `gpu_slices` (a function giving
+    the timed run's packed codes and scales for a list of slice indices) the same leg also
+    checks a sample of the timed outputs against the oracle."""
     import oracle
 
     threads = max(1, min(os.cpu_count() or 1, 64))
@@ -147,8 +176,26 @@ def cpu_baseline(w, x_host, p1, p2, budget_s: float = 10.0):
         dt = time.perf_counter() - t
     elems = reps * n * w.M * w.N
     what = f"{reps} passes over all {w.K} slices" if reps > 1 else f"first {n} of {w.K} slices"
-    return {"value": elems / dt / 1e9, "unit": "Gelem/s", "cores": threads, "kind": "oracle",
-            "sample": f"{what} ({elems} elements), {dt:.2f} s wall on {threads} threads"}
+    rec = {"value": elems / dt / 1e9, "unit": "Gelem/s", "cores": threads, "kind": "oracle",
+           "cpu_model": cpu_model(),
+           "sample": f"{what} ({elems} elements), {dt:.2f} s wall on {threads} threads"}
+    if gpu_slices is not None:
+        import numpy as np
+
+        from oracle.compare import compare
+
+        rng = np.random.default_rng(0)
+        count = 8 if w.M * w.N > 16384 else 128
+        idx = sorted({0, w.K // 2, w.K - 1, *rng.integers(0, w.K, count).tolist()})
+        packed, scale = gpu_slices(idx)
+        orc = oracle.run(x_host[idx], p1, p2, w.dtype, w.mode, w.clip_ratio, w.dst_type_max, nthreads=threads)
+        rep = compare(orc, packed, scale)
+        rec["parity_of_timed_outputs"] = {
+            "slices": len(idx), "elements": rep["elements"], "ok": rep["ok"], "mismatch": rep["mismatch"],
+            "mismatch_cap": rep["mismatch_cap"], "outside_tie_window": rep["mismatch_out_of_window"],
+            "outside_tie_window_cap": rep["out_of_window_cap"], "scale_ties": rep.get("scale_ties"),
+            "alt_groups": rep.get("alt_groups"), "errors": rep["errors"][:3]}
+    return rec
 
 
 def cpu_baseline_dequant(w, packed, scale, budget_s: float = 10.0):
@@ -169,19 +216,156 @@ def cpu_baseline_dequant(w, packed, scale, budget_s: float = 10.0):
             "sample": f"{reps} passes over all {w.K} slices ({elems} elements), {dt:.2f} s wall on 1 thread"}
 
 
+def percentile_summary(ms):
+    import numpy as np
+
+    a = np.asarray(ms, dtype=np.float64) * 1e3
+    return {"mean": round(float(a.mean()), 3), "median": round(float(np.median(a)), 3),
+            "p10": round(float(np.percentile(a, 10)), 3), "p90": round(float(np.percentile(a, 90)), 3),
+            "unit": "us"}
+
+
+def time_launches(step, steps, warmup, stream):
+    """`steps` calls of step(i) back to back on `stream` bracketed by one event pair (the
+    step time), then `steps` more, each bracketed by its own pair (the launch durations)."""
+    import torch
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        step(i)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return total_ms, [a.elapsed_time(b) for a, b in ev]
+
+
+def launch_floor(stream, steps):
+    """Duration of a minimal kernel (a one-element add) launched the same way: the fixed cost
+    every launch pays."""
+    import torch
+
+    t = torch.zeros(1, device=torch.device("cuda:0"))
+
+    def step(i):
+        with torch.cuda.stream(stream):
+            t.add_(1.0)
+
+    total, each = time_launches(step, steps, 10, stream)
+    return {"what": "one-element torch add on the same stream", "step_us": round(total / steps * 1e3, 3),
+            "launch_us": percentile_summary(each)}
+
+
+def measure_workload(key, args, dev):
+    """One workload: inputs resident, timed launches, roofline, CPU baseline + parity."""
+    import numpy as np
+    import torch
+
+    import flatquant_transform_quant_amd as fq
+    import synth
+
+    w = synth.WORKLOADS[key]
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float16
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(tdt).to(dev)
+
+    print(f"[bench] {key}: generating K={w.K} M={w.M} N={w.N}", file=sys.stderr, flush=True)
+    x_host, p1, p2 = synth.make_inputs(w)
+    # rotate input/output sets so one lap touches > 2x the 256 MB last-level cache
+    per_set = algorithmic_bytes(w)
+    nsets = int(max(1, min(8, -(-(600 * 2 ** 20) // per_set))))
+    xs = [to_dev(x_host)]
+    for _ in range(1, nsets):
+        xs.append(xs[0].clone())  # distinct buffers with the same values
+    p1d = to_dev(p1)
+    p2d = to_dev(p2) if p2 is not None else None
+    outs = [fq.empty_outputs(w.K, w.M, w.N, w.mode, dev) for _ in range(nsets)]
+    execs = [fq.Executor(xs[i], p1d, p2d, outs[i][0], outs[i][1], w.mode, w.clip_ratio,
+                         w.dst_type_max, kernel=args.kernel) for i in range(nsets)]
+    kernel_id = execs[0].kernel
+    stream = torch.cuda.Stream(dev)  # the kernels' stream; every event is recorded on it
+    torch.cuda.synchronize()
+    total_ms, each_ms = time_launches(lambda i: execs[i % nsets].run(stream), args.steps, args.warmup, stream)
+    ms_per_step = total_ms / args.steps
+    lat = percentile_summary(each_ms)
+    mean_s = lat["mean"] / 1e6
+    elems = w.K * w.M * w.N
+    bytes_ = algorithmic_bytes(w)
+    flops = algorithmic_flops(w)
+    gbs = bytes_ / mean_s / 1e9
+    tfs = flops / mean_s / 1e12
+    hbm_frac = gbs / HBM_PEAK_GBS
+    mfma_frac = tfs / MFMA_BF16_PEAK_TFS
+    bound = "hbm" if bytes_ / (HBM_PEAK_GBS * 1e9) >= flops / (MFMA_BF16_PEAK_TFS * 1e12) else "mfma"
+    info = profile_info(w)
+    roof = ({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(hbm_frac, 4)}
+            if bound == "hbm" else
+            {"bound": "mfma", "achieved": round(tfs, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+             "frac": round(mfma_frac, 4)})
+    roof["traffic"] = info.get("traffic_bytes_per_dispatch") if info else None
+    roof["kernel"] = {1: "generic_kernel", 2: "mfma_small_kernel", 3: "mfma_wide_kernel"}.get(kernel_id)
+    roof["avg_launch_us"] = lat["mean"]
+    roof["algorithmic_bytes"] = bytes_
+    roof["algorithmic_flops"] = flops
+    roof["other_frac"] = round(mfma_frac if bound == "hbm" else hbm_frac, 4)
+    if info:
+        roof["profile"] = {"avg_us": round(info["avg_ns"] / 1e3, 3), "mfma_busy": info.get("mfma_busy"),
+                           "shader_clock_ghz": info.get("clock_ghz_est"), "source_hash": info["source_hash"]}
+    rec = {"workload": w.name, "K": w.K, "M": w.M, "N": w.N, "dtype": w.dtype, "mode": w.mode,
+           "clip_ratio": w.clip_ratio, "dst_type_max": w.dst_type_max, "two_sided": w.two_sided,
+           "buffer_sets": nsets, "value": round(elems * args.steps / (total_ms / 1e3) / 1e9, 2),
+           "unit": "Gelem/s", "ms_per_step": round(ms_per_step, 5), "launch_us": lat, "roofline": roof}
+    if w.K * w.M * w.N <= 2 ** 16:
+        rec["launch_floor"] = launch_floor(stream, args.steps)
+    for e in execs:
+        e.destroy()
+    out0, sc0 = outs[(args.steps - 1) % nsets]  # the last timed launch's outputs
+
+    def gpu_slices(idx):
+        t = torch.as_tensor(idx, device=dev)
+        packed = out0.contiguous().view(torch.uint8).reshape(w.K, -1)[t].cpu().numpy()
+        sc = sc0.contiguous()
+        scale = (sc.view(torch.uint8).reshape(w.K, -1)[t] if w.mode == "fp4" else sc[t]).cpu().numpy()
+        return packed, scale
+
+    rec["cpu_baseline"] = (None if args.no_cpu else
+                           cpu_baseline(w, x_host, p1, p2, args.cpu_budget, gpu_slices=gpu_slices))
+    del xs, outs, execs, out0, sc0
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
+HEADLINE = "c4"
+SUB_RECORDS = ("c1", "c2", "c3", "c5")
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="c2", help="workload key (c1..c5); c2 is the headline")
+    ap.add_argument("--config", default="all",
+                    help="all (the headline c4 with c1, c2, c3, c5 as sub-records) or one workload key")
     ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 generic, 2 mfma-small, 3 mfma-wide")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline (and its parity check)")
+    ap.add_argument("--cpu-budget", type=float, default=8.0)
     ap.add_argument("--op", default="quantize", choices=["quantize", "dequant", "mxgemm", "i4gemm"],
-                    help="quantize (the fused operator, default), dequant (codes + scales -> values) or "
-                         "mxgemm (the MXFP4 GEMM consuming a per-group workload's output)")
-    ap.add_argument("--gemm-out", type=int, default=8192, help="mxgemm: output features O")
+                    help="quantize (the fused operator, default), dequant (codes + scales -> values), "
+                         "mxgemm / i4gemm (the GEMMs consuming a workload's output)")
+    ap.add_argument("--gemm-out", type=int, default=8192, help="mxgemm / i4gemm: output features O")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this operator shards over K with no communication, and "
@@ -191,103 +375,48 @@ def main() -> int:
     import numpy as np
     import torch
 
-    import flatquant_transform_quant_amd as fq
     import synth
 
-    w = synth.WORKLOADS[args.config]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float16
+    if args.op != "quantize":
+        key = HEADLINE if args.config == "all" else args.config
+        w = synth.WORKLOADS[key]
+        tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float16
 
-    def to_dev(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(tdt).to(dev)
+        def to_dev(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(tdt).to(dev)
 
-    x_host, p1, p2 = synth.make_inputs(w)
-    if args.op == "dequant":
-        return bench_dequant(args, w, x_host, p1, p2, to_dev, dev, tdt)
-    if args.op == "mxgemm":
-        return bench_mx_gemm(args, w, x_host, p1, p2, to_dev, dev)
-    if args.op == "i4gemm":
+        x_host, p1, p2 = synth.make_inputs(w)
+        if args.op == "dequant":
+            return bench_dequant(args, w, x_host, p1, p2, to_dev, dev, tdt)
+        if args.op == "mxgemm":
+            return bench_mx_gemm(args, w, x_host, p1, p2, to_dev, dev)
         return bench_int4_gemm(args, w, x_host, p1, p2, to_dev, dev)
-    # rotate input/output sets so one lap touches > 2x the 256 MB last-level cache
-    per_set = algorithmic_bytes(w)
-    nsets = int(max(1, min(8, -(-(600 * 2 ** 20) // per_set))))
-    xs = [to_dev(x_host)]
-    for i in range(1, nsets):
-        # distinct buffers with the same values
-        xs.append(xs[0].clone())
-    p1d = to_dev(p1)
-    p2d = to_dev(p2) if p2 is not None else None
-    outs = [fq.empty_outputs(w.K, w.M, w.N, w.mode, dev) for _ in range(nsets)]
-    execs = [fq.Executor(xs[i], p1d, p2d, outs[i][0], outs[i][1], w.mode, w.clip_ratio,
-                         w.dst_type_max, kernel=args.kernel) for i in range(nsets)]
-    kernel_id = execs[0].kernel
-    stream = torch.cuda.Stream(dev)  # the kernels' stream; events are recorded on it
-    torch.cuda.synchronize()
 
-    for i in range(args.warmup):
-        execs[i % nsets].run(stream)
-    torch.cuda.synchronize()
-
-    # whole-job timing over exactly `steps` steps
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(args.steps):
-        execs[i % nsets].run(stream)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    ms_per_step = total_ms / args.steps
-
-    # Average launch duration of the fused kernel: the timed region holds exactly one
-    # launch per step, back to back on `stream`, so its events give the mean launch
-    # time (an event pair around each single launch would add the ~3-5 us cost of the
-    # event records themselves).  rocprofv3 --kernel-trace of the same command agrees.
-    avg_launch_ms = ms_per_step
-    elems = w.K * w.M * w.N
-    value = elems * args.steps / (total_ms / 1e3) / 1e9
-    bytes_ = algorithmic_bytes(w)
-    flops = algorithmic_flops(w)
-    gbs = bytes_ / (avg_launch_ms / 1e3) / 1e9
-    tfs = flops / (avg_launch_ms / 1e3) / 1e12
-    hbm_frac = gbs / HBM_PEAK_GBS
-    mfma_frac = tfs / MFMA_BF16_PEAK_TFS
-    bound = "hbm" if bytes_ / (HBM_PEAK_GBS * 1e9) >= flops / (MFMA_BF16_PEAK_TFS * 1e12) else "mfma"
-    traffic = profiled_traffic(w)
-    roof = ({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-             "frac": round(hbm_frac, 4), "traffic": traffic}
-            if bound == "hbm" else
-            {"bound": "mfma", "achieved": round(tfs, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-             "frac": round(mfma_frac, 4), "traffic": traffic})
-    roof["kernel"] = {1: "generic_kernel", 2: "mfma_small_kernel", 3: "mfma_wide_kernel"}.get(kernel_id)
-    roof["avg_launch_us"] = round(avg_launch_ms * 1e3, 3)
-    roof["algorithmic_bytes"] = bytes_
-    roof["algorithmic_flops"] = flops
-    roof["other_frac"] = round(mfma_frac if bound == "hbm" else hbm_frac, 4)
-
-    for e in execs:
-        e.destroy()
-    cpu = None if args.no_cpu else cpu_baseline(w, x_host, p1, p2, args.cpu_budget)
+    keys = [HEADLINE, *SUB_RECORDS] if args.config == "all" else [args.config]
+    recs = [measure_workload(k, args, dev) for k in keys]
+    head = recs[0]
     line = {
         "metric": "Gelem/s quantized (x[K,M,N] elems) + % of HBM/MFMA roofline, 1 MI355X",
-        "value": round(value, 2),
+        "value": head["value"],
         "unit": "Gelem/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": head["dtype"],
         "data": "synthetic",
-        "config": {"workload": w.name, "K": w.K, "M": w.M, "N": w.N, "mode": w.mode,
-                   "clip_ratio": w.clip_ratio, "dst_type_max": w.dst_type_max,
-                   "two_sided": w.two_sided, "buffer_sets": nsets, "parallelism": "none"},
-        "roofline": roof,
-        "cpu_baseline": cpu,
+        "config": {"workload": head["workload"], "K": head["K"], "M": head["M"], "N": head["N"],
+                   "mode": head["mode"], "clip_ratio": head["clip_ratio"], "dst_type_max": head["dst_type_max"],
+                   "two_sided": head["two_sided"], "buffer_sets": head["buffer_sets"], "parallelism": "none"},
+        "launch_us": head["launch_us"],
+        "roofline": head["roofline"],
+        "cpu_baseline": head["cpu_baseline"],
+        "sub_records": recs[1:],
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -45,13 +45,21 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   return r;
 }
 
-template <int DT>
+// FIXUP: redo only the per-token slices whose stored scale is below 2^-126 (and above 0).
+// The 256-class two-sided kernel encodes y * (1 / scale), and 1 / scale overflows for a
+// scale below 2^-128; its slices with such tiny scales are recomputed here, where the
+// codes come from y / scale.  Every other slice is skipped after one scale read.
+template <int DT, bool FIXUP>
 __global__ __launch_bounds__(kGenericThreads) void generic_kernel(Problem pb, Buffers b) {
   extern __shared__ uint16_t Ts[];  // M * N
   __shared__ float red[kGenericThreads / 64];
   const int M = static_cast<int>(pb.M), N = static_cast<int>(pb.N), MN = M * N;
   const int tid = threadIdx.x;
   for (int64_t k = blockIdx.x; k < pb.K; k += gridDim.x) {
+    if constexpr (FIXUP) {
+      const float s_old = static_cast<const float*>(b.scale)[k];  // the same for every thread
+      if (!(s_old > 0.0f && s_old < 0x1p-126f)) continue;
+    }
     const uint16_t* xk = b.x + k * pb.xs_k;  // row m of the slice at xk + m * xs_m
     const int64_t xs_m = pb.xs_m;
     // [FQV2] 第1步: T = x_k . P2, rounded to the dtype; skipped for an empty P2.
@@ -162,20 +170,31 @@ int grid_for(int64_t total, int threads) {
   return static_cast<int>(g);
 }
 
-}  // namespace
-
-hipError_t launch_generic(const Problem& pb, const Buffers& b, hipStream_t s) {
+template <bool FIXUP>
+hipError_t launch_generic_t(const Problem& pb, const Buffers& b, hipStream_t s, int max_grid) {
   const size_t lds = static_cast<size_t>(pb.M * pb.N) * 2;
-  const int grid = static_cast<int>(pb.K < 4096 ? pb.K : 4096);
-  const void* fn = pb.dtype == kBF16 ? reinterpret_cast<const void*>(generic_kernel<kBF16>)
-                                     : reinterpret_cast<const void*>(generic_kernel<kF16>);
+  const int grid = static_cast<int>(pb.K < max_grid ? pb.K : max_grid);
+  const void* fn = pb.dtype == kBF16 ? reinterpret_cast<const void*>(generic_kernel<kBF16, FIXUP>)
+                                     : reinterpret_cast<const void*>(generic_kernel<kF16, FIXUP>);
   hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (err != hipSuccess) return err;
   if (pb.dtype == kBF16)
-    generic_kernel<kBF16><<<grid, kGenericThreads, lds, s>>>(pb, b);
+    generic_kernel<kBF16, FIXUP><<<grid, kGenericThreads, lds, s>>>(pb, b);
   else
-    generic_kernel<kF16><<<grid, kGenericThreads, lds, s>>>(pb, b);
+    generic_kernel<kF16, FIXUP><<<grid, kGenericThreads, lds, s>>>(pb, b);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_generic(const Problem& pb, const Buffers& b, hipStream_t s) {
+  return launch_generic_t<false>(pb, b, s, 4096);
+}
+
+hipError_t launch_tiny_scale_fixup(const Problem& pb, const Buffers& b, hipStream_t s) {
+  if (byte_codes(pb.mode) || pb.mode == kPerTokenInt32 || pb.mode == kPerTokenInt4)
+    return launch_generic_t<true>(pb, b, s, 256);
+  return hipSuccess;  // per group: the scales are powers of two, nothing overflows
 }
 
 hipError_t launch_gather16(const uint16_t* src, uint16_t* dst, const int64_t shape[3],

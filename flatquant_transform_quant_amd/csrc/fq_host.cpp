@@ -328,7 +328,13 @@ fq_status fq_run(void* workspace, uint64_t workspaceSize, fq_executor* executor,
     if (err != hipSuccess) { st = fail_runtime("strided input gather launch", err); break; }
     switch (e->kernel) {
       case fq::kMfmaSmall: err = fq::launch_mfma_small(pb, b, stream); break;
-      case fq::kMfmaWide: err = fq::launch_mfma_wide(pb, b, stream); break;
+      case fq::kMfmaWide:
+        err = fq::launch_mfma_wide(pb, b, stream);
+        // its per-token epilogue multiplies by 1 / scale: slices with a scale below 2^-126
+        // are re-encoded by division
+        if (err == hipSuccess && pb.two_sided && pb.mode != fq::kPerGroupFp4)
+          err = fq::launch_tiny_scale_fixup(pb, b, stream);
+        break;
       default: err = fq::launch_generic(pb, b, stream); break;
     }
     if (err != hipSuccess) { st = fail_runtime("transform-quantize kernel launch", err); break; }

@@ -56,6 +56,9 @@ __host__ __device__ inline int64_t e8m0_bytes_per_slice(int64_t MN) { return 2 *
 
 // Launchers (enqueue only; return the launch status).
 hipError_t launch_generic(const Problem& pb, const Buffers& b, hipStream_t s);
+// Re-encodes, after a kernel that encodes y * (1 / scale), the per-token slices whose scale
+// is below 2^-126 (where 1 / scale can overflow), with y / scale; skips every other slice.
+hipError_t launch_tiny_scale_fixup(const Problem& pb, const Buffers& b, hipStream_t s);
 bool mfma_small_supports(const Problem& pb);
 hipError_t launch_mfma_small(const Problem& pb, const Buffers& b, hipStream_t s);
 bool mfma_wide_supports(const Problem& pb);

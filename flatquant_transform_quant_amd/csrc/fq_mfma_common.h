@@ -211,18 +211,38 @@ __device__ __forceinline__ float wave_max(float v) {
 // ---- per-token int4 ------------------------------------------------------------------
 // RNE(y * inv) with the round-to-integer done by the fp32 adder: fma(y, inv, 1.5*2^23 + 8)
 // rounds the exact product once at unit spacing (ties to even, as 1.5*2^23 + 8 is even),
-// leaving code + 8 in the low mantissa bits.  The clamp to [-8, 7] is an integer clamp of
-// the bit pattern (needed only when 7/clipRatio can reach 7.5).  Result: low nibble =
-// code + 8, bits 4..7 zero, bits above are the constant's (ignored by the packers).
+// leaving code + 8 in the low mantissa bits.  The clamp to [-8, 7] is a clamp of the bit
+// pattern as a SIGNED integer (needed only when 7/clipRatio can reach 7.5): over positive
+// floats the bit order is the value order, and a sum that went negative (y * inv below
+// -12582920, possible when clipRatio is below about 5.6e-7) has its sign bit set, so it
+// sorts below every positive pattern and clamps to -8.  Result: low nibble = code + 8,
+// bits 4..7 zero, bits above are the constant's (ignored by the packers).
 constexpr float kInt4Magic = 12582920.0f;  // 1.5 * 2^23 + 8
-constexpr uint32_t kInt4MagicLo = 0x4B400000u;  // bits of 1.5 * 2^23 (code -8)
-constexpr uint32_t kInt4MagicHi = 0x4B40000Fu;  // code +7
+constexpr int32_t kInt4MagicLo = 0x4B400000;  // bits of 1.5 * 2^23 (code -8)
+constexpr int32_t kInt4MagicHi = 0x4B40000F;  // code +7
 
 template <bool CLAMP>
 __device__ __forceinline__ uint32_t int4_biased(float y, float inv) {
-  uint32_t b = __float_as_uint(__builtin_fmaf(y, inv, kInt4Magic));
+  int32_t b = __float_as_int(__builtin_fmaf(y, inv, kInt4Magic));
   if constexpr (CLAMP) b = min(max(b, kInt4MagicLo), kInt4MagicHi);
-  return b;
+  return static_cast<uint32_t>(b);
+}
+
+// The reciprocal of a per-token scale as a pair (pre, inv) with y * scale^-1 = (y * pre) * inv.
+// For a scale below 2^-126 the reciprocal itself can overflow (1 / scale is +inf below
+// 2^-128); there both factors are taken with 2^64 moved into y: pre = 2^64 (exact: y is at
+// most max|y| = scale * d, far from overflow) and inv = 1 / (scale * 2^64) (scale * 2^64 is
+// exact).  A zero scale (all-zero slice) gives inv = 0 and so codes of 0.
+struct TokenRecip {
+  float pre, inv;
+  bool tiny;
+};
+__device__ __forceinline__ TokenRecip token_recip(float scale) {
+  TokenRecip r;
+  r.tiny = scale > 0.0f && scale < 0x1p-126f;
+  r.pre = r.tiny ? 0x1p64f : 1.0f;
+  r.inv = scale > 0.0f ? 1.0f / (scale * r.pre) : 0.0f;
+  return r;
 }
 
 // Two biased codes -> one byte (low nibble = first), in the low byte of the result.

@@ -225,8 +225,18 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()), (small_waves<M, N, 
 #pragma unroll
           for (int i = 0; i < 4; ++i) amax = fmaxf(amax, __builtin_fabsf(y[it][nt][i]));
       amax = wave_max(amax);
-      const float scale = amax / pb.d;
-      const float inv = scale > 0.0f ? 1.0f / scale : 0.0f;
+      // (every lane holds the same maximum; the scale is made wave-uniform so the branch
+      // below is a scalar one)
+      const float scale = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(amax / pb.d)));
+      const TokenRecip rc = token_recip(scale);
+      if (rc.tiny) {
+        // a scale below 2^-126: y * 2^64 exactly, and inv = 1 / (scale * 2^64)
+#pragma unroll
+        for (int it = 0; it < MT; ++it)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) y[it][nt] *= rc.pre;
+      }
+      const float inv = rc.inv;
       if (lane == 0) static_cast<float*>(b.scale)[s] = scale;
       if constexpr (Q != 0) {
         // 8-bit codes (the dequant_swiglu_quant page, section 3.4): the lane's R codes of a

@@ -94,6 +94,8 @@ def lib():
         L.fqo_dequant8.restype = ctypes.c_int
         L.fqo_int4_gemm.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, p, p, p, p, p]
         L.fqo_int4_gemm.restype = ctypes.c_int
+        L.fqo_decode16.argtypes = [p, ctypes.c_int64, ctypes.c_int, p]
+        L.fqo_decode16.restype = ctypes.c_int
         L.fqo_mx_gemm.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, p, p, p, p, p, p]
         L.fqo_mx_gemm.restype = ctypes.c_int
         _lib = L
@@ -144,6 +146,15 @@ def e8m0_v1(amax: float) -> int:
 def e8m0_v2(amax: float, dmax: float, how: str = "bits") -> int:
     fn = lib().fqo_e8m0_v2_bits if how == "bits" else lib().fqo_e8m0_v2_frexp
     return fn(amax, dmax)
+
+
+def decode16(bits, dtype: str) -> np.ndarray:
+    """The oracle's own decoding of 16-bit dtype bits to float64 (fqo_decode16)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(b.shape, np.float64)
+    if lib().fqo_decode16(b.ctypes.data, b.size, _DT[dtype], out.ctypes.data) != 0:
+        raise ValueError("fqo_decode16 rejected the dtype")
+    return out
 
 
 def round_f32(v: float) -> float:

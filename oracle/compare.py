@@ -11,9 +11,18 @@ The rule (per element of x[K, M, N]):
     per scale) that the error bound itself spans several of them where y is a small result
     of cancellation;
   * such differences may make up at most ceil(1e-4 * elements) of a result;
+  * for the 4-bit codes, the differences outside the stated 1e-6 tie window (reachable only
+    through the fp32 summation error bound, mostly through the dtype rounding of the
+    intermediate) may make up at most ceil(1e-5 * elements) -- about five times the largest
+    measured rate (1.8e-6 of elements, over millions of elements of every workload).  The
+    8-bit codes keep the overall cap alone: with 127 or more steps a scale, a flipped
+    rounding of the intermediate (about one in 10^4 of its elements for 256-term sums) moves
+    y across an FP8 code boundary about once, so outside the window they run at 1e-5 (64 x 64)
+    to 8e-5 (256 x 256) of elements;
   * per-token fp32 scales agree within 1e-5 relative -- or, for a slice whose largest
     element is itself moved by a reachable rounding tie of the intermediate, lie inside the
-    oracle's reachable scale interval (counted as "scale_ties");
+    oracle's reachable scale interval (counted as "scale_ties"; at most
+    max(1, ceil(0.02 * slices)) of them, against a measured rate of at most 1 in 96);
   * an e8m0 code equals the oracle's, or is the oracle's alternative code when the group's
     max is within error (or 1e-6 relative) of a power-of-two boundary; that group's
     codes are then checked against the oracle's encoding under the alternative code;
@@ -26,6 +35,8 @@ import math
 import numpy as np
 
 MISMATCH_CAP_REL = 1e-4
+OUT_OF_WINDOW_CAP_REL = {"4bit": 1e-5, "8bit": MISMATCH_CAP_REL}
+SCALE_TIES_CAP_REL = 0.02
 SCALE_REL_TOL = 1e-5
 
 
@@ -97,6 +108,10 @@ def compare(orc: dict, gpu_packed: np.ndarray, gpu_scale: np.ndarray, max_report
         if "scale_lo" in orc:
             in_range = (gs >= orc["scale_lo"]) & (gs <= orc["scale_hi"])
         rep["scale_ties"] = int((~tight & in_range).sum())
+        rep["scale_ties_cap"] = max(1, math.ceil(SCALE_TIES_CAP_REL * S))
+        if rep["scale_ties"] > rep["scale_ties_cap"]:
+            errs.append(f"{rep['scale_ties']} slices with a scale outside 1e-5 (inside the reachable interval) "
+                        f"exceed the cap {rep['scale_ties_cap']}")
         bad = np.nonzero(~tight & ~in_range)[0]
         for s in bad[:max_report]:
             errs.append(f"slice {s}: scale {gs[s]!r} vs oracle {os_[s]!r} "
@@ -155,5 +170,11 @@ def compare(orc: dict, gpu_packed: np.ndarray, gpu_scale: np.ndarray, max_report
     rep["mismatch_cap"] = cap
     if rep["mismatch"] > cap:
         errs.append(f"{rep['mismatch']} tie mismatches exceed the cap {cap}")
+    rep["mismatch_out_of_window"] = rep["mismatch"] - rep["mismatch_in_stated_window"]
+    ocap = math.ceil(OUT_OF_WINDOW_CAP_REL["8bit" if byte_codes else "4bit"] * rep["elements"])
+    rep["out_of_window_cap"] = ocap
+    if rep["mismatch_out_of_window"] > ocap:
+        errs.append(f"{rep['mismatch_out_of_window']} mismatches outside the stated 1e-6 tie window exceed the "
+                    f"cap {ocap}")
     rep["ok"] = not errs
     return rep

@@ -97,6 +97,14 @@ static double f16_value(uint16_t h) {
 
 static double dt_value(uint16_t h, int dtype) { return dtype == FQO_BF16 ? bf16_value(h) : f16_value(h); }
 
+/* The decoding above over an array, exported for the pins (every bit pattern of both
+ * formats is checked against independent decoders). */
+int fqo_decode16(const uint16_t* bits, int64_t n, int dtype, double* out) {
+  if (dtype != FQO_F16 && dtype != FQO_BF16) return -1;
+  for (int64_t i = 0; i < n; ++i) out[i] = dt_value(bits[i], dtype);
+  return 0;
+}
+
 /* ---- round to nearest even into a binary format -------------------------
  * A format with `frac` fraction bits, minimum normal exponent `emin` and
  * largest finite value `maxv`.  Textbook construction: scale so that the

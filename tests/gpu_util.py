@@ -72,7 +72,8 @@ def check(x, p1, p2, dt, mode, clip, dmax, kernel=fq.KERNEL_AUTO, label="", slic
     idx = np.arange(K) if slices is None else np.asarray(slices)
     orc = oracle.run(x[idx], p1, p2, dt, mode, clip, dmax, nthreads=8)
     rep = compare(orc, packed[idx], scale[idx])
-    say(f"[gpu]   -> mismatches {rep['mismatch']} (in stated window {rep['mismatch_in_stated_window']}, "
-        f"cap {rep['mismatch_cap']}), flagged {rep['flagged']}, alt groups {rep['alt_groups']}, "
-        f"max scale rel {rep['max_scale_rel']:.2e}, scale ties {rep.get('scale_ties', 0)}, ok={rep['ok']}")
+    say(f"[gpu]   -> mismatches {rep['mismatch']} (cap {rep['mismatch_cap']}; outside the stated window "
+        f"{rep['mismatch_out_of_window']}, cap {rep['out_of_window_cap']}), flagged {rep['flagged']}, "
+        f"alt groups {rep['alt_groups']}, max scale rel {rep['max_scale_rel']:.2e}, scale ties "
+        f"{rep.get('scale_ties', 0)} (cap {rep.get('scale_ties_cap', 0)}), ok={rep['ok']}")
     return rep

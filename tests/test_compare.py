@@ -196,3 +196,42 @@ def test_byte_codes_rule(mode):
     g[s, f] = _level_to_code(int(r["hi"][s, f]) + 1, mode)
     assert not compare(r, g, r["scale"])["ok"]
     assert not compare(r, r["packed"], r["scale"] * np.float32(1.001))["ok"]
+
+
+def test_out_of_window_cap():
+    """Differences at elements the oracle flags only through the fp32 error bound (not a tie
+    within 1e-6) are allowed up to ceil(1e-5 * elements) for the 4-bit codes; one more fails."""
+    r = _pertoken(8)
+    codes = unpack_nibbles(r["packed"], r["M"] * r["N"])
+    idx = np.argwhere((r["hi"] > r["lvl"]) & (r["ns_tie"] == 0))
+    cap = int(np.ceil(1e-5 * codes.size))
+    assert len(idx) > cap
+    for n, want_ok in ((cap, True), (cap + 1, False)):
+        c = codes.copy()
+        for s, f in idx[:n]:
+            c[s, f] = (c[s, f] + 1) & 0xF
+        rep = compare(r, _repack(c), r["scale"])
+        assert rep["ok"] == want_ok and rep["mismatch_out_of_window"] == n and rep["out_of_window_cap"] == cap
+
+
+def test_scale_ties_cap():
+    """Scales outside 1e-5 but inside the reachable interval are allowed on at most
+    max(1, ceil(0.02 * slices)) slices."""
+    r = _pertoken(64)
+    sc = r["scale"].astype(np.float64)
+    lo, hi = r["scale_lo"].astype(np.float64), r["scale_hi"].astype(np.float64)
+    dev = np.maximum(hi - sc, sc - lo) / sc
+    wide = np.nonzero(dev > 1.5e-5)[0]
+    cap = max(1, int(np.ceil(0.02 * 64)))
+    if len(wide) <= cap:
+        # widen more slices' intervals on a copy, as an ambiguous intermediate would
+        r = dict(r)
+        r["scale_hi"] = (r["scale"] * np.float32(1 + 1e-3)).astype(np.float32)
+        hi = r["scale_hi"].astype(np.float64)
+        wide = np.arange(64)
+    for n, want_ok in ((cap, True), (cap + 1, False)):
+        g = r["scale"].copy()
+        for s in wide[:n]:
+            g[s] = np.float32(hi[s] if hi[s] - sc[s] >= sc[s] - lo[s] else lo[s])
+        rep = compare(r, r["packed"], g)
+        assert rep["ok"] == want_ok and rep["scale_ties"] == n

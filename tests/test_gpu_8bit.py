@@ -29,7 +29,9 @@ def _inputs(M, N, dt, K, seed):
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
 def test_8bit_shapes_every_kernel(mode, dt):
     for i, (M, N) in enumerate(SHAPES):
-        K = 6 if M * N <= 64 * 64 else 3
+        # (256 x 256: enough slices that the FP8 mismatch count, about 8e-5 of elements
+        # against the 1e-4 cap, does not hinge on one slice)
+        K = 6 if M * N <= 64 * 64 else (12 if M * N == 65536 else 3)
         x, p1, p2 = _inputs(M, N, dt, K, seed=M * 1000 + N)
         clip = 1.0 if i % 2 == 0 else 0.9
         xd, p1d, p2d = to_dev(x, dt), to_dev(p1, dt), to_dev(p2, dt)

@@ -135,8 +135,10 @@ def test_full_size_sampled(key):
     say(f"[gpu] generating {key} full size K={w.K}")
     x, p1, p2 = synth.make_inputs(w)
     rng = np.random.default_rng(0)
-    n_rand = 12 if w.M * w.N <= 8192 else 4
-    slices = sorted({0, 1, w.K // 2, w.K - 2, w.K - 1, *rng.integers(0, w.K, n_rand).tolist()})
+    # every CU's first and last slice of the persistent walk are among the 256-class samples
+    n_rand = 12 if w.M * w.N <= 8192 else 64
+    slices = sorted({0, 1, 255, 256, w.K // 2, w.K - 257, w.K - 256, w.K - 2, w.K - 1,
+                     *rng.integers(0, w.K, n_rand).tolist()})
     rep = check(x, p1, p2, w.dtype, w.mode, w.clip_ratio, w.dst_type_max, label=f"{key} full",
                 slices=slices)
     assert rep["ok"], rep["errors"]
@@ -163,7 +165,7 @@ def test_deterministic_across_runs_and_streams(key):
         assert np.array_equal(ref[0], got[0]) and np.array_equal(ref[1], got[1])
 
 
-@pytest.mark.parametrize("key", ["c1", "c2", "c3", "c5"])
+@pytest.mark.parametrize("key", ["c1", "c2", "c3", "c4", "c5"])
 def test_canary_guards_untouched(key):
     """Outputs placed between 4 KB guard bands: nothing outside them is written."""
     w = synth.WORKLOADS[key]
