@@ -69,6 +69,8 @@ def _load():
     L.fq_get_workspace_size.restype = ctypes.c_int32
     L.fq_run.argtypes = [vp, ctypes.c_uint64, vp, vp]
     L.fq_run.restype = ctypes.c_int32
+    L.fq_run_no_alloc.argtypes = [vp, vp]
+    L.fq_run_no_alloc.restype = ctypes.c_int32
     L.fq_executor_destroy.argtypes = [vp]
     L.fq_executor_destroy.restype = None
     L.fq_executor_set_repeatable.argtypes = [vp, ctypes.c_int32]
@@ -95,8 +97,9 @@ def _load():
 
 lib = _load()
 EXPORTS = ("fq_get_workspace_size", "fq_run", "fq_executor_destroy", "fq_executor_set_repeatable",
-           "fq_executor_set_kernel", "fq_executor_kernel", "fq_status_string", "fq_last_error", "fq_dequant", "fq_v1_get_workspace_size", "fq_mx_gemm",
-           "fq_int4_gemm")
+           "fq_executor_set_kernel", "fq_executor_kernel", "fq_status_string", "fq_last_error", "fq_dequant",
+           "fq_v1_get_workspace_size", "fq_mx_gemm", "fq_int4_gemm", "fq_run_no_alloc")
+NO_ALLOC_SCRATCH_BYTES = 64 << 20  # FQ_NO_ALLOC_SCRATCH_BYTES of include/fq.h
 
 
 def status_string(status: int) -> str:
@@ -146,6 +149,10 @@ def fq_v1_get_workspace_size(x: FqTensor, p1: FqTensor, p2: FqTensor, clip_ratio
 
 def fq_run(workspace_ptr: int, workspace_size: int, executor: int, stream_ptr: int) -> int:
     return lib.fq_run(workspace_ptr or None, workspace_size, executor, stream_ptr or None)
+
+
+def fq_run_no_alloc(executor: int, stream_ptr: int) -> int:
+    return lib.fq_run_no_alloc(executor, stream_ptr or None)
 
 
 def fq_executor_destroy(executor: int) -> None:

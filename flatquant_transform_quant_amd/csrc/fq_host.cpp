@@ -384,6 +384,67 @@ void fq_executor_destroy(fq_executor* executor) {
   if (live(executor)) release(executor);
 }
 
+}  // extern "C"
+
+// ---- fq_run without a caller-allocated workspace ------------------------------------------
+// The staging buffer of non-contiguous tensors (the workspace of fq_run) taken from a
+// file-scope device array instead.  Each device the library runs on holds its own copy
+// (FQ_NO_ALLOC_SCRATCH_BYTES) until the process ends.  Host code never uses the array's
+// name as an address: the device address of the current device's copy is looked up once
+// per device with hipGetSymbolAddress and kept.
+static __device__ __align__(256) uint8_t scratch[FQ_NO_ALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];  // per device id, set on the first call on that device
+
+fq_status scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return fail_runtime("hipGetDevice", err);
+  if (dev < 0 || dev >= 64) return fail_runtime("device id beyond the scratch table", hipErrorInvalidDevice);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || !p) return fail_runtime("hipGetSymbolAddress of the scratch array", err);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FQ_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+fq_status fq_run_no_alloc(fq_executor* executor, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (!executor) return FQ_ERR_PARAM_NULLPTR;
+  if (!live(executor)) return FQ_ERR_PARAM_INVALID;
+  fq_executor* e = executor;
+  if (e->ws_size > FQ_NO_ALLOC_SCRATCH_BYTES) {
+    std::snprintf(g_last_error, sizeof(g_last_error),
+                  "the planned workspace of %llu bytes exceeds the %llu-byte scratch of fq_run_no_alloc",
+                  static_cast<unsigned long long>(e->ws_size),
+                  static_cast<unsigned long long>(FQ_NO_ALLOC_SCRATCH_BYTES));
+    if (!e->repeatable) release(e);
+    return FQ_ERR_PARAM_INVALID;
+  }
+  void* ws = nullptr;
+  if (e->ws_size > 0) {
+    fq_status st = device_is_gfx950() ? scratch_of_current_device(&ws)
+                                      : fail_runtime("the current device is not gfx950", hipSuccess);
+    if (st != FQ_SUCCESS) {
+      if (!e->repeatable) release(e);
+      return st;
+    }
+  }
+  // the same launches as fq_run, with the scratch array as the workspace (no allocation)
+  return fq_run(ws, e->ws_size, e, stream);
+}
+
 fq_status fq_v1_get_workspace_size(const fq_tensor* x, const fq_tensor* kroneckerP1,
                                    const fq_tensor* kroneckerP2, double clipRatio, const fq_tensor* out,
                                    const fq_tensor* quantScale, uint64_t* workspaceSize, fq_executor** executor) {

@@ -141,6 +141,22 @@ fq_status fq_v1_get_workspace_size(const fq_tensor* x, const fq_tensor* kronecke
  * Calls with distinct executors may come from different host threads. */
 fq_status fq_run(void* workspace, uint64_t workspaceSize, fq_executor* executor, hipStream_t stream);
 
+/* ---- second stage without a workspace allocation ------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph capture, serving loops
+ * that forbid hipMalloc, harnesses that forbid it): fq_run with the staging buffer of
+ * non-contiguous tensors taken from a device array inside the library instead of a
+ * caller-allocated workspace.  The array holds FQ_NO_ALLOC_SCRATCH_BYTES (64 MiB) on every
+ * device the library runs on, until the process ends.  No hipMalloc, hipFree or other
+ * allocating call is made.  Behaviour otherwise as fq_run (single-use executors are released
+ * whatever the outcome).  Errors: NULL executor -> FQ_ERR_PARAM_NULLPTR; executor not live,
+ * or a planned workspace above FQ_NO_ALLOC_SCRATCH_BYTES -> FQ_ERR_PARAM_INVALID (checked
+ * before any HIP call; fq_last_error() names the sizes); not a gfx950 device or a launch
+ * failure -> FQ_ERR_RUNTIME.  Every call on one device shares that device's array: calls that
+ * overlap in time on one device (different streams, or different host threads) race on it and
+ * must be ordered by the caller.  The array is overwritten before it is read on every call. */
+#define FQ_NO_ALLOC_SCRATCH_BYTES (64ull << 20)
+fq_status fq_run_no_alloc(fq_executor* executor, hipStream_t stream);
+
 /* ---- dequantization ------------------------------------------------------------------
  * The values of the codes fq_run writes, in a 16-bit float dtype: the second half of a
  * quantize -> dequantize ("fake-quant") round trip, e.g. to measure the RMS error

@@ -268,6 +268,23 @@ def test_run_argument_checks_without_device():
         fq.fq_executor_destroy(ex)
 
 
+def test_run_no_alloc_argument_checks_without_device():
+    """fq_run_no_alloc: NULL and dead executors, and a planned workspace above its 64 MiB
+    scratch, are rejected before any HIP call; a rejected single-use executor is released."""
+    assert fq.fq_run_no_alloc(0, 0) == NULLP
+    p = problem()
+    # a strided x of 262144 x 16 x 16 bf16 stages 128 MiB through the workspace
+    p["x"] = tens(fq.DT_BFLOAT16, (262144, 16, 16), (512, 32, 2))
+    p["out"] = tens(fq.DT_INT32, (262144, 16, 2))
+    p["sc"] = tens(fq.DT_FLOAT32, (262144,))
+    st, ws, ex = fq.fq_get_workspace_size(p["x"], p["p1"], p["p2"], 1.0, 0.0, p["out"], p["sc"])
+    assert st == OK and ws > fq.NO_ALLOC_SCRATCH_BYTES
+    assert fq.fq_run_no_alloc(ex, 0) == INVAL
+    assert "exceeds" in fq.fq_last_error() and str(ws) in fq.fq_last_error()
+    assert fq.fq_run_no_alloc(ex, 0) == INVAL  # released: no longer live
+    assert fq.fq_executor_kernel(ex) < 0
+
+
 def test_kernel_selection_api():
     st, ws, ex = fq.fq_get_workspace_size(*[problem()[k] for k in ("x", "p1", "p2")], 1.0, 0.0,
                                           problem()["out"], problem()["sc"])
