@@ -48,17 +48,33 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 // FIXUP: redo only the per-token slices whose stored scale is below 2^-126 (and above 0).
 // The 256-class two-sided kernel encodes y * (1 / scale), and 1 / scale overflows for a
 // scale below 2^-128; its slices with such tiny scales are recomputed here, where the
-// codes come from y / scale.  Every other slice is skipped after one scale read.
+// codes come from y / scale.  Workgroup g looks at slices [256 g, 256 g + 256): each thread
+// reads one scale (all in parallel), and only the flagged slices are recomputed.
+__device__ __forceinline__ bool tiny_scale(float s) { return s > 0.0f && s < 0x1p-126f; }
+
 template <int DT, bool FIXUP>
 __global__ __launch_bounds__(kGenericThreads) void generic_kernel(Problem pb, Buffers b) {
   extern __shared__ uint16_t Ts[];  // M * N
   __shared__ float red[kGenericThreads / 64];
+  __shared__ uint32_t flags[kGenericThreads / 32];
   const int M = static_cast<int>(pb.M), N = static_cast<int>(pb.N), MN = M * N;
   const int tid = threadIdx.x;
-  for (int64_t k = blockIdx.x; k < pb.K; k += gridDim.x) {
+  int64_t k_begin = blockIdx.x, k_end = pb.K, k_step = gridDim.x;
+  if constexpr (FIXUP) {
+    k_begin = int64_t(blockIdx.x) * kGenericThreads;
+    k_end = k_begin + kGenericThreads < pb.K ? k_begin + kGenericThreads : pb.K;
+    k_step = 1;
+    if (tid < kGenericThreads / 32) flags[tid] = 0u;
+    __syncthreads();
+    const int64_t mine = k_begin + tid;
+    if (mine < k_end && tiny_scale(static_cast<const float*>(b.scale)[mine]))
+      atomicOr(&flags[tid >> 5], 1u << (tid & 31));
+    __syncthreads();
+  }
+  for (int64_t k = k_begin; k < k_end; k += k_step) {
     if constexpr (FIXUP) {
-      const float s_old = static_cast<const float*>(b.scale)[k];  // the same for every thread
-      if (!(s_old > 0.0f && s_old < 0x1p-126f)) continue;
+      const int i = static_cast<int>(k - k_begin);  // the same for every thread
+      if (!((flags[i >> 5] >> (i & 31)) & 1u)) continue;
     }
     const uint16_t* xk = b.x + k * pb.xs_k;  // row m of the slice at xk + m * xs_m
     const int64_t xs_m = pb.xs_m;
@@ -192,8 +208,11 @@ hipError_t launch_generic(const Problem& pb, const Buffers& b, hipStream_t s) {
 }
 
 hipError_t launch_tiny_scale_fixup(const Problem& pb, const Buffers& b, hipStream_t s) {
-  if (byte_codes(pb.mode) || pb.mode == kPerTokenInt32 || pb.mode == kPerTokenInt4)
-    return launch_generic_t<true>(pb, b, s, 256);
+  if (byte_codes(pb.mode) || pb.mode == kPerTokenInt32 || pb.mode == kPerTokenInt4) {
+    // one workgroup per 256 slices (the kernel's own grid rule for FIXUP)
+    const int64_t groups = (pb.K + kGenericThreads - 1) / kGenericThreads;
+    return launch_generic_t<true>(pb, b, s, static_cast<int>(groups));
+  }
   return hipSuccess;  // per group: the scales are powers of two, nothing overflows
 }
 

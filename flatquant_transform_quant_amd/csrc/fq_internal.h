@@ -18,7 +18,7 @@ enum Mode : int32_t {
 };
 // codes of one byte each (the 8-bit per-token modes) rather than two codes a byte
 __host__ __device__ inline bool byte_codes(int32_t mode) { return mode >= kPerTokenInt8; }
-enum Kernel : int32_t { kAuto = 0, kGeneric = 1, kMfmaSmall = 2, kMfmaWide = 3 };
+enum Kernel : int32_t { kAuto = 0, kGeneric = 1, kMfmaSmall = 2, kMfmaWide = 3, kMfmaWideT = 4 };
 
 // One planned problem, as the kernels see it (all tensors contiguous).
 struct Problem {
@@ -63,6 +63,10 @@ bool mfma_small_supports(const Problem& pb);
 hipError_t launch_mfma_small(const Problem& pb, const Buffers& b, hipStream_t s);
 bool mfma_wide_supports(const Problem& pb);
 hipError_t launch_mfma_wide(const Problem& pb, const Buffers& b, hipStream_t s);
+// The pipelined 256 x 256 two-sided per-token int4 kernel (codes formed under the next
+// slice's first products).
+bool mfma_wide2t_supports(const Problem& pb);
+hipError_t launch_mfma_wide2t(const Problem& pb, const Buffers& b, hipStream_t s);
 
 // Dequantization of contiguous codes/scales into a contiguous [K, M, N] 16-bit output.
 hipError_t launch_dequant(int32_t dtype, bool per_group, int64_t K, int64_t M, int64_t N, const uint8_t* codes,
