@@ -131,6 +131,7 @@ bool kernel_supports(int32_t k, const fq_executor* e) {
 }
 
 int32_t auto_kernel(const fq_executor* e) {
+  if (kernel_supports(fq::kMfmaWideT, e)) return fq::kMfmaWideT;
   if (kernel_supports(fq::kMfmaWide, e)) return fq::kMfmaWide;
   if (kernel_supports(fq::kMfmaSmall, e)) return fq::kMfmaSmall;
   return fq::kGeneric;

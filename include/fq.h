@@ -241,9 +241,10 @@ fq_status fq_executor_set_repeatable(fq_executor* executor, int32_t repeat);
 /* Kernel variant the executor will launch: 0 = the automatic choice, 1 = the generic
  * kernel (any shape), 2 = the small-slice MFMA kernel (one wave per slice), 3 = the
  * whole-workgroup MFMA kernel for 256-class slices, 4 = its pipelined form for 256 x 256
- * slices with both transforms and per-token int4 codes (INT32 / INT4 out).  Selecting a variant that does not support the planned
- * problem returns FQ_ERR_PARAM_INVALID and leaves the executor unchanged.  Meant for
- * tests and benchmarks. */
+ * slices with both transforms and per-token int4 codes (INT32 / INT4 out; the automatic
+ * choice there).  Selecting a variant that does not support the planned problem returns
+ * FQ_ERR_PARAM_INVALID and leaves the executor unchanged.  Meant for tests and
+ * benchmarks. */
 fq_status fq_executor_set_kernel(fq_executor* executor, int32_t variant);
 
 /* The variant the executor will launch (1 .. 4), or a negative value for NULL. */
