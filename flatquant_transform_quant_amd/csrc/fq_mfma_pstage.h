@@ -16,7 +16,7 @@ namespace fq {
 
 template <int DT, int M, int N, int THREADS>
 struct PStage {
-  static constexpr int MT = M / 16, NT = N / 16, R = N / 16, KS1 = N / 32, KS2 = (M + 31) / 32;
+  static constexpr int MT = M / 16, NT = N / 16, R = N / 16, KS1 = (N + 31) / 32, KS2 = (M + 31) / 32;
   static constexpr int FRAG2 = KS1 * NT * 64, FRAG1 = MT * KS2 * 64;  // u32x4 slots
   // P2 goes by 8x8 blocks (rows 32ks + 8g .. +7, columns 8cb .. 8cb+7): one thread loads
   // the block's 8 rows (16 bytes each), pairs the rows of each column with v_perm_b32 and
@@ -82,6 +82,11 @@ struct PStage {
   __device__ __forceinline__ void scatter_p2(const Problem& pb, u32x4_t* frag2, int tid) {
     asm volatile("" : "+v"(tid));
     if (pb.two_sided != 0) {
+      if constexpr (N < 32) {
+        // N = 16: the k-slots 16 .. 31 of the padded contraction (lane groups 2 and 3) are zero
+        for (int idx = tid; idx < FRAG2; idx += THREADS)
+          if (((idx & 63) >> 4) >= N / 8) frag2[idx] = u32x4_t{0u, 0u, 0u, 0u};
+      }
 #pragma unroll
       for (int q = 0; q < L2; ++q) {
         const int blk = tid + q * THREADS;

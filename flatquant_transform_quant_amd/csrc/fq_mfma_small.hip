@@ -1,5 +1,6 @@
 // Small-slice MFMA kernel: one wave per slice x_k [M, N] for M in {16, 32, 64, 128},
-// N in {32, 64, 128}, M*N <= 8192, both modes, both dtypes.
+// N in {32, 64, 128}, M*N <= 8192, both modes, both dtypes; and N = 16 for the int4 per-token
+// codes (GEMM1's contraction padded to 32 with zero columns of x and zero rows of P2).
 //
 // [FQV2] 拆开算 第1步/第2步 on the matrix cores, fused with 第3步/第4步:
 //   GEMM1  T = x_k . P2   A = x rows (straight from HBM, 16 B per lane),
@@ -11,7 +12,8 @@
 //   The epilogue quantizes y from registers; y is never stored.
 // Column labelling: output column c of n-tile nt is the real column R*c + nt (R = N/16),
 // so after the last n-tile every lane holds R consecutive columns of 4 rows -- R/2 code
-// bytes per row, and a 32-group spans 32/R neighbouring lanes.
+// bytes per row, and a 32-group spans 32/R neighbouring lanes.  At N = 16 (R = 1) a lane
+// holds one column and the two lanes of a column pair form the pair's code byte together.
 // An empty P2 ([0, 0]) is run as P2 = I: T = RNE(x * 1) = x exactly.
 //
 // The waves of a workgroup share P1/P2 fragments staged once in LDS in operand order (one
@@ -56,11 +58,11 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()), (small_waves<M, N, 
   constexpr int kSmallWaves = small_waves<M, N, PG>();
   constexpr int kSmallThreads = 64 * kSmallWaves;
   constexpr int MT = M / 16, NT = N / 16, R = N / 16;
-  constexpr int KS1 = N / 32;              // GEMM1 k-steps over j
+  constexpr int KS1 = (N + 31) / 32;       // GEMM1 k-steps over j (N = 16: one, half of it zeros)
   constexpr int KS2 = (M + 31) / 32;       // GEMM2 k-steps over m
   constexpr int MN = M * N;
   constexpr int SPAN = 32 / R;             // lanes per 32-group (per-group mode)
-  static_assert(N % 32 == 0 && M % 16 == 0 && R >= 2, "unsupported shape");
+  static_assert(((N % 32 == 0 && R >= 2) || (N == 16 && !PG && Q == 0)) && M % 16 == 0, "unsupported shape");
 
   __shared__ u32x4_t frag2[KS1 * NT * 64];  // B fragments of P2 (or of I)
   __shared__ u32x4_t frag1[MT * KS2 * 64];  // A fragments of P1 (k relabelled)
@@ -101,8 +103,9 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()), (small_waves<M, N, 
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int ks = 0; ks < KS1; ++ks)
-        xa[buf][mt][ks] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (c * xs_m + 32 * ks + 8 * g) * 2,
-                                                                16 * mt * xs_m * 2, 0);
+        xa[buf][mt][ks] = __builtin_amdgcn_raw_buffer_load_b128(
+            rsrc, (N >= 32 || 8 * g < N) ? (c * xs_m + 32 * ks + 8 * g) * 2 : x_span,  // past N: zeros
+            16 * mt * xs_m * 2, 0);
   };
   // ---- stage P2 / P1 fragments (once per workgroup) ----
   // The P loads go first and the x loads of the first slices right after them, so the
@@ -167,7 +170,7 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()), (small_waves<M, N, 
     // e8m0 byte).  Made opaque per slice so the per-row addresses are formed here, with
     // the row as an immediate offset, instead of being hoisted out of the slice loop and
     // held in registers.
-    int code_off = Q ? 4 * g * N + R * c : 4 * g * (N / 2) + (R / 2) * c;
+    int code_off = Q ? 4 * g * N + R * c : 4 * g * (N / 2) + (R >= 2 ? (R / 2) * c : c / 2);
     int e8_off = CODE_BYTES + 4 * g * (N / 32) + (R * c) / 32;
     asm volatile("" : "+v"(code_off), "+v"(e8_off));
     // ---- GEMM1: T = x . P2 (fp32), rounded to the dtype and written straight into the
@@ -269,13 +272,20 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()), (small_waves<M, N, 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r0 = 16 * it + i;  // row - 4g
-          uint32_t by[R / 2];
+          uint32_t by[R >= 2 ? R / 2 : 1];
+          if constexpr (R == 1) {
+            // columns c and c ^ 1 (lane c ^ 1 holds the other): both lanes form the same byte
+            const uint32_t own = int4_biased<CLAMP>(y[it][0][i], inv);
+            const uint32_t nbr = dpp_u<kDppQuadXor1>(own);
+            by[0] = (c & 1) ? pair_byte(nbr, own) : pair_byte(own, nbr);
+          } else {
 #pragma unroll
-          for (int p = 0; p < R / 2; ++p)
-            by[p] = pair_byte(int4_biased<CLAMP>(y[it][2 * p][i], inv),
-                              int4_biased<CLAMP>(y[it][2 * p + 1][i], inv));
+            for (int p = 0; p < R / 2; ++p)
+              by[p] = pair_byte(int4_biased<CLAMP>(y[it][2 * p][i], inv),
+                                int4_biased<CLAMP>(y[it][2 * p + 1][i], inv));
+          }
           uint8_t* dst = st + code_off + r0 * (N / 2);
-          if constexpr (R == 2) {
+          if constexpr (R <= 2) {
             *dst = static_cast<uint8_t>(by[0] ^ 0x88u);
           } else if constexpr (R == 4) {
             *reinterpret_cast<uint16_t*>(dst) =
@@ -364,6 +374,14 @@ hipError_t launch_one(const Problem& pb, const Buffers& b, hipStream_t s) {
   return hipGetLastError();
 }
 
+// int4 per-token codes (INT32 / INT4 out)
+template <int DT, int M, int N>
+hipError_t dispatch_int4(const Problem& pb, const Buffers& b, hipStream_t s) {
+  // The int4 clamp can only bite when (7/clipRatio) * (1 + 4 ulp) reaches 7.5.
+  if (pb.d >= 7.4999f) return launch_one<DT, M, N, false, true, kE8V1>(pb, b, s);
+  return launch_one<DT, M, N, false, false, kE8V1>(pb, b, s);
+}
+
 template <int DT, int M, int N, bool PG>
 hipError_t dispatch_clamp(const Problem& pb, const Buffers& b, hipStream_t s) {
   if constexpr (PG) {
@@ -382,9 +400,7 @@ hipError_t dispatch_clamp(const Problem& pb, const Buffers& b, hipStream_t s) {
       case kPerTokenE5M2: return launch_one<DT, M, N, false, false, kE8V1, kPerTokenE5M2>(pb, b, s);
       default: break;
     }
-    // The int4 clamp can only bite when (7/clipRatio) * (1 + 4 ulp) reaches 7.5.
-    if (pb.d >= 7.4999f) return launch_one<DT, M, N, false, true, kE8V1>(pb, b, s);
-    return launch_one<DT, M, N, false, false, kE8V1>(pb, b, s);
+    return dispatch_int4<DT, M, N>(pb, b, s);
   }
 }
 
@@ -398,6 +414,9 @@ hipError_t dispatch_mode(const Problem& pb, const Buffers& b, hipStream_t s) {
 template <int DT, int M>
 hipError_t dispatch_n(const Problem& pb, const Buffers& b, hipStream_t s) {
   switch (pb.N) {
+    case 16:
+      if (pb.mode == kPerTokenInt32 || pb.mode == kPerTokenInt4) return dispatch_int4<DT, M, 16>(pb, b, s);
+      break;
     case 32: return dispatch_mode<DT, M, 32>(pb, b, s);
     case 64: return dispatch_mode<DT, M, 64>(pb, b, s);
     case 128:
@@ -422,7 +441,10 @@ hipError_t dispatch_m(const Problem& pb, const Buffers& b, hipStream_t s) {
 
 bool mfma_small_supports(const Problem& pb) {
   const bool m_ok = pb.M == 16 || pb.M == 32 || pb.M == 64 || pb.M == 128;
-  const bool n_ok = pb.N == 32 || pb.N == 64 || pb.N == 128;
+  // N = 16: int4 per-token codes only (one code a lane per row: the 8-bit and per-group
+  // layouts are not implemented for it)
+  const bool n_ok = pb.N == 32 || pb.N == 64 || pb.N == 128 ||
+                    (pb.N == 16 && (pb.mode == kPerTokenInt32 || pb.mode == kPerTokenInt4));
   // registers: the per-token path keeps all of y (M*N/64 fp32 per lane)
   const int64_t cap = pb.mode == kPerGroupFp4 ? 8192 : 4096;
   return m_ok && n_ok && pb.M * pb.N <= cap;

@@ -45,6 +45,7 @@ EDGE_PER_TOKEN = [  # (M, N, mode)
     (64, 64, "int32"), (128, 128, "int32"), (256, 256, "int32"),
     (1, 2, "int4"), (3, 2, "int4"), (17, 34, "int4"), (33, 30, "int4"), (64, 128, "int4"),
     (255, 254, "int4"), (256, 256, "int4"), (128, 256, "int4"),
+    (32, 16, "int4"), (64, 16, "int32"), (128, 16, "int4"),  # N = 16 on the small MFMA kernel
 ]
 
 
@@ -89,6 +90,7 @@ def test_k_not_a_multiple_of_the_grid():
 
 
 @pytest.mark.parametrize("M,N,mode,kernel", [(16, 32, "int32", fq.KERNEL_MFMA_SMALL),
+                                            (16, 16, "int4", fq.KERNEL_MFMA_SMALL),
                                             (16, 32, "fp4", fq.KERNEL_MFMA_SMALL),
                                             (1, 8, "int4", fq.KERNEL_GENERIC)])
 def test_largest_k(M, N, mode, kernel):
