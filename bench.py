@@ -74,8 +74,8 @@ def algorithmic_flops(w, K=None) -> int:
 
 # the source file of each profiled kernel
 KERNEL_SOURCES = {"generic": "fq_generic.hip", "mfma_small": "fq_mfma_small.hip", "mfma_wide1": "fq_mfma_wide.hip",
-                  "mfma_wide2": "fq_mfma_wide.hip", "dequant": "fq_dequant.hip", "mx_gemm_kernel": "fq_mx_gemm.hip",
-                  "int4_gemm_kernel": "fq_int4_gemm.hip"}
+                  "mfma_wide2": "fq_mfma_wide.hip", "mfma_wide2t": "fq_mfma_wide2t.hip", "dequant": "fq_dequant.hip",
+                  "mx_gemm_kernel": "fq_mx_gemm.hip", "int4_gemm_kernel": "fq_int4_gemm.hip"}
 
 
 def kernel_source_hash(kernel: str | None = None) -> str:
@@ -267,6 +267,30 @@ def launch_floor(stream, steps):
             "launch_us": percentile_summary(each)}
 
 
+def copy_reference(nbytes, nsets, stream, steps, dev):
+    """A torch device copy moving the same bytes as one launch (half read, half written),
+    over as many rotating buffer sets: what plain streaming reaches at this transfer size."""
+    import torch
+
+    half = max(1, nbytes // 2)
+    bufs = [(torch.empty(half, dtype=torch.uint8, device=dev), torch.empty(half, dtype=torch.uint8, device=dev))
+            for _ in range(nsets)]
+
+    def step(i):
+        src, dst = bufs[i % nsets]
+        with torch.cuda.stream(stream):
+            dst.copy_(src)
+
+    total, each = time_launches(step, steps, 5, stream)
+    lat = percentile_summary(each)
+    step_us = total / steps * 1e3
+    del bufs
+    torch.cuda.empty_cache()
+    return {"what": "torch copy of the same bytes (half read, half written), rotating sets as above",
+            "bytes": 2 * half, "step_us": round(step_us, 3), "frac": round(2 * half / (step_us * 1e-6) / (HBM_PEAK_GBS * 1e9), 4),
+            "launch_us": lat}
+
+
 def measure_workload(key, args, dev):
     """One workload: inputs resident, timed launches, roofline, CPU baseline + parity."""
     import numpy as np
@@ -316,7 +340,8 @@ def measure_workload(key, args, dev):
             {"bound": "mfma", "achieved": round(tfs, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
              "frac": round(mfma_frac, 4)})
     roof["traffic"] = info.get("traffic_bytes_per_dispatch") if info else None
-    roof["kernel"] = {1: "generic_kernel", 2: "mfma_small_kernel", 3: "mfma_wide_kernel"}.get(kernel_id)
+    roof["kernel"] = {1: "generic_kernel", 2: "mfma_small_kernel", 3: "mfma_wide_kernel",
+                      4: "mfma_wide2t_kernel"}.get(kernel_id)
     roof["avg_launch_us"] = round(ms_per_step * 1e3, 3)
     roof["algorithmic_bytes"] = bytes_
     roof["algorithmic_flops"] = flops
@@ -330,6 +355,8 @@ def measure_workload(key, args, dev):
            "unit": "Gelem/s", "ms_per_step": round(ms_per_step, 5), "launch_us": lat, "roofline": roof}
     if w.K * w.M * w.N <= 2 ** 16:
         rec["launch_floor"] = launch_floor(stream, args.steps)
+    if bound == "hbm":
+        rec["copy_reference"] = copy_reference(bytes_, nsets, stream, args.steps, dev)
     for e in execs:
         e.destroy()
     out0, sc0 = outs[(args.steps - 1) % nsets]  # the last timed launch's outputs
@@ -360,7 +387,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="all",
                     help="all (the headline c4 with c1, c2, c3, c5 as sub-records) or one workload key")
-    ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 generic, 2 mfma-small, 3 mfma-wide")
+    ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 generic, 2 mfma-small, 3 mfma-wide, 4 mfma-wide pipelined (256x256 two-sided per-token)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline (and its parity check)")
     ap.add_argument("--cpu-budget", type=float, default=8.0)
     ap.add_argument("--op", default="quantize", choices=["quantize", "dequant", "mxgemm", "i4gemm"],

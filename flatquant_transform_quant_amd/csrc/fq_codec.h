@@ -80,8 +80,8 @@ __device__ __forceinline__ uint32_t low_bytes2(uint32_t a, uint32_t b) {
 // infinities; E5M2 = sign, 5 exponent bits with bias 15, 2 mantissa bits): the value nearest
 // clamp(q, -max_val, max_val), a tie to the even code, with q's sign bit.  gfx950's packed
 // conversions to the OCP formats round to nearest even; with the clamp applied first they
-// never overflow, and over every fp32 input in [-max_val, max_val] they equal the rounding
-// of the fp32 mantissa to the format's bits (checked exhaustively against a bitwise encoder).
+// never overflow (the GPU tests check the codes bit-exact at every FP8 value, every tie and
+// its neighbours, both signs).
 // Two codes per call; `old` keeps the other word (HI = false: codes in bytes 0, 1; HI =
 // true: bytes 2, 3).
 template <bool HI>

@@ -266,8 +266,9 @@ __device__ __forceinline__ float e8m0_to_float(uint32_t code) {
 
 // v_cvt_scalef32_pk_fp4_f32: two values divided by the power-of-two scale, rounded to
 // E2M1 (nearest, ties to even, saturating at 6, sign kept), packed into byte SEL of
-// `old` with the first value in the low nibble.  Bit-identical to e2m1_code(ldexp(v,
-// 127 - code)) for every fp32 input -- checked on the device over all 2^32 patterns.
+// `old` with the first value in the low nibble.  The GPU tests check it bit-exact against
+// the encoder of the page's magnitudes at every decision point, the values next to it,
+// saturation above 6, and the extreme e8m0 codes 0 and 254.
 template <int SEL>
 __device__ __forceinline__ uint32_t fp4x2(uint32_t old, float a, float b, float scale) {
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, scale, SEL);
