@@ -37,7 +37,7 @@ struct fq_executor {
   fq_tensor x, p1, p2, out, scale;
   bool stage_x, stage_p1, stage_p2, stage_out, stage_scale;
   bool x_direct;  // a non-contiguous x read in place through its strides (no gather)
-  uint64_t off_x, off_p1, off_p2, off_out, off_scale, ws_size;
+  uint64_t off_x, off_p1, off_p2, off_out, off_scale, off_ctr, ws_size;
 };
 
 namespace {
@@ -275,6 +275,8 @@ fq_status fq_get_workspace_size(const fq_tensor* x, const fq_tensor* kroneckerP1
   e->off_scale = take(e->stage_scale, mode == fq::kPerGroupFp4
                                           ? uint64_t(K * fq::e8m0_bytes_per_slice(MN))
                                           : uint64_t(K) * 4);
+  // the slice counter of the pipelined 256 x 256 kernel (it hands out slices at run time)
+  e->off_ctr = take(kernel_supports(fq::kMfmaWideT, e), 4);
   e->ws_size = off;
   e->kernel = auto_kernel(e);
   {
@@ -338,6 +340,7 @@ fq_status fq_run(void* workspace, uint64_t workspaceSize, fq_executor* executor,
           err = fq::launch_tiny_scale_fixup(pb, b, stream);
         break;
       case fq::kMfmaWideT:
+        b.ctr = reinterpret_cast<uint32_t*>(ws + e->off_ctr);
         err = fq::launch_mfma_wide2t(pb, b, stream);
         if (err == hipSuccess) err = fq::launch_tiny_scale_fixup(pb, b, stream);  // as above
         break;

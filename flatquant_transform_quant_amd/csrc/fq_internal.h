@@ -45,6 +45,7 @@ struct Buffers {
   const uint16_t* p2;
   uint8_t* codes;
   void* scale;
+  uint32_t* ctr = nullptr;  // slice counter of the kernels that hand out slices at run time (4 bytes)
 };
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

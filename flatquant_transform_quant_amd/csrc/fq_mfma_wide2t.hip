@@ -28,6 +28,13 @@
 // where G1'(c) is chunk c of the wave's next slice; the codes of this slice run during
 // G1'(0), G1'(1) and the next slice's G2(0).  The slice's max|y| is reduced across the 4
 // waves through an LDS buffer that is free at that point.
+//
+// Slices are handed out at run time: a counter in device memory (zeroed before the launch)
+// gives each workgroup its next slice, one atomic add per slice, taken two slices ahead
+// (the next slice's first x chunk is requested halfway through the current one) and passed
+// to the workgroup's waves with the max reduction.  The XCDs of the device run at clocks a
+// few percent apart under this load, and with a fixed share of the slices per workgroup
+// the launch ended with the slowest (every workgroup takes the same cycle count).
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -46,7 +53,16 @@ constexpr int kNChunk = kW / kChunk;
 constexpr int kIT = kW / 16;  // 16-row tiles of y
 constexpr int kYA = 8;        // y tiles 0 .. kYA-1 in accumulation registers, the rest in ordinary ones
 constexpr int kEl = kIT * 16;  // y elements a lane
-constexpr int kBarStage = 8;   // the stage of a GEMM2 block that passes the barrier of the GEMM1 block before it
+constexpr int kBarStage = 8;
+
+// A ticket of the slice counter: the counter's value before adding one.  An increment that
+// wraps at 2^32 - 1 (the same as adding one for every reachable value) rather than an add: the
+// compiler rewrites a single-address add into a wave-combined form that reads the reply
+// straight away, with a wait for every memory access in flight, where this form leaves the
+// wait at the reply's first use.
+__device__ __forceinline__ uint32_t take_ticket(uint32_t* ctr) {
+  return __builtin_amdgcn_atomic_inc32(ctr, 0xFFFFFFFFu, __ATOMIC_RELAXED, "agent");
+}   // the stage of a GEMM2 block that passes the barrier of the GEMM1 block before it
 
 // GEMM2 of chunks 6 and 7 as one 32-stage block: stage s -> (tile, chunk).  Chunk 7 starts
 // at stage 3 (its T is rounded during stages 1 and 2) and the accumulation-register tiles
@@ -202,7 +218,13 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_wide2t_kernel(Problem pb, Bu
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, g = lane >> 4;
-  const int64_t stride = gridDim.x;
+  // The workgroup's first two slices (tickets of the slice counter; one thread takes them and
+  // they reach every wave through xs[1], which is free until the first GEMM1 block)
+  uint32_t tk0 = 0, tk1 = 0;
+  if (tid == 0) {
+    tk0 = take_ticket(b.ctr);
+    tk1 = take_ticket(b.ctr);
+  }
 
   // ---- P1 -> LDS fragments: P1[i, m] -> frag1[(it*8 + ch)*64 + 16*gg + i%16] element t,
   // m = 32ch + (t < 4 ? 4gg + t : 16 + 4gg + t - 4): GEMM1's accumulator rows are GEMM2's
@@ -244,18 +266,20 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_wide2t_kernel(Problem pb, Bu
     }
   p2f_fence(p2f);
 
-  // Chunk j of the workgroup: slice blockIdx.x + (j / 8) * gridDim.x, x rows 32 * (j % 8) ..
+  // Chunk cc of a slice: x rows 32cc .. 32cc+31.
   // Load h of wave w covers chunk rows 8h + 4(w/2) .. +3, slots 16(w%2) .. +15: lane l takes
   // row + (l % 4), slot + l / 4.  Bounded buffer loads (zeros past K, no memory access):
   // unconditional, so the compiler's memory-counter waits cover exactly the chunk consumed.
   u32x4_t xr[D][XR];
   const int ld_off = ((4 * (w >> 1) + (lane & 3)) * 32 + 16 * (w & 1) + (lane >> 2)) * 16;
-  auto load_chunk = [&](int64_t j, u32x4_t* r) {
-    const int64_t slice = blockIdx.x + (j >> 3) * stride;
+  auto chunk_rsrc = [&](int64_t slice, int cc) {
     const bool in = slice < pb.K;
-    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(b.x + (in ? slice : 0) * (kW * kW) + (j & 7) * (kChunk * kW)),
+    return __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(b.x + (in ? slice : 0) * (kW * kW) + cc * (kChunk * kW)),
         static_cast<int16_t>(0), in ? kChunk * kW * 2 : 0, kBufferWord3);
+  };
+  auto load_chunk = [&](int64_t slice, int cc, u32x4_t* r) {
+    const auto rsrc = chunk_rsrc(slice, cc);
 #pragma unroll
     for (int h = 0; h < XR; ++h) r[h] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, ld_off, h * 8 * kW * 2, 0);
   };
@@ -266,13 +290,6 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_wide2t_kernel(Problem pb, Bu
 #pragma unroll
     for (int h = 0; h < XR; ++h) dst[((h & 1) ? st_odd : st_even) + (h >> 1) * 64] = r[h];
   };
-  auto chunk_rsrc = [&](int64_t j) {
-    const int64_t slice = blockIdx.x + (j >> 3) * stride;
-    const bool in = slice < pb.K;
-    return __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(b.x + (in ? slice : 0) * (kW * kW) + (j & 7) * (kChunk * kW)),
-        static_cast<int16_t>(0), in ? kChunk * kW * 2 : 0, kBufferWord3);
-  };
   auto load_piece = [&](const auto& rsrc, int h, u32x4_t& r) {
     r = __builtin_amdgcn_raw_buffer_load_b128(rsrc, ld_off, h * 8 * kW * 2, 0);
   };
@@ -282,8 +299,20 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_wide2t_kernel(Problem pb, Bu
   int f1_lo = lane, f1_hi = lane + kIT / 2 * kNChunk * 64;
   asm volatile("" : "+v"(rd_base), "+v"(f1_lo), "+v"(f1_hi));
 
-  int64_t s = blockIdx.x;
+  // the current and the next slice (wave-uniform)
+  int64_t s = 0, s_nx = 0;
+  {
+    uint32_t* slot = reinterpret_cast<uint32_t*>(xs[1]);
+    if (tid == 0) {
+      slot[0] = tk0;
+      slot[1] = tk1;
+    }
+    lds_barrier();
+    s = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(slot[0]));
+    s_nx = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(slot[1]));
+  }
   if (s >= pb.K) return;
+  uint32_t tk2 = 0;  // the ticket of the slice after the next one (thread 0)
 
   f32x4_t y[kIT][kNT];
   f32x4_t acc[2 * kNT];
@@ -311,16 +340,16 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_wide2t_kernel(Problem pb, Bu
     }
   };
 
-  // One GEMM1 block for chunk j of the workgroup (chunk cj = j % 8 of its slice).  During
-  // stages 2, 5, 8 and 11 chunk j + 1 goes from registers to LDS, a quarter at a time, and
-  // the registers each quarter frees are refilled with chunk j + 1 + D.  TAIL: T is rounded
+  // One GEMM1 block for chunk cj of the current slice.  During stages 2, 5, 8 and 11 chunk
+  // cj + 1 goes from registers to LDS, a quarter at a time, and the registers each quarter
+  // frees are refilled with chunk cj + 1 + D (of the next slice from 8 on).  TAIL: T is rounded
   // into tb[cj & 1] and a barrier ends the block (the next block is GEMM1 too and needs the
   // accumulators); otherwise the GEMM2 block after it does both (g2_tail).  The barrier makes
   // chunk j + 1 visible and releases the buffer this block read.  VIS(k, nt) runs VALU work
   // after each product.  NEXT_G2 / NEXT_CH: the block after this one (its first P fragments
   // are read during this block's last stages, unless it is the GEMM1 block of chunk j + 1,
   // whose chunk is visible only after this block's barrier).
-  auto g1_block = [&](int64_t j, auto cjv, auto carry_inv, auto tailv, auto next_g2v, auto next_chv, auto&& vis) {
+  auto g1_block = [&](auto cjv, auto carry_inv, auto tailv, auto next_g2v, auto next_chv, auto&& vis) {
     constexpr int cj = decltype(cjv)::value;
     constexpr bool carry_in = decltype(carry_inv)::value;
     constexpr bool tail = decltype(tailv)::value;
@@ -332,7 +361,8 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_wide2t_kernel(Problem pb, Bu
       read_g1(buf, 1, 1);
       read_g1(buf, 2, 2);
     }
-    const auto rs_x = chunk_rsrc(j + 1 + D);
+    constexpr int ld_ch = cj + 1 + D;
+    const auto rs_x = chunk_rsrc(ld_ch < kNChunk ? s : s_nx, ld_ch % kNChunk);
     __builtin_amdgcn_sched_barrier(0);
     static_for<0, 16>([&](auto kv) {
       constexpr int k = decltype(kv)::value;
@@ -572,7 +602,6 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_wide2t_kernel(Problem pb, Bu
   using I1 = std::integral_constant<int, 1>;
   auto nothing = [](auto, auto) {};
   auto nothing1 = [](auto) {};
-  int64_t j0 = 0;  // chunk index of the current slice's chunk 0
 
   // y starts at zero: the first slice's GEMM2 block of chunk 0 runs code steps of a slice
   // that does not exist (stored nowhere) over it
@@ -583,20 +612,22 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_wide2t_kernel(Problem pb, Bu
   redefine_a_tiles(y);
 
   // prologue: chunk 0 in LDS, chunks 1 .. D in registers (chunk k in xr[k % D])
-  load_chunk(0, xr[0]);
+  load_chunk(s, 0, xr[0]);
   store_chunk(xr[0], xs[0]);
 #pragma unroll
   for (int k = 1; k <= D; ++k) {
     __builtin_amdgcn_sched_barrier(0);
-    load_chunk(k, xr[k % D]);
+    load_chunk(s, k, xr[k % D]);
   }
   __builtin_amdgcn_sched_barrier(0);
   lds_barrier();
   // the first slice's GEMM1 of chunks 0 and 1 (nothing to encode yet)
-  g1_block(j0 + 0, I0{}, F{}, T{}, F{}, I0{}, nothing);
-  g1_block(j0 + 1, I1{}, F{}, F{}, T{}, I0{}, nothing);
+  g1_block(I0{}, F{}, T{}, F{}, I0{}, nothing);
+  g1_block(I1{}, F{}, F{}, T{}, I0{}, nothing);
 
   while (true) {
+    // the ticket of the slice after the next one, published with this slice's max reduction
+    if (tid == 0) tk2 = take_ticket(b.ctr);
     // ---- slice s: G2(0) G1(2) G2(1) G1(3) ... G2(5) G1(7) G2(6+7); each GEMM2 block ends
     // the GEMM1 block before it; G2(0) also runs the last code steps of the previous slice ----
     g2_block(I0{}, T{}, I0{}, I0{}, [&](auto tv) { g2_tail_pre(tv, I1{}, std::integral_constant<int, kBarStage>{}); },
@@ -604,7 +635,7 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_wide2t_kernel(Problem pb, Bu
                g2_tail_post(tv, ntv, I1{});
                enc_at(std::integral_constant<int, 128 + kNT * decltype(tv)::value + decltype(ntv)::value>{});
              });
-    g1_block(j0 + 2, std::integral_constant<int, 2>{}, T{}, F{}, T{}, I1{}, nothing);
+    g1_block(std::integral_constant<int, 2>{}, T{}, F{}, T{}, I1{}, nothing);
     static_for<1, 6>([&](auto cv) {
       constexpr int c = decltype(cv)::value;
       // G2(c) ends G1(c + 1) (tb[(c + 1) & 1]); then G1(c + 2), ahead of G2(c + 1)
@@ -613,40 +644,47 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_wide2t_kernel(Problem pb, Bu
                  g2_tail_pre(tv, std::integral_constant<int, (c + 1) & 1>{}, std::integral_constant<int, kBarStage>{});
                },
                [&](auto tv, auto ntv) { g2_tail_post(tv, ntv, std::integral_constant<int, (c + 1) & 1>{}); });
-      g1_block(j0 + c + 2, std::integral_constant<int, c + 2>{}, T{}, F{}, T{}, std::integral_constant<int, c + 1>{},
-               nothing);
+      g1_block(std::integral_constant<int, c + 2>{}, T{}, F{}, T{}, std::integral_constant<int, c + 1>{}, nothing);
     });
     m67_block();
 
     // ---- [FQV2] 第3步 pertoken: max|y| over the slice (4 waves).  The partial maxima pass
-    // through xs[1]: its last reader, GEMM1 of chunk 7, is behind the merged block's barrier,
-    // and its next writer, G1'(0), starts after the second barrier below. ----
+    // through xs[1] (and with them the ticket of the slice after the next one): its last
+    // reader, GEMM1 of chunk 7, is behind the merged block's barrier, and its next writer,
+    // G1'(0), starts after the second barrier below. ----
+    int64_t s_nx2 = 0;
     {
       float* red = reinterpret_cast<float*>(xs[1]);
       red[w] = wave_max(fmaxf(am[0], am[1]));  // every lane writes the same value
+      if (tid == 0) reinterpret_cast<uint32_t*>(red)[4] = tk2;
       lds_barrier();
       amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+      s_nx2 = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(reinterpret_cast<const uint32_t*>(red)[4]));
       lds_barrier();
       am[0] = 0.0f;
       am[1] = 0.0f;
     }
     sp = s;
-    s += stride;
-    j0 += kNChunk;
+    s = s_nx;
+    s_nx = s_nx2;
 
     // ---- the next slice's GEMM1 of chunks 0 and 1 (zeros past K), with slice sp's scale and
     // its first code steps ----
     redefine_a_tiles(y);
-    g1_block(j0 + 0, I0{}, T{}, T{}, F{}, I0{}, [&](auto kv, auto ntv) {
+    g1_block(I0{}, T{}, T{}, F{}, I0{}, [&](auto kv, auto ntv) {
       enc_at(std::integral_constant<int, kNT * decltype(kv)::value + decltype(ntv)::value>{});
     });
-    g1_block(j0 + 1, I1{}, F{}, F{}, T{}, I0{}, [&](auto kv, auto ntv) {
+    g1_block(I1{}, F{}, F{}, T{}, I0{}, [&](auto kv, auto ntv) {
       enc_at(std::integral_constant<int, 64 + kNT * decltype(kv)::value + decltype(ntv)::value>{});
     });
     if (s >= pb.K) break;
   }
   // the last slice's remaining code steps (no GEMM2 block follows)
   static_for<128, 192>([&](auto posv) { enc_at(posv); });
+}
+
+__global__ void zero_counter(uint32_t* ctr) {
+  if (threadIdx.x == 0) *ctr = 0u;
 }
 
 }  // namespace
@@ -657,6 +695,7 @@ bool mfma_wide2t_supports(const Problem& pb) {
 
 hipError_t launch_mfma_wide2t(const Problem& pb, const Buffers& b, hipStream_t s) {
   if (!mfma_wide2t_supports(pb)) return hipErrorNotSupported;
+  if (!b.ctr) return hipErrorInvalidValue;
   static int cus = 0;
   if (cus == 0) {
     int dev = 0;
@@ -665,6 +704,8 @@ hipError_t launch_mfma_wide2t(const Problem& pb, const Buffers& b, hipStream_t s
     if (e != hipSuccess) return e;
   }
   const int grid = static_cast<int>(pb.K < cus ? pb.K : cus);
+  // the slice counter starts from zero (a kernel, not a memset: the launch may be captured)
+  zero_counter<<<1, 64, 0, s>>>(b.ctr);
   // the int4 clamp can only bite when (7/clipRatio) * (1 + 4 ulp) reaches 7.5
   const bool clamp = pb.d >= 7.4999f;
   if (pb.dtype == kBF16) {

@@ -112,9 +112,12 @@ typedef struct fq_executor fq_executor; /* opaque, owned by the library */
  *   dstTypeMax  0.0 or in [6.0, 12.0]; used by the FLOAT4_E2M1 mode only; 0.0 is V1.
  * Checks run in this order: NULL pointers (FQ_ERR_PARAM_NULLPTR), then clipRatio and
  * the ranges of x's dimensions, then dtypes, shapes and dstTypeMax
- * (FQ_ERR_PARAM_INVALID).  On success *workspaceSize holds the bytes fq_run needs (0
- * when every tensor is contiguous) and *executor a new executor.  On failure no
- * executor is created.  Host only: makes no HIP call and may run without a GPU. */
+ * (FQ_ERR_PARAM_INVALID).  On success *workspaceSize holds the bytes fq_run needs and
+ * *executor a new executor: the staged copies of non-contiguous tensors, plus 256 bytes
+ * for a slice counter when the pipelined 256 x 256 kernel (variant 4: both transforms,
+ * int4 per-token codes) can run the call; 0 when every tensor is contiguous and that kernel
+ * does not apply.  On failure no executor is created.  Host only: makes no HIP call and
+ * may run without a GPU. */
 fq_status fq_get_workspace_size(const fq_tensor* x, const fq_tensor* kroneckerP1,
                                 const fq_tensor* kroneckerP2, double clipRatio, double dstTypeMax,
                                 const fq_tensor* out, const fq_tensor* quantScale,
@@ -131,7 +134,9 @@ fq_status fq_v1_get_workspace_size(const fq_tensor* x, const fq_tensor* kronecke
 /* ---- second stage ------------------------------------------------------------------
  * Enqueues the fused computation on `stream` (0 = the null stream) and returns without
  * synchronizing.  `workspace` is device memory of at least workspaceSize bytes (may be
- * NULL when the planned size is 0).  By default the executor is single-use: fq_run
+ * NULL when the planned size is 0); its contents need not be initialised (fq_run sets
+ * what it reads, on the stream), and work enqueued with one workspace must not overlap in
+ * time with other work using the same bytes.  By default the executor is single-use: fq_run
  * releases it, whether it succeeds or fails.  A repeatable executor
  * (fq_executor_set_repeatable) survives and must be released with fq_executor_destroy.
  * Results are deterministic: the same inputs give the same bits on every run.

@@ -72,6 +72,15 @@ def test_valid_plans_have_zero_workspace(mode):
     assert (st, ws) == (OK, 0)
 
 
+@pytest.mark.parametrize("mode,p2_empty,ws", [("int32", False, 256), ("int4", False, 256), ("fp4", False, 0),
+                                              ("fp4", True, 0), ("int8", False, 0)])
+def test_pipelined_kernel_plans_a_slice_counter(mode, p2_empty, ws):
+    """At M = N = 256 with both transforms and int4 per-token codes the pipelined kernel
+    hands out slices at run time from a counter in the workspace (256 bytes); the other
+    256 x 256 plans keep a zero workspace."""
+    assert plan(problem(40, 256, 256, mode=mode, p2_empty=p2_empty)) == (OK, ws)
+
+
 def test_example_problem_from_page_plans():
     # fp16 x [16,16,16], P [16,16], out INT32 [16,16,2], scale [16], clip 1.0, dstTypeMax 0.0
     assert plan(problem(16, 16, 16, fq.DT_FLOAT16, "int32")) == (OK, 0)

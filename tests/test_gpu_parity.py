@@ -118,6 +118,35 @@ def test_k_ragged_whole_workgroup_kernels(key):
         assert rep["ok"], rep["errors"]
 
 
+@pytest.mark.parametrize("K", [1, 255, 256, 257, 700, 32768])
+def test_pipelined_kernel_writes_every_slice(K):
+    """The pipelined 256 x 256 kernel hands out slices at run time from a counter in the
+    workspace (zeroed by the library before each launch): on two runs of one executor, with
+    the workspace filled with 0xFF bytes first and the outputs with a marker before each
+    run, every slice's scale and codes are written, and they equal those of the two-sided
+    256-class kernel, which walks a fixed share of the slices per workgroup."""
+    w = synth.WORKLOADS["c4"]
+    say(f"[gpu] pipelined kernel, every slice, K={K}")
+    x, p1, p2 = synth.make_inputs(w, 0, K)
+    xd, p1d, p2d = to_dev(x, w.dtype), to_dev(p1, w.dtype), to_dev(p2, w.dtype)
+    ref = fetch(*run_lib(xd, p1d, p2d, w.mode, w.clip_ratio, w.dst_type_max, fq.KERNEL_MFMA_WIDE), w.mode, K)
+    out, sc = fq.empty_outputs(K, w.M, w.N, w.mode, DEV)
+    ex = fq.Executor(xd, p1d, p2d, out, sc, w.mode, w.clip_ratio, w.dst_type_max, kernel=fq.KERNEL_MFMA_WIDE_T)
+    assert ex.kernel == fq.KERNEL_MFMA_WIDE_T and ex.workspace_size > 0
+    ex.workspace.fill_(0xFF)
+    for run in range(2):
+        out.view(torch.uint8).fill_(0xEE)
+        sc.fill_(float("nan"))
+        ex.run()
+        torch.cuda.synchronize()
+        packed, scale = fetch(out, sc, w.mode, K)
+        assert not np.isnan(scale).any(), f"run {run}: {int(np.isnan(scale).sum())} slices without a scale"
+        unwritten = int((packed == 0xEE).all(axis=1).sum())
+        assert unwritten == 0, f"run {run}: {unwritten} slices without codes"
+        assert np.array_equal(packed, ref[0]) and np.array_equal(scale, ref[1]), f"run {run}"
+    ex.destroy()
+
+
 def test_zero_input_gives_zero_scale_and_codes():
     for mode, dmax in (("int32", 0.0), ("fp4", 0.0), ("fp4", 8.0)):
         x = np.zeros((4, 64, 64), np.uint16)
