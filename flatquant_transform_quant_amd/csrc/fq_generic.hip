@@ -70,6 +70,11 @@ __global__ __launch_bounds__(kGenericThreads) void generic_kernel(Problem pb, Bu
     if (mine < k_end && tiny_scale(static_cast<const float*>(b.scale)[mine]))
       atomicOr(&flags[tid >> 5], 1u << (tid & 31));
     __syncthreads();
+    // none flagged (the usual case): the workgroup is done
+    uint32_t any = 0;
+#pragma unroll
+    for (int i = 0; i < kGenericThreads / 32; ++i) any |= flags[i];
+    if (any == 0u) return;
   }
   for (int64_t k = k_begin; k < k_end; k += k_step) {
     if constexpr (FIXUP) {
