@@ -1,6 +1,9 @@
 // Small-slice MFMA kernel: one wave per slice x_k [M, N] for M in {16, 32, 64, 128},
 // N in {32, 64, 128}, M*N <= 8192, both modes, both dtypes; and N = 16 for the int4 per-token
 // codes (GEMM1's contraction padded to 32 with zero columns of x and zero rows of P2).
+// Per token, above 4096 elements a slice's y (M*N/64 fp32 a lane) and two slices of x in
+// flight need more registers than two waves per SIMD have: those shapes run one wave per
+// SIMD.
 //
 // [FQV2] 拆开算 第1步/第2步 on the matrix cores, fused with 第3步/第4步:
 //   GEMM1  T = x_k . P2   A = x rows (straight from HBM, 16 B per lane),
@@ -36,7 +39,13 @@ namespace {
 // extra slice every wave queues at the start delays every wave's first slice).
 template <int M, int N, bool PG>
 constexpr int prefetch_depth() {
-  return (M * N < 4096) ? 2 : 1;
+  return (M * N < 4096 || (!PG && M * N > 4096)) ? 2 : 1;
+}
+
+// Per-token slices above 4096 elements: one wave per SIMD (512 registers a wave).
+template <int M, int N, bool PG>
+constexpr bool one_wave_per_simd() {
+  return !PG && M * N > 4096;
 }
 
 // Waves per workgroup: 8 from 4096 elements up (one workgroup per CU, so the CU stages
@@ -52,8 +61,10 @@ constexpr int small_waves() {
 template <int DT, int M, int N, bool PG, bool CLAMP, int SV, int Q>
 // (The second launch bound is HIP's minimum of waves per SIMD: 2 keeps the 4-wave variants
 // to 256 registers, the budget they were written for, also where one wave per SIMD is
-// launched; an 8-wave workgroup already puts two on each SIMD.)
-__global__ __launch_bounds__((64 * small_waves<M, N, PG>()), (small_waves<M, N, PG>() == 8 ? 1 : 2)) void mfma_small_kernel(
+// launched; an 8-wave workgroup already puts two on each SIMD; the large per-token slices
+// take 512.)
+__global__ __launch_bounds__((64 * small_waves<M, N, PG>()),
+                             ((small_waves<M, N, PG>() == 8 || one_wave_per_simd<M, N, PG>()) ? 1 : 2)) void mfma_small_kernel(
     Problem pb, Buffers b) {
   constexpr int kSmallWaves = small_waves<M, N, PG>();
   constexpr int kSmallThreads = 64 * kSmallWaves;
@@ -407,8 +418,7 @@ hipError_t dispatch_clamp(const Problem& pb, const Buffers& b, hipStream_t s) {
 template <int DT, int M, int N>
 hipError_t dispatch_mode(const Problem& pb, const Buffers& b, hipStream_t s) {
   if (pb.mode == kPerGroupFp4) return dispatch_clamp<DT, M, N, true>(pb, b, s);
-  if constexpr (M * N <= 4096) return dispatch_clamp<DT, M, N, false>(pb, b, s);
-  return hipErrorNotSupported;
+  return dispatch_clamp<DT, M, N, false>(pb, b, s);
 }
 
 template <int DT, int M>
@@ -446,8 +456,7 @@ bool mfma_small_supports(const Problem& pb) {
   const bool n_ok = pb.N == 32 || pb.N == 64 || pb.N == 128 ||
                     (pb.N == 16 && (pb.mode == kPerTokenInt32 || pb.mode == kPerTokenInt4));
   // registers: the per-token path keeps all of y (M*N/64 fp32 per lane)
-  const int64_t cap = pb.mode == kPerGroupFp4 ? 8192 : 4096;
-  return m_ok && n_ok && pb.M * pb.N <= cap;
+  return m_ok && n_ok && pb.M * pb.N <= 8192;
 }
 
 hipError_t launch_mfma_small(const Problem& pb, const Buffers& b, hipStream_t s) {

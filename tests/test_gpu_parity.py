@@ -46,6 +46,7 @@ EDGE_PER_TOKEN = [  # (M, N, mode)
     (1, 2, "int4"), (3, 2, "int4"), (17, 34, "int4"), (33, 30, "int4"), (64, 128, "int4"),
     (255, 254, "int4"), (256, 256, "int4"), (128, 256, "int4"),
     (32, 16, "int4"), (64, 16, "int32"), (128, 16, "int4"),  # N = 16 on the small MFMA kernel
+    (128, 64, "int32"),  # with (64, 128): one wave per SIMD on the small MFMA kernel
 ]
 
 
