@@ -1,9 +1,10 @@
 // Small-slice MFMA kernel: one wave per slice x_k [M, N] for M in {16, 32, 64, 128},
-// N in {32, 64, 128}, M*N <= 8192, both modes, both dtypes; and N = 16 for the int4 per-token
-// codes (GEMM1's contraction padded to 32 with zero columns of x and zero rows of P2).
-// Per token, above 4096 elements a slice's y (M*N/64 fp32 a lane) and two slices of x in
-// flight need more registers than two waves per SIMD have: those shapes run one wave per
-// SIMD.
+// N in {32, 64, 128}, M*N <= 8192 per token and up to 128 x 128 per group, both dtypes; and
+// N = 16 for the int4 per-token codes (GEMM1's contraction padded to 32 with zero columns
+// of x and zero rows of P2).  Per token above 4096 elements (a slice's y, M*N/64 fp32 a
+// lane, with two slices of x in flight) and per group above 8192 (x and T of a slice, M*N/32
+// registers each) the registers of two waves per SIMD do not suffice: those shapes run one
+// wave per SIMD.
 //
 // [FQV2] 拆开算 第1步/第2步 on the matrix cores, fused with 第3步/第4步:
 //   GEMM1  T = x_k . P2   A = x rows (straight from HBM, 16 B per lane),
@@ -31,22 +32,24 @@
 namespace fq {
 namespace {
 
+// One wave per SIMD (512 registers a wave): per-token slices above 4096 elements, per-group
+// ones above 8192.
+template <int M, int N, bool PG>
+constexpr bool one_wave_per_simd() {
+  return M * N > (PG ? 8192 : 4096);
+}
+
 // Slices of x kept in flight per wave: two for slices under 4096 elements (the loads of
 // the slice two ahead are issued as soon as the current one's first product has consumed
-// its registers), one from 4096 up.  At 4096 elements one slice in flight in each of two
+// its registers) and where one wave runs per SIMD, one otherwise.  At 4096 elements one slice in flight in each of two
 // waves per SIMD beats two slices in flight in one wave per SIMD by 4-5% (while one wave
 // waits for its x the other computes); three slices in flight measured slower still (the
 // extra slice every wave queues at the start delays every wave's first slice).
 template <int M, int N, bool PG>
 constexpr int prefetch_depth() {
-  return (M * N < 4096 || (!PG && M * N > 4096)) ? 2 : 1;
+  return (M * N < 4096 || one_wave_per_simd<M, N, PG>()) ? 2 : 1;
 }
 
-// Per-token slices above 4096 elements: one wave per SIMD (512 registers a wave).
-template <int M, int N, bool PG>
-constexpr bool one_wave_per_simd() {
-  return !PG && M * N > 4096;
-}
 
 // Waves per workgroup: 8 from 4096 elements up (one workgroup per CU, so the CU stages
 // its P fragments once: 6-9% faster at M=64, N=128 than two 4-wave workgroups), 4 for the
@@ -418,7 +421,8 @@ hipError_t dispatch_clamp(const Problem& pb, const Buffers& b, hipStream_t s) {
 template <int DT, int M, int N>
 hipError_t dispatch_mode(const Problem& pb, const Buffers& b, hipStream_t s) {
   if (pb.mode == kPerGroupFp4) return dispatch_clamp<DT, M, N, true>(pb, b, s);
-  return dispatch_clamp<DT, M, N, false>(pb, b, s);
+  if constexpr (M * N <= 8192) return dispatch_clamp<DT, M, N, false>(pb, b, s);
+  return hipErrorNotSupported;
 }
 
 template <int DT, int M>
@@ -430,8 +434,7 @@ hipError_t dispatch_n(const Problem& pb, const Buffers& b, hipStream_t s) {
     case 32: return dispatch_mode<DT, M, 32>(pb, b, s);
     case 64: return dispatch_mode<DT, M, 64>(pb, b, s);
     case 128:
-      if constexpr (M * 128 <= 8192) return dispatch_mode<DT, M, 128>(pb, b, s);
-      break;
+      return dispatch_mode<DT, M, 128>(pb, b, s);
   }
   return hipErrorNotSupported;
 }
@@ -456,7 +459,7 @@ bool mfma_small_supports(const Problem& pb) {
   const bool n_ok = pb.N == 32 || pb.N == 64 || pb.N == 128 ||
                     (pb.N == 16 && (pb.mode == kPerTokenInt32 || pb.mode == kPerTokenInt4));
   // registers: the per-token path keeps all of y (M*N/64 fp32 per lane)
-  return m_ok && n_ok && pb.M * pb.N <= 8192;
+  return m_ok && n_ok && (pb.mode == kPerGroupFp4 || pb.M * pb.N <= 8192);
 }
 
 hipError_t launch_mfma_small(const Problem& pb, const Buffers& b, hipStream_t s) {

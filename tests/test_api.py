@@ -82,12 +82,12 @@ def test_pipelined_kernel_plans_a_slice_counter(mode, p2_empty, ws):
 
 
 @pytest.mark.parametrize("M,N,mode,kernel", [(64, 64, "int32", 2), (64, 128, "int4", 2), (128, 64, "int32", 2),
-                                            (64, 128, "int8", 2), (128, 128, "int32", 1), (128, 128, "fp4", 1),
-                                            (64, 128, "fp4", 2), (86, 128, "int4", 1)])
+                                            (64, 128, "int8", 2), (128, 128, "int32", 1), (128, 128, "fp4", 2),
+                                            (64, 128, "fp4", 2), (86, 128, "int4", 1), (128, 256, "fp4", 1)])
 def test_automatic_kernel_by_shape(M, N, mode, kernel):
     """The one-wave-per-slice MFMA kernel takes per-token slices up to 8192 elements (one
-    wave per SIMD above 4096) and per-group ones up to 8192; other shapes below 256 x 256
-    take the generic kernel."""
+    wave per SIMD above 4096) and per-group ones up to 128 x 128 (one wave per SIMD above
+    8192); other shapes below 256 x 256 take the generic kernel."""
     st, ws, ex = fq.fq_get_workspace_size(*[problem(3, M, N, mode=mode)[k] for k in ("x", "p1", "p2")], 1.0, 0.0,
                                           problem(3, M, N, mode=mode)["out"], problem(3, M, N, mode=mode)["sc"])
     assert st == OK

@@ -66,6 +66,7 @@ EDGE_PER_GROUP = [  # (M, N, two_sided, dmax)
     (17, 18, True, 0.0), (16, 16, True, 0.0), (32, 32, False, 8.0), (64, 128, True, 0.0),
     (64, 128, False, 10.0), (128, 64, True, 12.0), (255, 254, True, 6.0), (256, 256, True, 0.0),
     (256, 256, False, 8.0), (1, 256, False, 0.0), (256, 2, False, 7.0),
+    (128, 128, True, 0.0), (128, 128, False, 8.0),  # one wave per SIMD on the small MFMA kernel
 ]
 
 
