@@ -4,6 +4,10 @@
 //   P1[i, m]  -> frag1[(it*KS2 + ks2)*64 + 16*g + i%16], element t, where m = 32ks2 + w and
 //                w = 4g + t (t < 4) or 16 + 4g + (t - 4) (t >= 4); columns past M are zero
 //
+// With PAD the transforms are smaller than the fragments (M x M and N x N are the padded
+// sizes, the problem's own are pb.M and pb.N, N a multiple of 8): rows and columns past
+// them are zero, so the padded products equal the real ones on the real rows and columns.
+//
 // P2's layout makes it GEMM1's B operand with output column R*c + nt in lane c of n-tile
 // nt; P1's relabels the contraction index m so that GEMM1's accumulator registers are
 // GEMM2's B operand as they stand (a lane's two 4-row accumulator blocks are its 8
@@ -14,7 +18,7 @@
 
 namespace fq {
 
-template <int DT, int M, int N, int THREADS>
+template <int DT, int M, int N, int THREADS, bool PAD = false>
 struct PStage {
   static constexpr int MT = M / 16, NT = N / 16, R = N / 16, KS1 = (N + 31) / 32, KS2 = (M + 31) / 32;
   static constexpr int FRAG2 = KS1 * NT * 64, FRAG1 = MT * KS2 * 64;  // u32x4 slots
@@ -34,26 +38,50 @@ struct PStage {
   // is conditional.
   __device__ __forceinline__ void issue(const Problem& pb, const Buffers& b, int tid) {
     issue_p2(pb, b, tid);
-    issue_p1(b, tid);
+    issue_p1(pb, b, tid);
   }
   __device__ __forceinline__ void issue_p2(const Problem& pb, const Buffers& b, int tid) {
     // the staging's own copy of the thread index: its lane arithmetic is not shared with
     // (and kept live for) the kernel's slice loop
     asm volatile("" : "+v"(tid));
     const bool two = pb.two_sided != 0;
+    const int Nr = PAD ? static_cast<int>(pb.N) : N;  // P2's own size (a multiple of 8 with PAD)
     const auto rs2 = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(two ? b.p2 : b.p1),
-                                                      static_cast<int16_t>(0), two ? N * N * 2 : 0, kBufferWord3);
+                                                      static_cast<int16_t>(0), two ? Nr * Nr * 2 : 0, kBufferWord3);
 #pragma unroll
     for (int q = 0; q < L2; ++q) {
       const int blk = tid + q * THREADS;
       const int rb = blk / (N / 8), cb = blk % (N / 8);  // rows 8rb .. +7, columns 8cb .. +7
-      const int off = blk < B2 ? ((8 * rb) * N + 8 * cb) * 2 : N * N * 2;  // past the end: zeros
+      const bool in = blk < B2 && (!PAD || (8 * rb < Nr && 8 * cb < Nr));
+      const int off = in ? ((8 * rb) * Nr + 8 * cb) * 2 : Nr * Nr * 2;  // past the end: zeros
 #pragma unroll
-      for (int t = 0; t < 8; ++t) r2[q][t] = __builtin_amdgcn_raw_buffer_load_b128(rs2, off + t * N * 2, 0, 0);
+      for (int t = 0; t < 8; ++t) r2[q][t] = __builtin_amdgcn_raw_buffer_load_b128(rs2, off + t * Nr * 2, 0, 0);
     }
   }
-  __device__ __forceinline__ void issue_p1(const Buffers& b, int tid) {
+  __device__ __forceinline__ void issue_p1(const Problem& pb, const Buffers& b, int tid) {
     asm volatile("" : "+v"(tid));
+    if constexpr (PAD) {
+      // element by element (P1's own size need not be a multiple of 4); zeros past it
+      const int Mr = static_cast<int>(pb.M);
+      const auto rs1 = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(b.p1), static_cast<int16_t>(0),
+                                                        Mr * Mr * 2, kBufferWord3);
+#pragma unroll
+      for (int q = 0; q < L1; ++q) {
+        const int slot = tid + q * THREADS;
+        const int l = slot & 63, f = slot >> 6, it = f / KS2, ks2 = f % KS2;
+        const int i = 16 * it + (l & 15), gg = l >> 4;
+        uint32_t e[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int m = 32 * ks2 + (t < 4 ? 4 * gg + t : 16 + 4 * gg + (t - 4));
+          const bool in = slot < FRAG1 && i < Mr && m < Mr;
+          e[t] = __builtin_amdgcn_raw_buffer_load_b16(rs1, in ? (i * Mr + m) * 2 : Mr * Mr * 2, 0, 0);
+        }
+#pragma unroll
+        for (int p = 0; p < 4; ++p) r1[q][p] = e[2 * p] | (e[2 * p + 1] << 16);
+      }
+      return;
+    }
     const auto rs1 = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(b.p1), static_cast<int16_t>(0),
                                                       M * M * 2, kBufferWord3);
 #pragma unroll

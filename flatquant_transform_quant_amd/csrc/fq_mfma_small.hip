@@ -5,6 +5,12 @@
 // lane, with two slices of x in flight) and per group above 8192 (x and T of a slice, M*N/32
 // registers each) the registers of two waves per SIMD do not suffice: those shapes run one
 // wave per SIMD.
+// PAD (per token): a slice of M x N elements with M <= 128 and N <= 128 a multiple of 8 runs
+// in the instantiation of the next sizes up (16, 32, 64, 128; 32 up for the 8-bit codes):
+// x's rows and columns past the slice's own read zeros through the bounded loads, P1 and P2
+// are staged with zero rows and columns past their own sizes, so the padded y is the real
+// one bordered by zeros (max|y| unchanged), and the codes are staged and stored for the
+// real rows and columns only.
 //
 // [FQV2] 拆开算 第1步/第2步 on the matrix cores, fused with 第3步/第4步:
 //   GEMM1  T = x_k . P2   A = x rows (straight from HBM, 16 B per lane),
@@ -61,7 +67,8 @@ constexpr int small_waves() {
 
 // CLAMP (per token): the int4 or INT8 clamp is compiled in.  SV (per group): the e8m0 rule.  Q (per
 // token): 0 for int4 codes, else the 8-bit mode (kPerTokenInt8 / E4M3 / E5M2), one byte a code.
-template <int DT, int M, int N, bool PG, bool CLAMP, int SV, int Q>
+// PAD: M and N are the padded sizes of a smaller per-token slice (pb.M x pb.N).
+template <int DT, int M, int N, bool PG, bool CLAMP, int SV, int Q, bool PAD>
 // (The second launch bound is HIP's minimum of waves per SIMD: 2 keeps the 4-wave variants
 // to 256 registers, the budget they were written for, also where one wave per SIMD is
 // launched; an 8-wave workgroup already puts two on each SIMD; the large per-token slices
@@ -77,6 +84,9 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()),
   constexpr int MN = M * N;
   constexpr int SPAN = 32 / R;             // lanes per 32-group (per-group mode)
   static_assert(((N % 32 == 0 && R >= 2) || (N == 16 && !PG && Q == 0)) && M % 16 == 0, "unsupported shape");
+  static_assert(!(PAD && PG), "padding is for the per-token modes");
+  // the slice's own sizes (the template's with no padding)
+  const int Mr = PAD ? static_cast<int>(pb.M) : M, Nr = PAD ? static_cast<int>(pb.N) : N;
 
   __shared__ u32x4_t frag2[KS1 * NT * 64];  // B fragments of P2 (or of I)
   __shared__ u32x4_t frag1[MT * KS2 * 64];  // A fragments of P1 (k relabelled)
@@ -107,7 +117,7 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()),
   // x's slice and row strides (M*N and N for a contiguous x; a strided x is read in place)
   const int64_t xs_k = pb.xs_k;
   const int xs_m = static_cast<int>(pb.xs_m);
-  const int x_span = ((M - 1) * xs_m + N) * 2;  // bytes a slice spans
+  const int x_span = ((Mr - 1) * xs_m + Nr) * 2;  // bytes a slice spans
   auto load_x = [&](int buf, int64_t slice) {
     const bool in = slice < pb.K;
     const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(b.x + (in ? slice : 0) * xs_k),
@@ -118,7 +128,10 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()),
 #pragma unroll
       for (int ks = 0; ks < KS1; ++ks)
         xa[buf][mt][ks] = __builtin_amdgcn_raw_buffer_load_b128(
-            rsrc, (N >= 32 || 8 * g < N) ? (c * xs_m + 32 * ks + 8 * g) * 2 : x_span,  // past N: zeros
+            rsrc,
+            ((N >= 32 || 8 * g < N) && (!PAD || (16 * mt + c < Mr && 32 * ks + 8 * g < Nr)))
+                ? (c * xs_m + 32 * ks + 8 * g) * 2
+                : x_span,  // past the slice's rows or columns: zeros
             16 * mt * xs_m * 2, 0);
   };
   // ---- stage P2 / P1 fragments (once per workgroup) ----
@@ -126,7 +139,7 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()),
   // staging waits for P alone (the memory counter completes in issue order) while x is
   // still arriving.
   {
-    PStage<DT, M, N, kSmallThreads> ps;
+    PStage<DT, M, N, kSmallThreads, PAD> ps;
     if constexpr (PF > 1) {
       ps.issue(pb, b, tid);
       __builtin_amdgcn_sched_barrier(0);  // keep the issue order: P, then x
@@ -144,7 +157,7 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()),
       // at 4096 elements: the staging then waits behind it).
       ps.issue_p2(pb, b, tid);
       ps.scatter_p2(pb, frag2, tid);
-      ps.issue_p1(b, tid);
+      ps.issue_p1(pb, b, tid);
       ps.scatter_p1(frag1, tid);
     }
   }
@@ -157,13 +170,21 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()),
   auto flush = [&](int64_t slice) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    u32x4_t* gcodes = reinterpret_cast<u32x4_t*>(b.codes + slice * CODE_BYTES);
+    if constexpr (PAD) {
+      // the slice's own codes, a multiple of 4 bytes (N is a multiple of 8)
+      const int cb = Q ? Mr * Nr : Mr * Nr / 2;
+      uint32_t* g32 = reinterpret_cast<uint32_t*>(b.codes + slice * cb);
+      const uint32_t* s32 = reinterpret_cast<const uint32_t*>(st);
+      for (int q = lane; q < cb / 4; q += 64) __builtin_nontemporal_store(s32[q], &g32[q]);
+    } else {
+      u32x4_t* gcodes = reinterpret_cast<u32x4_t*>(b.codes + slice * CODE_BYTES);
 #pragma unroll
-    // the codes are written once and not read back by this kernel: non-temporal stores
-    for (int q = 0; q < CODE_BYTES / 16 / 64; ++q) __builtin_nontemporal_store(stage[wave][q * 64 + lane], &gcodes[q * 64 + lane]);
-    if constexpr ((CODE_BYTES / 16) % 64 != 0) {
-      constexpr int q = CODE_BYTES / 16 / 64;
-      if (q * 64 + lane < CODE_BYTES / 16) __builtin_nontemporal_store(stage[wave][q * 64 + lane], &gcodes[q * 64 + lane]);
+      // the codes are written once and not read back by this kernel: non-temporal stores
+      for (int q = 0; q < CODE_BYTES / 16 / 64; ++q) __builtin_nontemporal_store(stage[wave][q * 64 + lane], &gcodes[q * 64 + lane]);
+      if constexpr ((CODE_BYTES / 16) % 64 != 0) {
+        constexpr int q = CODE_BYTES / 16 / 64;
+        if (q * 64 + lane < CODE_BYTES / 16) __builtin_nontemporal_store(stage[wave][q * 64 + lane], &gcodes[q * 64 + lane]);
+      }
     }
     if constexpr (PG) {
       const uint32_t* se = reinterpret_cast<const uint32_t*>(st + CODE_BYTES);
@@ -184,7 +205,9 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()),
     // e8m0 byte).  Made opaque per slice so the per-row addresses are formed here, with
     // the row as an immediate offset, instead of being hoisted out of the slice loop and
     // held in registers.
-    int code_off = Q ? 4 * g * N + R * c : 4 * g * (N / 2) + (R >= 2 ? (R / 2) * c : c / 2);
+    // (codes staged as the slice's own rows: NROW elements a row)
+    const int NROW = PAD ? Nr : N;
+    int code_off = Q ? 4 * g * NROW + R * c : 4 * g * (NROW / 2) + (R >= 2 ? (R / 2) * c : c / 2);
     int e8_off = CODE_BYTES + 4 * g * (N / 32) + (R * c) / 32;
     asm volatile("" : "+v"(code_off), "+v"(e8_off));
     // ---- GEMM1: T = x . P2 (fp32), rounded to the dtype and written straight into the
@@ -272,12 +295,14 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()),
                 w[q] = code8x4<Q, CLAMP>(y[it][4 * q][i], y[it][4 * q + 1][i], y[it][4 * q + 2][i],
                                          y[it][4 * q + 3][i], inv);
             }
-            uint8_t* dst = st + code_off + r0 * N;
-            if constexpr (R == 2) {
-              *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(w[0]);
-            } else {
+            uint8_t* dst = st + code_off + r0 * NROW;
+            if (!PAD || (r0 + 4 * g < Mr && R * c < Nr)) {  // the slice's own rows and columns
+              if constexpr (R == 2) {
+                *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(w[0]);
+              } else {
 #pragma unroll
-              for (int q = 0; q < R / 4; ++q) reinterpret_cast<uint32_t*>(dst)[q] = w[q];
+                for (int q = 0; q < R / 4; ++q) reinterpret_cast<uint32_t*>(dst)[q] = w[q];
+              }
             }
           }
       } else {
@@ -298,14 +323,16 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()),
               by[p] = pair_byte(int4_biased<CLAMP>(y[it][2 * p][i], inv),
                                 int4_biased<CLAMP>(y[it][2 * p + 1][i], inv));
           }
-          uint8_t* dst = st + code_off + r0 * (N / 2);
-          if constexpr (R <= 2) {
-            *dst = static_cast<uint8_t>(by[0] ^ 0x88u);
-          } else if constexpr (R == 4) {
-            *reinterpret_cast<uint16_t*>(dst) =
-                static_cast<uint16_t>(unbias(__builtin_amdgcn_perm(by[1], by[0], 0x0C0C0400u)));
-          } else {
-            *reinterpret_cast<uint32_t*>(dst) = unbias(gather4(by[0], by[1], by[2], by[3]));
+          uint8_t* dst = st + code_off + r0 * (NROW / 2);
+          if (!PAD || (r0 + 4 * g < Mr && R * c < Nr)) {  // the slice's own rows and columns
+            if constexpr (R <= 2) {
+              *dst = static_cast<uint8_t>(by[0] ^ 0x88u);
+            } else if constexpr (R == 4) {
+              *reinterpret_cast<uint16_t*>(dst) =
+                  static_cast<uint16_t>(unbias(__builtin_amdgcn_perm(by[1], by[0], 0x0C0C0400u)));
+            } else {
+              *reinterpret_cast<uint32_t*>(dst) = unbias(gather4(by[0], by[1], by[2], by[3]));
+            }
           }
         }
       }
@@ -368,7 +395,7 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()),
     if (s + q * waves < pb.K) process(q, s + q * waves);
 }
 
-template <int DT, int M, int N, bool PG, bool CLAMP, int SV, int Q = 0>
+template <int DT, int M, int N, bool PG, bool CLAMP, int SV, int Q = 0, bool PAD = false>
 hipError_t launch_one(const Problem& pb, const Buffers& b, hipStream_t s) {
   constexpr int kWaves = small_waves<M, N, PG>(), kThreads = 64 * kWaves;
   static int grid_cap = 0;  // workgroups that fit the device at once (per instantiation)
@@ -377,26 +404,26 @@ hipError_t launch_one(const Problem& pb, const Buffers& b, hipStream_t s) {
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e == hipSuccess)
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_small_kernel<DT, M, N, PG, CLAMP, SV, Q>,
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_small_kernel<DT, M, N, PG, CLAMP, SV, Q, PAD>,
                                                        kThreads, 0);
     if (e != hipSuccess) return e;
     grid_cap = cus * (per_cu > 0 ? per_cu : 1);
   }
   const int64_t need = (pb.K + kWaves - 1) / kWaves;
   const int grid = static_cast<int>(need < grid_cap ? need : grid_cap);
-  mfma_small_kernel<DT, M, N, PG, CLAMP, SV, Q><<<grid, kThreads, 0, s>>>(pb, b);
+  mfma_small_kernel<DT, M, N, PG, CLAMP, SV, Q, PAD><<<grid, kThreads, 0, s>>>(pb, b);
   return hipGetLastError();
 }
 
 // int4 per-token codes (INT32 / INT4 out)
-template <int DT, int M, int N>
+template <int DT, int M, int N, bool PAD>
 hipError_t dispatch_int4(const Problem& pb, const Buffers& b, hipStream_t s) {
   // The int4 clamp can only bite when (7/clipRatio) * (1 + 4 ulp) reaches 7.5.
-  if (pb.d >= 7.4999f) return launch_one<DT, M, N, false, true, kE8V1>(pb, b, s);
-  return launch_one<DT, M, N, false, false, kE8V1>(pb, b, s);
+  if (pb.d >= 7.4999f) return launch_one<DT, M, N, false, true, kE8V1, 0, PAD>(pb, b, s);
+  return launch_one<DT, M, N, false, false, kE8V1, 0, PAD>(pb, b, s);
 }
 
-template <int DT, int M, int N, bool PG>
+template <int DT, int M, int N, bool PG, bool PAD>
 hipError_t dispatch_clamp(const Problem& pb, const Buffers& b, hipStream_t s) {
   if constexpr (PG) {
     switch (e8m0_variant(pb)) {
@@ -408,63 +435,84 @@ hipError_t dispatch_clamp(const Problem& pb, const Buffers& b, hipStream_t s) {
     switch (pb.mode) {
       case kPerTokenInt8:
         // The INT8 clamp can only bite when (127/clipRatio) * (1 + 4 ulp) reaches 127.5.
-        if (pb.d >= 127.4999f) return launch_one<DT, M, N, false, true, kE8V1, kPerTokenInt8>(pb, b, s);
-        return launch_one<DT, M, N, false, false, kE8V1, kPerTokenInt8>(pb, b, s);
-      case kPerTokenE4M3: return launch_one<DT, M, N, false, false, kE8V1, kPerTokenE4M3>(pb, b, s);
-      case kPerTokenE5M2: return launch_one<DT, M, N, false, false, kE8V1, kPerTokenE5M2>(pb, b, s);
+        if (pb.d >= 127.4999f) return launch_one<DT, M, N, false, true, kE8V1, kPerTokenInt8, PAD>(pb, b, s);
+        return launch_one<DT, M, N, false, false, kE8V1, kPerTokenInt8, PAD>(pb, b, s);
+      case kPerTokenE4M3: return launch_one<DT, M, N, false, false, kE8V1, kPerTokenE4M3, PAD>(pb, b, s);
+      case kPerTokenE5M2: return launch_one<DT, M, N, false, false, kE8V1, kPerTokenE5M2, PAD>(pb, b, s);
       default: break;
     }
-    return dispatch_int4<DT, M, N>(pb, b, s);
+    return dispatch_int4<DT, M, N, PAD>(pb, b, s);
   }
 }
 
-template <int DT, int M, int N>
+template <int DT, int M, int N, bool PAD>
 hipError_t dispatch_mode(const Problem& pb, const Buffers& b, hipStream_t s) {
-  if (pb.mode == kPerGroupFp4) return dispatch_clamp<DT, M, N, true>(pb, b, s);
-  if constexpr (M * N <= 8192) return dispatch_clamp<DT, M, N, false>(pb, b, s);
+  if constexpr (!PAD) {
+    if (pb.mode == kPerGroupFp4) return dispatch_clamp<DT, M, N, true, false>(pb, b, s);
+  }
+  if constexpr (M * N <= 8192) return dispatch_clamp<DT, M, N, false, PAD>(pb, b, s);
   return hipErrorNotSupported;
 }
 
-template <int DT, int M>
+bool int4_codes(const Problem& pb) { return pb.mode == kPerTokenInt32 || pb.mode == kPerTokenInt4; }
+
+// The sizes an instantiation is chosen by: the slice's own, or with padding the next of
+// 16, 32, 64, 128 (N from 32 for the 8-bit codes, whose layout needs two columns a lane).
+int pad_up(int v) { return v <= 16 ? 16 : v <= 32 ? 32 : v <= 64 ? 64 : 128; }
+int padded_m(const Problem& pb) { return pad_up(static_cast<int>(pb.M)); }
+int padded_n(const Problem& pb) {
+  const int n = pad_up(static_cast<int>(pb.N));
+  return (n == 16 && !int4_codes(pb)) ? 32 : n;
+}
+
+template <int DT, int M, bool PAD>
 hipError_t dispatch_n(const Problem& pb, const Buffers& b, hipStream_t s) {
-  switch (pb.N) {
+  switch (PAD ? padded_n(pb) : static_cast<int>(pb.N)) {
     case 16:
-      if (pb.mode == kPerTokenInt32 || pb.mode == kPerTokenInt4) return dispatch_int4<DT, M, 16>(pb, b, s);
+      if (int4_codes(pb)) return dispatch_int4<DT, M, 16, PAD>(pb, b, s);
       break;
-    case 32: return dispatch_mode<DT, M, 32>(pb, b, s);
-    case 64: return dispatch_mode<DT, M, 64>(pb, b, s);
-    case 128:
-      return dispatch_mode<DT, M, 128>(pb, b, s);
+    case 32: return dispatch_mode<DT, M, 32, PAD>(pb, b, s);
+    case 64: return dispatch_mode<DT, M, 64, PAD>(pb, b, s);
+    case 128: return dispatch_mode<DT, M, 128, PAD>(pb, b, s);
   }
   return hipErrorNotSupported;
 }
 
-template <int DT>
+template <int DT, bool PAD>
 hipError_t dispatch_m(const Problem& pb, const Buffers& b, hipStream_t s) {
-  switch (pb.M) {
-    case 16: return dispatch_n<DT, 16>(pb, b, s);
-    case 32: return dispatch_n<DT, 32>(pb, b, s);
-    case 64: return dispatch_n<DT, 64>(pb, b, s);
-    case 128: return dispatch_n<DT, 128>(pb, b, s);
+  switch (PAD ? padded_m(pb) : static_cast<int>(pb.M)) {
+    case 16: return dispatch_n<DT, 16, PAD>(pb, b, s);
+    case 32: return dispatch_n<DT, 32, PAD>(pb, b, s);
+    case 64: return dispatch_n<DT, 64, PAD>(pb, b, s);
+    case 128: return dispatch_n<DT, 128, PAD>(pb, b, s);
   }
   return hipErrorNotSupported;
 }
 
-}  // namespace
-
-bool mfma_small_supports(const Problem& pb) {
+// Runs at the slice's own sizes (no padding).
+bool exact_shape(const Problem& pb) {
   const bool m_ok = pb.M == 16 || pb.M == 32 || pb.M == 64 || pb.M == 128;
   // N = 16: int4 per-token codes only (one code a lane per row: the 8-bit and per-group
   // layouts are not implemented for it)
-  const bool n_ok = pb.N == 32 || pb.N == 64 || pb.N == 128 ||
-                    (pb.N == 16 && (pb.mode == kPerTokenInt32 || pb.mode == kPerTokenInt4));
+  const bool n_ok = pb.N == 32 || pb.N == 64 || pb.N == 128 || (pb.N == 16 && int4_codes(pb));
   // registers: the per-token path keeps all of y (M*N/64 fp32 per lane)
   return m_ok && n_ok && (pb.mode == kPerGroupFp4 || pb.M * pb.N <= 8192);
 }
 
+// Runs padded: per token, M and N up to 128, N a multiple of 8, padded sizes within 8192.
+bool padded_shape(const Problem& pb) {
+  return pb.mode != kPerGroupFp4 && pb.M >= 1 && pb.M <= 128 && pb.N >= 8 && pb.N <= 128 && pb.N % 8 == 0 &&
+         padded_m(pb) * padded_n(pb) <= 8192;
+}
+
+}  // namespace
+
+bool mfma_small_supports(const Problem& pb) { return exact_shape(pb) || padded_shape(pb); }
+
 hipError_t launch_mfma_small(const Problem& pb, const Buffers& b, hipStream_t s) {
-  if (!mfma_small_supports(pb)) return hipErrorNotSupported;
-  return pb.dtype == kBF16 ? dispatch_m<kBF16>(pb, b, s) : dispatch_m<kF16>(pb, b, s);
+  if (exact_shape(pb)) return pb.dtype == kBF16 ? dispatch_m<kBF16, false>(pb, b, s) : dispatch_m<kF16, false>(pb, b, s);
+  if (padded_shape(pb)) return pb.dtype == kBF16 ? dispatch_m<kBF16, true>(pb, b, s) : dispatch_m<kF16, true>(pb, b, s);
+  return hipErrorNotSupported;
 }
 
 }  // namespace fq

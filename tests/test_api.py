@@ -83,11 +83,15 @@ def test_pipelined_kernel_plans_a_slice_counter(mode, p2_empty, ws):
 
 @pytest.mark.parametrize("M,N,mode,kernel", [(64, 64, "int32", 2), (64, 128, "int4", 2), (128, 64, "int32", 2),
                                             (64, 128, "int8", 2), (128, 128, "int32", 1), (128, 128, "fp4", 2),
-                                            (64, 128, "fp4", 2), (86, 128, "int4", 1), (128, 256, "fp4", 1)])
+                                            (64, 128, "fp4", 2), (86, 128, "int4", 1), (128, 256, "fp4", 1),
+                                            (17, 24, "int32", 2), (86, 64, "int4", 2), (33, 40, "int8", 2),
+                                            (3, 8, "int32", 2), (40, 120, "e5m2", 2), (17, 34, "int4", 1),
+                                            (33, 30, "int4", 1), (129, 64, "int32", 1), (17, 32, "fp4", 1)])
 def test_automatic_kernel_by_shape(M, N, mode, kernel):
     """The one-wave-per-slice MFMA kernel takes per-token slices up to 8192 elements (one
-    wave per SIMD above 4096) and per-group ones up to 128 x 128 (one wave per SIMD above
-    8192); other shapes below 256 x 256 take the generic kernel."""
+    wave per SIMD above 4096), padded to its sizes when M <= 128 and N <= 128 is a multiple
+    of 8, and per-group ones of its sizes up to 128 x 128 (one wave per SIMD above 8192);
+    other shapes below 256 x 256 take the generic kernel."""
     st, ws, ex = fq.fq_get_workspace_size(*[problem(3, M, N, mode=mode)[k] for k in ("x", "p1", "p2")], 1.0, 0.0,
                                           problem(3, M, N, mode=mode)["out"], problem(3, M, N, mode=mode)["sc"])
     assert st == OK
@@ -496,7 +500,8 @@ def test_8bit_strided_output_is_staged_in_the_workspace(mode):
 
 
 def test_8bit_modes_pick_a_kernel_by_shape():
-    for M, N, want in [(64, 64, 2), (32, 128, 2), (256, 256, 3), (48, 40, 1)]:
+    # (48 x 40 runs padded to 64 x 64; N = 36 is not a multiple of 8)
+    for M, N, want in [(64, 64, 2), (32, 128, 2), (256, 256, 3), (48, 40, 2), (48, 36, 1)]:
         p = problem(K=8, M=M, N=N, mode="int8")
         st, ws, ex = fq.fq_get_workspace_size(p["x"], p["p1"], p["p2"], 1.0, 0.0, p["out"], p["sc"])
         assert st == OK

@@ -47,6 +47,7 @@ EDGE_PER_TOKEN = [  # (M, N, mode)
     (255, 254, "int4"), (256, 256, "int4"), (128, 256, "int4"),
     (32, 16, "int4"), (64, 16, "int32"), (128, 16, "int4"),  # N = 16 on the small MFMA kernel
     (128, 64, "int32"),  # with (64, 128): one wave per SIMD on the small MFMA kernel
+    (86, 64, "int4"), (56, 64, "int32"), (40, 120, "int32"), (9, 8, "int4"),  # padded on it
 ]
 
 
@@ -147,6 +148,34 @@ def test_pipelined_kernel_writes_every_slice(K):
         assert unwritten == 0, f"run {run}: {unwritten} slices without codes"
         assert np.array_equal(packed, ref[0]) and np.array_equal(scale, ref[1]), f"run {run}"
     ex.destroy()
+
+
+@pytest.mark.parametrize("M,N,mode,K", [(33, 40, "int4", 1031), (86, 64, "int32", 300), (17, 24, "int8", 517),
+                                         (40, 120, "int4", 257), (3, 8, "int32", 700), (100, 16, "e4m3", 129)])
+def test_padded_shapes_on_the_small_kernel(M, N, mode, K):
+    """Per-token slices of other sizes (M up to 128, N a multiple of 8 up to 128) run the
+    one-wave-per-slice MFMA kernel padded to its next sizes: every slice against the oracle at
+    a K that leaves a ragged last pass (a slice's codes need not be a multiple of 16 bytes),
+    and nothing written outside the outputs (4 KB guard bands around them)."""
+    say(f"[gpu] padded {M}x{N} {mode} K={K}")
+    x, p1, p2 = _inputs(M, N, "bf16", K, seed=M * 1000 + N + 3)
+    xd, p1d, p2d = to_dev(x, "bf16"), to_dev(p1, "bf16"), to_dev(p2, "bf16")
+    assert fq.KERNEL_MFMA_SMALL in supported_kernels(xd, p1d, p2d, mode, 0.9, 0.0)
+    rep = check(x, p1, p2, "bf16", mode, 0.9, 0.0, kernel=fq.KERNEL_MFMA_SMALL, label="padded")
+    assert rep["ok"], rep["errors"]
+    G = 4096
+    ref_out, ref_sc = fq.empty_outputs(K, M, N, mode, DEV)
+    nb_out = ref_out.numel() * ref_out.element_size()
+    nb_sc = ref_sc.numel() * ref_sc.element_size()
+    big_o = torch.full((G + nb_out + G,), 0xA5, dtype=torch.uint8, device=DEV)
+    big_s = torch.full((G + nb_sc + G,), 0x5A, dtype=torch.uint8, device=DEV)
+    out = big_o[G:G + nb_out].view(ref_out.dtype).reshape(ref_out.shape)
+    sc = big_s[G:G + nb_sc].view(ref_sc.dtype).reshape(ref_sc.shape)
+    fq.quantize(xd, p1d, p2d, out, sc, mode, 0.9, 0.0, kernel=fq.KERNEL_MFMA_SMALL)
+    torch.cuda.synchronize()
+    bo, bs = big_o.cpu().numpy(), big_s.cpu().numpy()
+    assert (bo[:G] == 0xA5).all() and (bo[G + nb_out:] == 0xA5).all()
+    assert (bs[:G] == 0x5A).all() and (bs[G + nb_sc:] == 0x5A).all()
 
 
 def test_zero_input_gives_zero_scale_and_codes():
