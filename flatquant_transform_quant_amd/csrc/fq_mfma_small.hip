@@ -5,12 +5,13 @@
 // lane, with two slices of x in flight) and per group above 8192 (x and T of a slice, M*N/32
 // registers each) the registers of two waves per SIMD do not suffice: those shapes run one
 // wave per SIMD.
-// PAD (per token): a slice of M x N elements with M <= 128 and N <= 128 a multiple of 8 runs
-// in the instantiation of the next sizes up (16, 32, 64, 128; 32 up for the 8-bit codes):
-// x's rows and columns past the slice's own read zeros through the bounded loads, P1 and P2
-// are staged with zero rows and columns past their own sizes, so the padded y is the real
-// one bordered by zeros (max|y| unchanged), and the codes are staged and stored for the
-// real rows and columns only.
+// PAD: a per-token slice of M x N elements with M <= 128 and N <= 128 a multiple of 8 runs
+// in the instantiation of the next sizes up (16, 32, 64, 128; 32 up for the 8-bit codes), a
+// per-group one with M <= 128 and N in {32, 64, 128} in that of the next M up (its 32-groups
+// stay inside rows): x's rows and columns past the slice's own read zeros through the
+// bounded loads, P1 and P2 are staged with zero rows and columns past their own sizes, so
+// the padded y is the real one bordered by zeros (max|y| unchanged), and the codes and e8m0
+// bytes are staged and stored for the real rows and columns only.
 //
 // [FQV2] 拆开算 第1步/第2步 on the matrix cores, fused with 第3步/第4步:
 //   GEMM1  T = x_k . P2   A = x rows (straight from HBM, 16 B per lane),
@@ -67,7 +68,7 @@ constexpr int small_waves() {
 
 // CLAMP (per token): the int4 or INT8 clamp is compiled in.  SV (per group): the e8m0 rule.  Q (per
 // token): 0 for int4 codes, else the 8-bit mode (kPerTokenInt8 / E4M3 / E5M2), one byte a code.
-// PAD: M and N are the padded sizes of a smaller per-token slice (pb.M x pb.N).
+// PAD: M and N are the padded sizes of a smaller slice (pb.M x pb.N; pb.N == N per group).
 template <int DT, int M, int N, bool PG, bool CLAMP, int SV, int Q, bool PAD>
 // (The second launch bound is HIP's minimum of waves per SIMD: 2 keeps the 4-wave variants
 // to 256 registers, the budget they were written for, also where one wave per SIMD is
@@ -84,7 +85,6 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()),
   constexpr int MN = M * N;
   constexpr int SPAN = 32 / R;             // lanes per 32-group (per-group mode)
   static_assert(((N % 32 == 0 && R >= 2) || (N == 16 && !PG && Q == 0)) && M % 16 == 0, "unsupported shape");
-  static_assert(!(PAD && PG), "padding is for the per-token modes");
   // the slice's own sizes (the template's with no padding)
   const int Mr = PAD ? static_cast<int>(pb.M) : M, Nr = PAD ? static_cast<int>(pb.N) : N;
 
@@ -120,6 +120,24 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()),
   const int x_span = ((Mr - 1) * xs_m + Nr) * 2;  // bytes a slice spans
   auto load_x = [&](int buf, int64_t slice) {
     const bool in = slice < pb.K;
+    if constexpr (PAD) {
+      // A resource per row tile whose range ends with the slice's last row in it (none past
+      // the slice's rows), so lanes on rows past it read zeros; columns past the slice's are
+      // sent past every range.
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int rows = Mr - 16 * mt < 16 ? Mr - 16 * mt : 16;
+        const auto rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(b.x + (in ? slice : 0) * xs_k + int64_t(16 * mt) * xs_m), static_cast<int16_t>(0),
+            (in && rows > 0) ? ((rows - 1) * xs_m + Nr) * 2 : 0, kBufferWord3);
+#pragma unroll
+        for (int ks = 0; ks < KS1; ++ks)
+          xa[buf][mt][ks] = __builtin_amdgcn_raw_buffer_load_b128(
+              rs, ((N >= 32 || 8 * g < N) && 32 * ks + 8 * g < Nr) ? (c * xs_m + 32 * ks + 8 * g) * 2 : 16 * xs_m * 2, 0,
+              0);
+      }
+      return;
+    }
     const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(b.x + (in ? slice : 0) * xs_k),
                                                         static_cast<int16_t>(0), in ? x_span : 0, kBufferWord3);
     // row tile in the scalar offset, k-step in the immediate: one address register
@@ -128,10 +146,7 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()),
 #pragma unroll
       for (int ks = 0; ks < KS1; ++ks)
         xa[buf][mt][ks] = __builtin_amdgcn_raw_buffer_load_b128(
-            rsrc,
-            ((N >= 32 || 8 * g < N) && (!PAD || (16 * mt + c < Mr && 32 * ks + 8 * g < Nr)))
-                ? (c * xs_m + 32 * ks + 8 * g) * 2
-                : x_span,  // past the slice's rows or columns: zeros
+            rsrc, (N >= 32 || 8 * g < N) ? (c * xs_m + 32 * ks + 8 * g) * 2 : x_span,  // past N: zeros
             16 * mt * xs_m * 2, 0);
   };
   // ---- stage P2 / P1 fragments (once per workgroup) ----
@@ -186,7 +201,12 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()),
         if (q * 64 + lane < CODE_BYTES / 16) __builtin_nontemporal_store(stage[wave][q * 64 + lane], &gcodes[q * 64 + lane]);
       }
     }
-    if constexpr (PG) {
+    if constexpr (PG && PAD) {
+      // the slice's e8m0 bytes and, after an odd count of groups, the zero pad byte
+      const int cb = Mr * Nr / 2, groups = Mr * Nr / 32, e8b = static_cast<int>(e8m0_bytes_per_slice(Mr * Nr));
+      uint8_t* ge = static_cast<uint8_t*>(b.scale) + slice * e8b;
+      for (int q = lane; q < e8b; q += 64) ge[q] = q < groups ? st[cb + q] : uint8_t(0);
+    } else if constexpr (PG) {
       const uint32_t* se = reinterpret_cast<const uint32_t*>(st + CODE_BYTES);
       uint32_t* ge = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(b.scale) +
                                                  slice * e8m0_bytes_per_slice(MN));
@@ -208,7 +228,9 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()),
     // (codes staged as the slice's own rows: NROW elements a row)
     const int NROW = PAD ? Nr : N;
     int code_off = Q ? 4 * g * NROW + R * c : 4 * g * (NROW / 2) + (R >= 2 ? (R / 2) * c : c / 2);
-    int e8_off = CODE_BYTES + 4 * g * (N / 32) + (R * c) / 32;
+    // the slice's own code bytes (the e8m0 bytes are staged after them)
+    const int CB = PAD ? (Q ? Mr * Nr : Mr * Nr / 2) : CODE_BYTES;
+    int e8_off = CB + 4 * g * (N / 32) + (R * c) / 32;
     asm volatile("" : "+v"(code_off), "+v"(e8_off));
     // ---- GEMM1: T = x . P2 (fp32), rounded to the dtype and written straight into the
     // GEMM2 B operands: bt[ks2][nt] = {T rows 32ks2 + 4g + 0..3, T rows 32ks2 + 16 + 4g + 0..3}
@@ -368,19 +390,22 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()),
             packed = fp4x2<3>(packed, y[6][i], y[7][i], sc);
           }
           uint8_t* dst = st + code_off + r0 * (N / 2);
-          if constexpr (R == 2) {
-            *dst = static_cast<uint8_t>(packed);
-          } else if constexpr (R == 4) {
-            *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(packed);
-          } else {
-            *reinterpret_cast<uint32_t*>(dst) = packed;
+          if (!PAD || r0 + 4 * g < Mr) {  // the slice's own rows
+            if constexpr (R == 2) {
+              *dst = static_cast<uint8_t>(packed);
+            } else if constexpr (R == 4) {
+              *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(packed);
+            } else {
+              *reinterpret_cast<uint32_t*>(dst) = packed;
+            }
+            // Group index (row*N + R*c)/32.  Every lane of a group holds the same code, so
+            // all of them store it (no branch).
+            st[e8_off + r0 * (N / 32)] = static_cast<uint8_t>(code);
           }
-          // Group index (row*N + R*c)/32.  Every lane of a group holds the same code, so
-          // all of them store it (no branch).
-          st[e8_off + r0 * (N / 32)] = static_cast<uint8_t>(code);
         }
       }
-      // (M*N/32 is even for every supported shape, so there is no pad byte)
+      // (M*N/32 is even for every shape of the template sizes; with PAD the flush writes
+      // the pad byte of an odd count of groups)
     }
     flush(s);
   };
@@ -427,9 +452,9 @@ template <int DT, int M, int N, bool PG, bool PAD>
 hipError_t dispatch_clamp(const Problem& pb, const Buffers& b, hipStream_t s) {
   if constexpr (PG) {
     switch (e8m0_variant(pb)) {
-      case kE8V1: return launch_one<DT, M, N, true, false, kE8V1>(pb, b, s);
-      case kE8V2Pow2: return launch_one<DT, M, N, true, false, kE8V2Pow2>(pb, b, s);
-      default: return launch_one<DT, M, N, true, false, kE8V2Div>(pb, b, s);
+      case kE8V1: return launch_one<DT, M, N, true, false, kE8V1, 0, PAD>(pb, b, s);
+      case kE8V2Pow2: return launch_one<DT, M, N, true, false, kE8V2Pow2, 0, PAD>(pb, b, s);
+      default: return launch_one<DT, M, N, true, false, kE8V2Div, 0, PAD>(pb, b, s);
     }
   } else {
     switch (pb.mode) {
@@ -447,9 +472,7 @@ hipError_t dispatch_clamp(const Problem& pb, const Buffers& b, hipStream_t s) {
 
 template <int DT, int M, int N, bool PAD>
 hipError_t dispatch_mode(const Problem& pb, const Buffers& b, hipStream_t s) {
-  if constexpr (!PAD) {
-    if (pb.mode == kPerGroupFp4) return dispatch_clamp<DT, M, N, true, false>(pb, b, s);
-  }
+  if (pb.mode == kPerGroupFp4) return dispatch_clamp<DT, M, N, true, PAD>(pb, b, s);
   if constexpr (M * N <= 8192) return dispatch_clamp<DT, M, N, false, PAD>(pb, b, s);
   return hipErrorNotSupported;
 }
@@ -457,10 +480,12 @@ hipError_t dispatch_mode(const Problem& pb, const Buffers& b, hipStream_t s) {
 bool int4_codes(const Problem& pb) { return pb.mode == kPerTokenInt32 || pb.mode == kPerTokenInt4; }
 
 // The sizes an instantiation is chosen by: the slice's own, or with padding the next of
-// 16, 32, 64, 128 (N from 32 for the 8-bit codes, whose layout needs two columns a lane).
+// 16, 32, 64, 128 (N from 32 for the 8-bit codes, whose layout needs two columns a lane;
+// N unpadded per group).
 int pad_up(int v) { return v <= 16 ? 16 : v <= 32 ? 32 : v <= 64 ? 64 : 128; }
 int padded_m(const Problem& pb) { return pad_up(static_cast<int>(pb.M)); }
 int padded_n(const Problem& pb) {
+  if (pb.mode == kPerGroupFp4) return static_cast<int>(pb.N);
   const int n = pad_up(static_cast<int>(pb.N));
   return (n == 16 && !int4_codes(pb)) ? 32 : n;
 }
@@ -499,10 +524,12 @@ bool exact_shape(const Problem& pb) {
   return m_ok && n_ok && (pb.mode == kPerGroupFp4 || pb.M * pb.N <= 8192);
 }
 
-// Runs padded: per token, M and N up to 128, N a multiple of 8, padded sizes within 8192.
+// Runs padded: per token, M and N up to 128, N a multiple of 8, padded sizes within 8192;
+// per group, M up to 128 and N one of 32, 64, 128.
 bool padded_shape(const Problem& pb) {
-  return pb.mode != kPerGroupFp4 && pb.M >= 1 && pb.M <= 128 && pb.N >= 8 && pb.N <= 128 && pb.N % 8 == 0 &&
-         padded_m(pb) * padded_n(pb) <= 8192;
+  if (pb.M < 1 || pb.M > 128) return false;
+  if (pb.mode == kPerGroupFp4) return pb.N == 32 || pb.N == 64 || pb.N == 128;
+  return pb.N >= 8 && pb.N <= 128 && pb.N % 8 == 0 && padded_m(pb) * padded_n(pb) <= 8192;
 }
 
 }  // namespace

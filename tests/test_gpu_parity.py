@@ -68,6 +68,7 @@ EDGE_PER_GROUP = [  # (M, N, two_sided, dmax)
     (64, 128, False, 10.0), (128, 64, True, 12.0), (255, 254, True, 6.0), (256, 256, True, 0.0),
     (256, 256, False, 8.0), (1, 256, False, 0.0), (256, 2, False, 7.0),
     (128, 128, True, 0.0), (128, 128, False, 8.0),  # one wave per SIMD on the small MFMA kernel
+    (86, 128, True, 0.0), (17, 32, False, 8.0), (33, 64, True, 12.0),  # M padded on it
 ]
 
 
@@ -176,6 +177,35 @@ def test_padded_shapes_on_the_small_kernel(M, N, mode, K):
     bo, bs = big_o.cpu().numpy(), big_s.cpu().numpy()
     assert (bo[:G] == 0xA5).all() and (bo[G + nb_out:] == 0xA5).all()
     assert (bs[:G] == 0x5A).all() and (bs[G + nb_sc:] == 0x5A).all()
+
+
+@pytest.mark.parametrize("M,N,two_sided,dmax,K", [(86, 128, True, 0.0, 300), (33, 32, False, 8.0, 517),
+                                                   (100, 64, True, 6.0, 257), (5, 128, False, 0.0, 1031)])
+def test_padded_per_group_on_the_small_kernel(M, N, two_sided, dmax, K):
+    """Per-group slices with M up to 128 and N of 32, 64 or 128 run the one-wave-per-slice
+    MFMA kernel with M padded: every slice's codes and e8m0 bytes against the oracle (an odd
+    count of groups ends with the zero pad byte: 33 x 32 has 33), and nothing written outside
+    the outputs."""
+    say(f"[gpu] padded per group {M}x{N} two_sided={two_sided} dmax={dmax} K={K}")
+    x, p1, p2 = _inputs(M, N, "bf16", K, seed=M * 1000 + N + 11, dist="laplace", two_sided=two_sided)
+    xd, p1d = to_dev(x, "bf16"), to_dev(p1, "bf16")
+    p2d = to_dev(p2, "bf16") if p2 is not None else None
+    assert fq.KERNEL_MFMA_SMALL in supported_kernels(xd, p1d, p2d, "fp4", 1.0, dmax)
+    rep = check(x, p1, p2, "bf16", "fp4", 1.0, dmax, kernel=fq.KERNEL_MFMA_SMALL, label="padded per group")
+    assert rep["ok"], rep["errors"]
+    G = 4096
+    ref_out, ref_sc = fq.empty_outputs(K, M, N, "fp4", DEV)
+    nb_out, nb_sc = ref_out.numel(), ref_sc.numel()
+    big_o = torch.full((G + nb_out + G,), 0xA5, dtype=torch.uint8, device=DEV)
+    big_s = torch.full((G + nb_sc + G,), 0x5A, dtype=torch.uint8, device=DEV)
+    out = big_o[G:G + nb_out].reshape(ref_out.shape)
+    sc = big_s[G:G + nb_sc].reshape(ref_sc.shape)
+    fq.quantize(xd, p1d, p2d, out, sc, "fp4", 1.0, dmax, kernel=fq.KERNEL_MFMA_SMALL)
+    torch.cuda.synchronize()
+    bo, bs = big_o.cpu().numpy(), big_s.cpu().numpy()
+    assert (bo[:G] == 0xA5).all() and (bo[G + nb_out:] == 0xA5).all()
+    assert (bs[:G] == 0x5A).all() and (bs[G + nb_sc:] == 0x5A).all()
+    # (the pad byte itself: compared with the oracle's zero above through check())
 
 
 def test_zero_input_gives_zero_scale_and_codes():
