@@ -1,10 +1,11 @@
 // Small-slice MFMA kernel: one wave per slice x_k [M, N] for M in {16, 32, 64, 128},
-// N in {32, 64, 128}, M*N <= 8192 per token and up to 128 x 128 per group, both dtypes; and
-// N = 16 for the int4 per-token codes (GEMM1's contraction padded to 32 with zero columns
-// of x and zero rows of P2).  Per token above 4096 elements (a slice's y, M*N/64 fp32 a
-// lane, with two slices of x in flight) and per group above 8192 (x and T of a slice, M*N/32
-// registers each) the registers of two waves per SIMD do not suffice: those shapes run one
-// wave per SIMD.
+// N in {32, 64, 128}, both modes, both dtypes; and N = 16 for the int4 per-token codes
+// (GEMM1's contraction padded to 32 with zero columns of x and zero rows of P2).  Per token
+// above 4096 elements (a slice's y, M*N/64 fp32 a lane, with two slices of x in flight) and
+// per group above 8192 (x and T of a slice, M*N/32 registers each) the registers of two
+// waves per SIMD do not suffice: those shapes run one wave per SIMD; per token above 8192
+// even those cannot hold all of y, and GEMM2 runs twice, one 16-row tile at a time (first
+// for max|y|, then for the codes).
 // PAD: a per-token slice of M x N elements with M <= 128 and N <= 128 a multiple of 8 runs
 // in the instantiation of the next sizes up (16, 32, 64, 128; 32 up for the 8-bit codes), a
 // per-group one with M <= 128 and N in {32, 64, 128} in that of the next M up (its 32-groups
@@ -112,7 +113,8 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()),
   // memory.  The loads are therefore issued unconditionally, which keeps the count of
   // memory operations in flight the same on every path, so the compiler's waits for a
   // buffer cover that buffer's loads only and not the ones issued after them.
-  constexpr int PF = prefetch_depth<M, N, PG>();
+  // (the 8-bit codes of a two-pass slice keep one slice in flight: two spill registers)
+  constexpr int PF = (Q != 0 && !PG && MN > 8192) ? 1 : prefetch_depth<M, N, PG>();
   u32x4_t xa[PF][MT][KS1];
   // x's slice and row strides (M*N and N for a contiguous x; a strided x is read in place)
   const int64_t xs_k = pb.xs_k;
@@ -264,58 +266,22 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()),
     load_x(buf, s + PF * waves);
 
     if constexpr (!PG) {
-      // ---- GEMM2: y = P1 . T, all of y (the scale needs max|y| over the slice) ----
-      f32x4_t y[MT][NT];
-#pragma unroll
-      for (int it = 0; it < MT; ++it)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) y[it][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks2 = 0; ks2 < KS2; ++ks2)
-#pragma unroll
-        for (int it = 0; it < MT; ++it) {
-          const u32x4_t a = frag1[(it * KS2 + ks2) * 64 + lane];
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) y[it][nt] = mfma16x16x32<DT>(a, bt[ks2][nt], y[it][nt]);
-        }
-      // [FQV2] 第3步 pertoken: scale = max|y| / (7/clipRatio); code = RNE(y / scale)
-      float amax = 0.0f;
-#pragma unroll
-      for (int it = 0; it < MT; ++it)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) amax = fmaxf(amax, __builtin_fabsf(y[it][nt][i]));
-      amax = wave_max(amax);
-      // (every lane holds the same maximum; the scale is made wave-uniform so the branch
-      // below is a scalar one)
-      const float scale = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(amax / pb.d)));
-      const TokenRecip rc = token_recip(scale);
-      if (rc.tiny) {
-        // a scale below 2^-126: y * 2^64 exactly, and inv = 1 / (scale * 2^64)
-#pragma unroll
-        for (int it = 0; it < MT; ++it)
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) y[it][nt] *= rc.pre;
-      }
-      const float inv = rc.inv;
-      if (lane == 0) static_cast<float*>(b.scale)[s] = scale;
-      if constexpr (Q != 0) {
-        // 8-bit codes (the dequant_swiglu_quant page, section 3.4): the lane's R codes of a
-        // row are R consecutive bytes
-#pragma unroll
-        for (int it = 0; it < MT; ++it)
+      // The codes of 16-row tile it of y (yt: its NT accumulator tiles), inv = 1 / scale.
+      auto encode_tile = [&](const int it, const f32x4_t* yt, const float inv) {
+        if constexpr (Q != 0) {
+          // 8-bit codes (the dequant_swiglu_quant page, section 3.4): the lane's R codes of a
+          // row are R consecutive bytes
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r0 = 16 * it + i;  // row - 4g
             uint32_t w[(R + 3) / 4];
             if constexpr (R == 2) {
-              w[0] = code8x2<Q>(y[it][0][i] * inv, y[it][1][i] * inv);
+              w[0] = code8x2<Q>(yt[0][i] * inv, yt[1][i] * inv);
             } else {
 #pragma unroll
               for (int q = 0; q < R / 4; ++q)
-                w[q] = code8x4<Q, CLAMP>(y[it][4 * q][i], y[it][4 * q + 1][i], y[it][4 * q + 2][i],
-                                         y[it][4 * q + 3][i], inv);
+                w[q] = code8x4<Q, CLAMP>(yt[4 * q][i], yt[4 * q + 1][i], yt[4 * q + 2][i],
+                                         yt[4 * q + 3][i], inv);
             }
             uint8_t* dst = st + code_off + r0 * NROW;
             if (!PAD || (r0 + 4 * g < Mr && R * c < Nr)) {  // the slice's own rows and columns
@@ -327,35 +293,113 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()),
               }
             }
           }
-      } else {
+        } else {
 #pragma unroll
-      for (int it = 0; it < MT; ++it)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r0 = 16 * it + i;  // row - 4g
-          uint32_t by[R >= 2 ? R / 2 : 1];
-          if constexpr (R == 1) {
-            // columns c and c ^ 1 (lane c ^ 1 holds the other): both lanes form the same byte
-            const uint32_t own = int4_biased<CLAMP>(y[it][0][i], inv);
-            const uint32_t nbr = dpp_u<kDppQuadXor1>(own);
-            by[0] = (c & 1) ? pair_byte(nbr, own) : pair_byte(own, nbr);
-          } else {
-#pragma unroll
-            for (int p = 0; p < R / 2; ++p)
-              by[p] = pair_byte(int4_biased<CLAMP>(y[it][2 * p][i], inv),
-                                int4_biased<CLAMP>(y[it][2 * p + 1][i], inv));
-          }
-          uint8_t* dst = st + code_off + r0 * (NROW / 2);
-          if (!PAD || (r0 + 4 * g < Mr && R * c < Nr)) {  // the slice's own rows and columns
-            if constexpr (R <= 2) {
-              *dst = static_cast<uint8_t>(by[0] ^ 0x88u);
-            } else if constexpr (R == 4) {
-              *reinterpret_cast<uint16_t*>(dst) =
-                  static_cast<uint16_t>(unbias(__builtin_amdgcn_perm(by[1], by[0], 0x0C0C0400u)));
+          for (int i = 0; i < 4; ++i) {
+            const int r0 = 16 * it + i;  // row - 4g
+            uint32_t by[R >= 2 ? R / 2 : 1];
+            if constexpr (R == 1) {
+              // columns c and c ^ 1 (lane c ^ 1 holds the other): both lanes form the same byte
+              const uint32_t own = int4_biased<CLAMP>(yt[0][i], inv);
+              const uint32_t nbr = dpp_u<kDppQuadXor1>(own);
+              by[0] = (c & 1) ? pair_byte(nbr, own) : pair_byte(own, nbr);
             } else {
-              *reinterpret_cast<uint32_t*>(dst) = unbias(gather4(by[0], by[1], by[2], by[3]));
+#pragma unroll
+              for (int p = 0; p < R / 2; ++p)
+                by[p] = pair_byte(int4_biased<CLAMP>(yt[2 * p][i], inv),
+                                  int4_biased<CLAMP>(yt[2 * p + 1][i], inv));
+            }
+            uint8_t* dst = st + code_off + r0 * (NROW / 2);
+            if (!PAD || (r0 + 4 * g < Mr && R * c < Nr)) {  // the slice's own rows and columns
+              if constexpr (R <= 2) {
+                *dst = static_cast<uint8_t>(by[0] ^ 0x88u);
+              } else if constexpr (R == 4) {
+                *reinterpret_cast<uint16_t*>(dst) =
+                    static_cast<uint16_t>(unbias(__builtin_amdgcn_perm(by[1], by[0], 0x0C0C0400u)));
+              } else {
+                *reinterpret_cast<uint32_t*>(dst) = unbias(gather4(by[0], by[1], by[2], by[3]));
+              }
             }
           }
+        }
+      };
+      if constexpr (MN <= 8192) {
+        // ---- GEMM2: y = P1 . T, all of y (the scale needs max|y| over the slice) ----
+        f32x4_t y[MT][NT];
+#pragma unroll
+        for (int it = 0; it < MT; ++it)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) y[it][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks2 = 0; ks2 < KS2; ++ks2)
+#pragma unroll
+          for (int it = 0; it < MT; ++it) {
+            const u32x4_t a = frag1[(it * KS2 + ks2) * 64 + lane];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) y[it][nt] = mfma16x16x32<DT>(a, bt[ks2][nt], y[it][nt]);
+          }
+        // [FQV2] 第3步 pertoken: scale = max|y| / (7/clipRatio); code = RNE(y / scale)
+        float amax = 0.0f;
+#pragma unroll
+        for (int it = 0; it < MT; ++it)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) amax = fmaxf(amax, __builtin_fabsf(y[it][nt][i]));
+        amax = wave_max(amax);
+        // (every lane holds the same maximum; the scale is made wave-uniform so the branch
+        // below is a scalar one)
+        const float scale = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(amax / pb.d)));
+        const TokenRecip rc = token_recip(scale);
+        if (rc.tiny) {
+          // a scale below 2^-126: y * 2^64 exactly, and inv = 1 / (scale * 2^64)
+#pragma unroll
+          for (int it = 0; it < MT; ++it)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) y[it][nt] *= rc.pre;
+        }
+        if (lane == 0) static_cast<float*>(b.scale)[s] = scale;
+#pragma unroll
+        for (int it = 0; it < MT; ++it) encode_tile(it, y[it], rc.inv);
+      } else {
+        // Above 8192 elements all of y does not fit the registers: GEMM2 runs twice, one
+        // 16-row tile at a time, first for max|y| (the scale), then for the codes.
+        auto gemm2_tile = [&](const int it, f32x4_t* yt) {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) yt[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks2 = 0; ks2 < KS2; ++ks2) {
+            const u32x4_t a = frag1[(it * KS2 + ks2) * 64 + lane];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) yt[nt] = mfma16x16x32<DT>(a, bt[ks2][nt], yt[nt]);
+          }
+        };
+        // [FQV2] 第3步 pertoken: scale = max|y| / (7/clipRatio); code = RNE(y / scale)
+        float amax = 0.0f;
+#pragma unroll
+        for (int it = 0; it < MT; ++it) {
+          asm volatile("" ::: "memory");  // one row tile live at a time
+          f32x4_t yt[NT];
+          gemm2_tile(it, yt);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) amax = fmaxf(amax, __builtin_fabsf(yt[nt][i]));
+        }
+        amax = wave_max(amax);
+        const float scale = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(amax / pb.d)));
+        const TokenRecip rc = token_recip(scale);
+        if (lane == 0) static_cast<float*>(b.scale)[s] = scale;
+#pragma unroll
+        for (int it = 0; it < MT; ++it) {
+          asm volatile("" ::: "memory");
+          f32x4_t yt[NT];
+          gemm2_tile(it, yt);  // the same products in the same order: the same y
+          if (rc.tiny) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) yt[nt] *= rc.pre;
+          }
+          encode_tile(it, yt, rc.inv);
         }
       }
     } else {
@@ -473,8 +517,7 @@ hipError_t dispatch_clamp(const Problem& pb, const Buffers& b, hipStream_t s) {
 template <int DT, int M, int N, bool PAD>
 hipError_t dispatch_mode(const Problem& pb, const Buffers& b, hipStream_t s) {
   if (pb.mode == kPerGroupFp4) return dispatch_clamp<DT, M, N, true, PAD>(pb, b, s);
-  if constexpr (M * N <= 8192) return dispatch_clamp<DT, M, N, false, PAD>(pb, b, s);
-  return hipErrorNotSupported;
+  return dispatch_clamp<DT, M, N, false, PAD>(pb, b, s);
 }
 
 bool int4_codes(const Problem& pb) { return pb.mode == kPerTokenInt32 || pb.mode == kPerTokenInt4; }
@@ -520,16 +563,15 @@ bool exact_shape(const Problem& pb) {
   // N = 16: int4 per-token codes only (one code a lane per row: the 8-bit and per-group
   // layouts are not implemented for it)
   const bool n_ok = pb.N == 32 || pb.N == 64 || pb.N == 128 || (pb.N == 16 && int4_codes(pb));
-  // registers: the per-token path keeps all of y (M*N/64 fp32 per lane)
-  return m_ok && n_ok && (pb.mode == kPerGroupFp4 || pb.M * pb.N <= 8192);
+  return m_ok && n_ok;
 }
 
-// Runs padded: per token, M and N up to 128, N a multiple of 8, padded sizes within 8192;
-// per group, M up to 128 and N one of 32, 64, 128.
+// Runs padded: per token, M and N up to 128, N a multiple of 8; per group, M up to 128 and
+// N one of 32, 64, 128.
 bool padded_shape(const Problem& pb) {
   if (pb.M < 1 || pb.M > 128) return false;
   if (pb.mode == kPerGroupFp4) return pb.N == 32 || pb.N == 64 || pb.N == 128;
-  return pb.N >= 8 && pb.N <= 128 && pb.N % 8 == 0 && padded_m(pb) * padded_n(pb) <= 8192;
+  return pb.N >= 8 && pb.N <= 128 && pb.N % 8 == 0;
 }
 
 }  // namespace

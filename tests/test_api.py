@@ -82,17 +82,19 @@ def test_pipelined_kernel_plans_a_slice_counter(mode, p2_empty, ws):
 
 
 @pytest.mark.parametrize("M,N,mode,kernel", [(64, 64, "int32", 2), (64, 128, "int4", 2), (128, 64, "int32", 2),
-                                            (64, 128, "int8", 2), (128, 128, "int32", 1), (128, 128, "fp4", 2),
-                                            (64, 128, "fp4", 2), (86, 128, "int4", 1), (128, 256, "fp4", 1),
+                                            (64, 128, "int8", 2), (128, 128, "int32", 2), (128, 128, "fp4", 2),
+                                            (64, 128, "fp4", 2), (86, 128, "int4", 2), (128, 256, "fp4", 1),
+                                            (112, 128, "int4", 2), (128, 128, "e4m3", 2), (128, 136, "int32", 1),
                                             (17, 24, "int32", 2), (86, 64, "int4", 2), (33, 40, "int8", 2),
                                             (3, 8, "int32", 2), (40, 120, "e5m2", 2), (17, 34, "int4", 1),
                                             (33, 30, "int4", 1), (129, 64, "int32", 1), (17, 32, "fp4", 2),
                                             (86, 128, "fp4", 2), (17, 48, "fp4", 1), (129, 32, "fp4", 1)])
 def test_automatic_kernel_by_shape(M, N, mode, kernel):
-    """The one-wave-per-slice MFMA kernel takes per-token slices up to 8192 elements (one
-    wave per SIMD above 4096), padded to its sizes when M <= 128 and N <= 128 is a multiple
-    of 8, and per-group ones up to 128 x 128 (one wave per SIMD above 8192), M padded when
-    N is 32, 64 or 128; other shapes below 256 x 256 take the generic kernel."""
+    """The one-wave-per-slice MFMA kernel takes per-token slices up to 128 x 128 (one wave
+    per SIMD above 4096 elements, two passes over GEMM2 above 8192), padded to its sizes when
+    N is a multiple of 8, and per-group ones up to 128 x 128 (one wave per SIMD above 8192),
+    M padded when N is 32, 64 or 128; other shapes below 256 x 256 take the generic
+    kernel."""
     st, ws, ex = fq.fq_get_workspace_size(*[problem(3, M, N, mode=mode)[k] for k in ("x", "p1", "p2")], 1.0, 0.0,
                                           problem(3, M, N, mode=mode)["out"], problem(3, M, N, mode=mode)["sc"])
     assert st == OK

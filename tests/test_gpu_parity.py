@@ -48,6 +48,7 @@ EDGE_PER_TOKEN = [  # (M, N, mode)
     (32, 16, "int4"), (64, 16, "int32"), (128, 16, "int4"),  # N = 16 on the small MFMA kernel
     (128, 64, "int32"),  # with (64, 128): one wave per SIMD on the small MFMA kernel
     (86, 64, "int4"), (56, 64, "int32"), (40, 120, "int32"), (9, 8, "int4"),  # padded on it
+    (112, 128, "int4"), (86, 128, "int32"), (100, 96, "int4"),  # two passes over GEMM2 on it
 ]
 
 
@@ -152,7 +153,8 @@ def test_pipelined_kernel_writes_every_slice(K):
 
 
 @pytest.mark.parametrize("M,N,mode,K", [(33, 40, "int4", 1031), (86, 64, "int32", 300), (17, 24, "int8", 517),
-                                         (40, 120, "int4", 257), (3, 8, "int32", 700), (100, 16, "e4m3", 129)])
+                                         (40, 120, "int4", 257), (3, 8, "int32", 700), (100, 16, "e4m3", 129),
+                                         (112, 128, "int4", 300), (128, 128, "int8", 130), (86, 128, "e5m2", 77)])
 def test_padded_shapes_on_the_small_kernel(M, N, mode, K):
     """Per-token slices of other sizes (M up to 128, N a multiple of 8 up to 128) run the
     one-wave-per-slice MFMA kernel padded to its next sizes: every slice against the oracle at

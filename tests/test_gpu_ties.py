@@ -132,7 +132,8 @@ def int4_values(d, e, dt):
 
 # clipRatio -> d = fl32(7 / clipRatio), exact for these
 CLIPS = {1.0: 7.0, 0.875: 8.0, 0.5: 14.0, 2.0 ** -23: 7.0 * 2.0 ** 23}
-SHAPES_TOKEN = [(64, 64), (32, 128), (16, 16), (17, 24), (256, 256)]
+SHAPES_TOKEN = [(64, 64), (32, 128), (16, 16), (17, 24), (256, 256),
+                (128, 128), (86, 128)]  # (two passes over GEMM2 on the small kernel, exact and padded)
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
