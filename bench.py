@@ -110,7 +110,9 @@ def profile_info(w, op="quantize"):
             for line in fh:
                 if line.startswith("machine-readable:"):
                     info = json.loads(line.split(":", 1)[1])
-                    if info.get("source_hash") == kernel_source_hash(info.get("kernel")):
+                    # (a GEMM summary's name ends with the workload its A came from; it has no
+                    # workload of its own)
+                    if info.get("workload") == w.name and info.get("source_hash") == kernel_source_hash(info.get("kernel")):
                         return info
     return None
 
