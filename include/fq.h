@@ -244,8 +244,10 @@ void fq_executor_destroy(fq_executor* executor);
 fq_status fq_executor_set_repeatable(fq_executor* executor, int32_t repeat);
 
 /* Kernel variant the executor will launch: 0 = the automatic choice, 1 = the generic
- * kernel (any shape), 2 = the small-slice MFMA kernel (one wave per slice), 3 = the
- * whole-workgroup MFMA kernel for 256-class slices, 4 = its pipelined form for 256 x 256
+ * kernel (any shape), 2 = the small-slice MFMA kernel (one wave per slice; M and N up to
+ * 128, run at the next of 16, 32, 64, 128 with zero padding where they are not one of
+ * them: per token N a multiple of 8, per group N one of 32, 64, 128), 3 = the
+ * whole-workgroup MFMA kernel for 256 x 256 slices, 4 = its pipelined form for 256 x 256
  * slices with both transforms and per-token int4 codes (INT32 / INT4 out; the automatic
  * choice there).  Selecting a variant that does not support the planned problem returns
  * FQ_ERR_PARAM_INVALID and leaves the executor unchanged.  Meant for tests and
