@@ -49,15 +49,15 @@ constexpr bool one_wave_per_simd() {
 
 // Slices of x kept in flight per wave: two for slices under 4096 elements (the loads of
 // the slice two ahead are issued as soon as the current one's first product has consumed
-// its registers) and where one wave runs per SIMD, one otherwise.  At 4096 elements one slice in flight in each of two
-// waves per SIMD beats two slices in flight in one wave per SIMD by 4-5% (while one wave
-// waits for its x the other computes); three slices in flight measured slower still (the
-// extra slice every wave queues at the start delays every wave's first slice).
+// its registers) and where one wave runs per SIMD, one otherwise.  At 4096 elements one
+// slice in flight in each of two waves per SIMD beats two slices in flight in one wave per
+// SIMD by 4-5% (while one wave waits for its x the other computes); three slices in flight
+// measured slower still (the extra slice every wave queues at the start delays every
+// wave's first slice).
 template <int M, int N, bool PG>
 constexpr int prefetch_depth() {
   return (M * N < 4096 || one_wave_per_simd<M, N, PG>()) ? 2 : 1;
 }
-
 
 // Waves per workgroup: 8 from 4096 elements up (one workgroup per CU, so the CU stages
 // its P fragments once: 6-9% faster at M=64, N=128 than two 4-wave workgroups), 4 for the
@@ -113,7 +113,7 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()),
   // memory.  The loads are therefore issued unconditionally, which keeps the count of
   // memory operations in flight the same on every path, so the compiler's waits for a
   // buffer cover that buffer's loads only and not the ones issued after them.
-  // (the 8-bit codes of a two-pass slice keep one slice in flight: two spill registers)
+  // (a two-pass slice with 8-bit codes keeps one slice in flight: with two the kernel spills)
   constexpr int PF = (Q != 0 && !PG && MN > 8192) ? 1 : prefetch_depth<M, N, PG>();
   u32x4_t xa[PF][MT][KS1];
   // x's slice and row strides (M*N and N for a contiguous x; a strided x is read in place)

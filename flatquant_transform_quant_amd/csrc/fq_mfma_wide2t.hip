@@ -30,7 +30,7 @@
 // waves through an LDS buffer that is free at that point.
 //
 // Slices are handed out at run time: a counter in device memory (zeroed before the launch)
-// gives each workgroup its next slice, one atomic add per slice, taken two slices ahead
+// gives each workgroup its next slice, one atomic increment per slice, taken two slices ahead
 // (the next slice's first x chunk is requested halfway through the current one) and passed
 // to the workgroup's waves with the max reduction.  The XCDs of the device run at clocks a
 // few percent apart under this load, and with a fixed share of the slices per workgroup
@@ -53,7 +53,7 @@ constexpr int kNChunk = kW / kChunk;
 constexpr int kIT = kW / 16;  // 16-row tiles of y
 constexpr int kYA = 8;        // y tiles 0 .. kYA-1 in accumulation registers, the rest in ordinary ones
 constexpr int kEl = kIT * 16;  // y elements a lane
-constexpr int kBarStage = 8;
+constexpr int kBarStage = 8;   // the stage of a GEMM2 block that passes the barrier of the GEMM1 block before it
 
 // A ticket of the slice counter: the counter's value before adding one.  An increment that
 // wraps at 2^32 - 1 (the same as adding one for every reachable value) rather than an add: the
@@ -62,7 +62,7 @@ constexpr int kBarStage = 8;
 // wait at the reply's first use.
 __device__ __forceinline__ uint32_t take_ticket(uint32_t* ctr) {
   return __builtin_amdgcn_atomic_inc32(ctr, 0xFFFFFFFFu, __ATOMIC_RELAXED, "agent");
-}   // the stage of a GEMM2 block that passes the barrier of the GEMM1 block before it
+}
 
 // GEMM2 of chunks 6 and 7 as one 32-stage block: stage s -> (tile, chunk).  Chunk 7 starts
 // at stage 3 (its T is rounded during stages 1 and 2) and the accumulation-register tiles
