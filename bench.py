@@ -74,7 +74,8 @@ def algorithmic_flops(w, K=None) -> int:
 
 # the source file of each profiled kernel
 KERNEL_SOURCES = {"generic": "fq_generic.hip", "mfma_small": "fq_mfma_small.hip", "mfma_wide1": "fq_mfma_wide.hip",
-                  "mfma_wide2": "fq_mfma_wide.hip", "mfma_wide2t": "fq_mfma_wide2t.hip", "dequant": "fq_dequant.hip",
+                  "mfma_wide2": "fq_mfma_wide.hip", "mfma_wide2t": "fq_mfma_wide2t.hip",
+                  "mfma_wide1s": "fq_mfma_wide1s.hip", "dequant": "fq_dequant.hip",
                   "mx_gemm_kernel": "fq_mx_gemm.hip", "int4_gemm_kernel": "fq_int4_gemm.hip"}
 
 
@@ -343,7 +344,7 @@ def measure_workload(key, args, dev):
              "frac": round(mfma_frac, 4)})
     roof["traffic"] = info.get("traffic_bytes_per_dispatch") if info else None
     roof["kernel"] = {1: "generic_kernel", 2: "mfma_small_kernel", 3: "mfma_wide_kernel",
-                      4: "mfma_wide2t_kernel"}.get(kernel_id)
+                      4: "mfma_wide2t_kernel", 5: "mfma_wide1s_kernel"}.get(kernel_id)
     roof["avg_launch_us"] = round(ms_per_step * 1e3, 3)
     roof["algorithmic_bytes"] = bytes_
     roof["algorithmic_flops"] = flops
@@ -389,7 +390,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="all",
                     help="all (the headline c4 with c1, c2, c3, c5 as sub-records) or one workload key")
-    ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 generic, 2 mfma-small, 3 mfma-wide, 4 mfma-wide pipelined (256x256 two-sided per-token)")
+    ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 generic, 2 mfma-small, 3 mfma-wide, 4 mfma-wide pipelined (256x256 two-sided per-token), 5 mfma-wide streaming (256x256 left-only per-group)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline (and its parity check)")
     ap.add_argument("--cpu-budget", type=float, default=8.0)
     ap.add_argument("--op", default="quantize", choices=["quantize", "dequant", "mxgemm", "i4gemm"],

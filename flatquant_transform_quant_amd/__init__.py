@@ -34,7 +34,7 @@ DT_FLOAT16, DT_BFLOAT16, DT_FLOAT32, DT_INT32, DT_INT4, DT_FLOAT4_E2M1, DT_FLOAT
 DT_INT8, DT_FLOAT8_E4M3FN, DT_FLOAT8_E5M2 = range(8, 11)
 BYTE_MODES = {"int8": DT_INT8, "e4m3": DT_FLOAT8_E4M3FN, "e5m2": DT_FLOAT8_E5M2}
 PER_TOKEN_MODES = ("int32", "int4") + tuple(BYTE_MODES)
-KERNEL_AUTO, KERNEL_GENERIC, KERNEL_MFMA_SMALL, KERNEL_MFMA_WIDE, KERNEL_MFMA_WIDE_T = 0, 1, 2, 3, 4
+KERNEL_AUTO, KERNEL_GENERIC, KERNEL_MFMA_SMALL, KERNEL_MFMA_WIDE, KERNEL_MFMA_WIDE_T, KERNEL_MFMA_WIDE_L = 0, 1, 2, 3, 4, 5
 
 
 class FqTensor(ctypes.Structure):

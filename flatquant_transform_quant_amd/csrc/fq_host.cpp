@@ -126,12 +126,14 @@ bool kernel_supports(int32_t k, const fq_executor* e) {
     case fq::kMfmaSmall: return vector_aligned(e) && fq::mfma_small_supports(e->pb);
     case fq::kMfmaWide: return !e->x_direct && vector_aligned(e) && fq::mfma_wide_supports(e->pb);
     case fq::kMfmaWideT: return !e->x_direct && vector_aligned(e) && fq::mfma_wide2t_supports(e->pb);
+    case fq::kMfmaWideL: return !e->x_direct && vector_aligned(e) && fq::mfma_wide1s_supports(e->pb);
     default: return false;
   }
 }
 
 int32_t auto_kernel(const fq_executor* e) {
   if (kernel_supports(fq::kMfmaWideT, e)) return fq::kMfmaWideT;
+  if (kernel_supports(fq::kMfmaWideL, e)) return fq::kMfmaWideL;
   if (kernel_supports(fq::kMfmaWide, e)) return fq::kMfmaWide;
   if (kernel_supports(fq::kMfmaSmall, e)) return fq::kMfmaSmall;
   return fq::kGeneric;
@@ -261,7 +263,7 @@ fq_status fq_get_workspace_size(const fq_tensor* x, const fq_tensor* kroneckerP1
     const bool ok = (sn == 1 || N == 1) && (sk % 8 == 0 || K == 1) && (sm % 8 == 0 || M == 1) &&
                     reinterpret_cast<uintptr_t>(x->data) % 16 == 0 && (M - 1) * sm + N < (int64_t(1) << 30) &&
                     (K - 1) * sk + (M - 1) * sm + N < (int64_t(1) << 62);
-    if (ok && auto_kernel(e) != fq::kMfmaWide && auto_kernel(e) != fq::kMfmaWideT) {
+    if (ok && auto_kernel(e) != fq::kMfmaWide && auto_kernel(e) != fq::kMfmaWideT && auto_kernel(e) != fq::kMfmaWideL) {
       e->stage_x = false;
       e->x_direct = true;
       e->pb.xs_k = K == 1 ? MN : sk;
@@ -344,6 +346,7 @@ fq_status fq_run(void* workspace, uint64_t workspaceSize, fq_executor* executor,
         err = fq::launch_mfma_wide2t(pb, b, stream);
         if (err == hipSuccess) err = fq::launch_tiny_scale_fixup(pb, b, stream);  // as above
         break;
+      case fq::kMfmaWideL: err = fq::launch_mfma_wide1s(pb, b, stream); break;
       default: err = fq::launch_generic(pb, b, stream); break;
     }
     if (err != hipSuccess) { st = fail_runtime("transform-quantize kernel launch", err); break; }

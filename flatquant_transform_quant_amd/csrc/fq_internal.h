@@ -18,7 +18,7 @@ enum Mode : int32_t {
 };
 // codes of one byte each (the 8-bit per-token modes) rather than two codes a byte
 __host__ __device__ inline bool byte_codes(int32_t mode) { return mode >= kPerTokenInt8; }
-enum Kernel : int32_t { kAuto = 0, kGeneric = 1, kMfmaSmall = 2, kMfmaWide = 3, kMfmaWideT = 4 };
+enum Kernel : int32_t { kAuto = 0, kGeneric = 1, kMfmaSmall = 2, kMfmaWide = 3, kMfmaWideT = 4, kMfmaWideL = 5 };
 
 // One planned problem, as the kernels see it (all tensors contiguous).
 struct Problem {
@@ -68,6 +68,10 @@ hipError_t launch_mfma_wide(const Problem& pb, const Buffers& b, hipStream_t s);
 // slice's first products).
 bool mfma_wide2t_supports(const Problem& pb);
 hipError_t launch_mfma_wide2t(const Problem& pb, const Buffers& b, hipStream_t s);
+// The streaming 256 x 256 left-only per-group kernel (x through an LDS-DMA ring, P1 in
+// registers).
+bool mfma_wide1s_supports(const Problem& pb);
+hipError_t launch_mfma_wide1s(const Problem& pb, const Buffers& b, hipStream_t s);
 
 // Dequantization of contiguous codes/scales into a contiguous [K, M, N] 16-bit output.
 hipError_t launch_dequant(int32_t dtype, bool per_group, int64_t K, int64_t M, int64_t N, const uint8_t* codes,

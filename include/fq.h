@@ -249,12 +249,14 @@ fq_status fq_executor_set_repeatable(fq_executor* executor, int32_t repeat);
  * them: per token N a multiple of 8, per group N one of 32, 64, 128), 3 = the
  * whole-workgroup MFMA kernel for 256 x 256 slices, 4 = its pipelined form for 256 x 256
  * slices with both transforms and per-token int4 codes (INT32 / INT4 out; the automatic
+ * choice there), 5 = the streaming MFMA kernel for 256 x 256 slices with an empty P2 and
+ * FLOAT4_E2M1 out (x through an LDS ring filled by DMA, P1 in registers; the automatic
  * choice there).  Selecting a variant that does not support the planned problem returns
  * FQ_ERR_PARAM_INVALID and leaves the executor unchanged.  Meant for tests and
  * benchmarks. */
 fq_status fq_executor_set_kernel(fq_executor* executor, int32_t variant);
 
-/* The variant the executor will launch (1 .. 4), or a negative value for NULL. */
+/* The variant the executor will launch (1 .. 5), or a negative value for NULL. */
 int32_t fq_executor_kernel(const fq_executor* executor);
 
 /* A static, human-readable name for a status code. */

@@ -49,7 +49,7 @@ def supported_kernels(x_dev, p1_dev, p2_dev, mode, clip, dmax):
     K, M, N = x_dev.shape
     out, sc = fq.empty_outputs(K, M, N, mode, DEV)
     ks = []
-    for k in (fq.KERNEL_GENERIC, fq.KERNEL_MFMA_SMALL, fq.KERNEL_MFMA_WIDE, fq.KERNEL_MFMA_WIDE_T):
+    for k in (fq.KERNEL_GENERIC, fq.KERNEL_MFMA_SMALL, fq.KERNEL_MFMA_WIDE, fq.KERNEL_MFMA_WIDE_T, fq.KERNEL_MFMA_WIDE_L):
         try:
             ex = fq.Executor(x_dev, p1_dev, p2_dev, out, sc, mode, clip, dmax, kernel=k)
         except fq.FqError:

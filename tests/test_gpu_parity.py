@@ -10,7 +10,9 @@ import pytest
 import torch
 
 import flatquant_transform_quant_amd as fq
+import oracle
 import synth
+from oracle.compare import compare
 from gpu_util import DEV, check, fetch, run_lib, say, supported_kernels, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -367,3 +369,29 @@ def test_strided_x_in_place_or_gathered(M, N, mode):
         torch.cuda.synchronize()
         got = fetch(out, sc, mode, K)
         assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1]), name
+
+
+@pytest.mark.parametrize("K", [1, 255, 256, 257, 700])
+def test_streaming_left_only_kernel_writes_every_slice(K):
+    """The streaming 256 x 256 left-only kernel (x through an LDS ring filled by DMA loads,
+    nine chunks ahead, across slice boundaries and past K): outputs pre-filled with a marker,
+    every slice compared with the oracle, on two runs of one executor."""
+    w = synth.WORKLOADS["c5"]
+    x, p1, _ = synth.make_inputs(w, 0, K)
+    xd, p1d = to_dev(x, w.dtype), to_dev(p1, w.dtype)
+    out, sc = fq.empty_outputs(K, w.M, w.N, w.mode, DEV)
+    ex = fq.Executor(xd, p1d, None, out, sc, w.mode, w.clip_ratio, w.dst_type_max, kernel=fq.KERNEL_MFMA_WIDE_L)
+    assert ex.kernel == fq.KERNEL_MFMA_WIDE_L
+    orc = oracle.run(x, p1, None, w.dtype, w.mode, w.clip_ratio, w.dst_type_max, nthreads=8)
+    try:
+        for run in range(2):
+            say(f"[gpu] streaming left-only kernel K={K} run {run}")
+            out.view(torch.uint8).fill_(0xEE)
+            sc.view(torch.uint8).fill_(0xEE)
+            ex.run()
+            torch.cuda.synchronize()
+            packed, scale = fetch(out, sc, w.mode, K)
+            rep = compare(orc, packed, scale)
+            assert rep["ok"], rep["errors"]
+    finally:
+        ex.destroy()

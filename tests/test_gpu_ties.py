@@ -275,6 +275,7 @@ def test_e2m1_every_decision_point_and_e8m0_rule_exact(dt, dmax):
             assert fq.KERNEL_MFMA_SMALL in ks
         if (M, N) == (256, 256):
             assert fq.KERNEL_MFMA_WIDE in ks
+            assert (fq.KERNEL_MFMA_WIDE_L in ks) == (not two)
         # the plan reached both branches of the V2 rule
         r = oracle.run(x, eye1, eye2, dt, "fp4", 1.0, dmax, ranges=False)
         if dmax > 0:
