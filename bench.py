@@ -98,10 +98,10 @@ def kernel_source_hash(kernel: str | None = None) -> str:
     return h.hexdigest()[:16]
 
 
-def profile_info(w, op="quantize"):
+def profile_info(w, op="quantize", kernel: str | None = None):
     """The machine-readable record of the committed rocprofv3 summary of this workload's
-    kernel (profiles/<kernel>_<workload>.md), or None when there is none or the kernel's
-    device code has changed since it was taken."""
+    kernel (profiles/<kernel>_<workload>.md; `kernel`, when given, names the one launched),
+    or None when there is none or the kernel's device code has changed since it was taken."""
     import glob
 
     for f in sorted(glob.glob(os.path.join(ROOT, "profiles", f"*_{w.name}.md"))):
@@ -113,6 +113,8 @@ def profile_info(w, op="quantize"):
                     info = json.loads(line.split(":", 1)[1])
                     # (a GEMM summary's name ends with the workload its A came from; it has no
                     # workload of its own)
+                    if kernel is not None and info.get("kernel") != kernel:
+                        continue
                     if info.get("workload") == w.name and info.get("source_hash") == kernel_source_hash(info.get("kernel")):
                         return info
     return None
@@ -336,15 +338,18 @@ def measure_workload(key, args, dev):
     hbm_frac = gbs / HBM_PEAK_GBS
     mfma_frac = tfs / MFMA_BF16_PEAK_TFS
     bound = "hbm" if bytes_ / (HBM_PEAK_GBS * 1e9) >= flops / (MFMA_BF16_PEAK_TFS * 1e12) else "mfma"
-    info = profile_info(w)
+    kname = {1: "generic_kernel", 2: "mfma_small_kernel", 3: "mfma_wide_kernel", 4: "mfma_wide2t_kernel",
+             5: "mfma_wide1s_kernel"}.get(kernel_id)
+    # the summaries name a kernel by its source family; the two forms of mfma_wide_kernel by side count
+    short = {"mfma_wide_kernel": "mfma_wide2" if w.two_sided else "mfma_wide1"}.get(kname, (kname or "")[:-len("_kernel")])
+    info = profile_info(w, kernel=short or None)
     roof = ({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
              "frac": round(hbm_frac, 4)}
             if bound == "hbm" else
             {"bound": "mfma", "achieved": round(tfs, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
              "frac": round(mfma_frac, 4)})
     roof["traffic"] = info.get("traffic_bytes_per_dispatch") if info else None
-    roof["kernel"] = {1: "generic_kernel", 2: "mfma_small_kernel", 3: "mfma_wide_kernel",
-                      4: "mfma_wide2t_kernel", 5: "mfma_wide1s_kernel"}.get(kernel_id)
+    roof["kernel"] = kname
     roof["avg_launch_us"] = round(ms_per_step * 1e3, 3)
     roof["algorithmic_bytes"] = bytes_
     roof["algorithmic_flops"] = flops
