@@ -10,7 +10,7 @@ import bench
 import synth
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-FUSED = {"generic", "mfma_small", "mfma_wide1", "mfma_wide2", "mfma_wide2t"}
+FUSED = {"generic", "mfma_small", "mfma_wide1", "mfma_wide2", "mfma_wide2t", "mfma_wide1s"}
 
 
 def _records():
@@ -33,6 +33,9 @@ def test_workload_lookup_takes_the_fused_kernels_own_summary():
     for key, w in synth.WORKLOADS.items():
         info = bench.profile_info(w)
         assert info is None or (info["kernel"] in FUSED and info["workload"] == w.name), (key, info)
+        for k in FUSED:  # a lookup for one kernel never returns another kernel's summary
+            ik = bench.profile_info(w, kernel=k)
+            assert ik is None or (ik["kernel"] == k and ik["workload"] == w.name), (key, k, ik)
         deq = bench.profile_info(w, "dequant")
         assert deq is None or (deq["kernel"] == "dequant" and deq["workload"] == w.name), (key, deq)
 
