@@ -213,14 +213,16 @@ def test_padded_per_group_on_the_small_kernel(M, N, two_sided, dmax, K):
 
 
 def test_zero_input_gives_zero_scale_and_codes():
-    for mode, dmax in (("int32", 0.0), ("fp4", 0.0), ("fp4", 8.0)):
-        x = np.zeros((4, 64, 64), np.uint16)
-        p = synth.gen_orthogonal(64, "bf16", 0, 2)
+    for n, mode, dmax, two in ((64, "int32", 0.0, True), (64, "fp4", 0.0, True), (64, "fp4", 8.0, True),
+                               (256, "fp4", 0.0, False), (256, "fp4", 8.0, False)):
+        x = np.zeros((4, n, n), np.uint16)
+        p = synth.gen_orthogonal(n, "bf16", 0, 2)
         xd, pd = to_dev(x, "bf16"), to_dev(p, "bf16")
-        for k in supported_kernels(xd, pd, pd, mode, 1.0, dmax):
-            out, sc = run_lib(xd, pd, pd, mode, 1.0, dmax, k)
+        p2d = pd if two else None
+        for k in supported_kernels(xd, pd, p2d, mode, 1.0, dmax):
+            out, sc = run_lib(xd, pd, p2d, mode, 1.0, dmax, k)
             packed, scale = fetch(out, sc, mode, 4)
-            assert (packed == 0).all() and (scale == 0).all()
+            assert (packed == 0).all() and (scale == 0).all(), (n, mode, dmax, two, k)
 
 
 @pytest.mark.parametrize("key", ["c2", "c3", "c4", "c5"])
@@ -341,18 +343,20 @@ def test_v1_form_runs_like_v2_with_dst_type_max_zero(key):
     assert np.array_equal(ref[0], got[0]) and np.array_equal(ref[1], got[1])
 
 
-@pytest.mark.parametrize("M,N,mode", [(64, 64, "int4"), (33, 40, "int32"), (64, 128, "fp4"), (256, 256, "int4"),
-                                      (64, 64, "e4m3")])
-def test_strided_x_in_place_or_gathered(M, N, mode):
+@pytest.mark.parametrize("M,N,mode,two_sided", [(64, 64, "int4", True), (33, 40, "int32", True),
+                                                (64, 128, "fp4", True), (256, 256, "int4", True),
+                                                (64, 64, "e4m3", True), (256, 256, "fp4", False)])
+def test_strided_x_in_place_or_gathered(M, N, mode, two_sided):
     """x as a view with padded rows and padded slices (read in place by the generic and
-    one-wave-per-slice kernels, gathered for the 256-class kernel), and with a non-unit
+    one-wave-per-slice kernels, gathered for the 256-class kernels), and with a non-unit
     innermost stride (always gathered): the codes and scales equal those of a contiguous x."""
     dt = "bf16"
     K = 9
-    x, p1, p2 = _inputs(M, N, dt, K, seed=M * 7 + N)
+    x, p1, p2 = _inputs(M, N, dt, K, seed=M * 7 + N, two_sided=two_sided)
     if mode == "int32" and N % 8:
         pytest.skip("INT32 needs N % 8 == 0")
-    xd, p1d, p2d = to_dev(x, dt), to_dev(p1, dt), to_dev(p2, dt)
+    xd, p1d = to_dev(x, dt), to_dev(p1, dt)
+    p2d = to_dev(p2, dt) if two_sided else None
     ref = fetch(*run_lib(xd, p1d, p2d, mode, 0.9, 0.0), mode, K)
     big = torch.zeros((K + 1, M + 3, N + 8), dtype=xd.dtype, device=DEV)
     big[:K, :M, :N] = xd
