@@ -553,3 +553,28 @@ def test_int4_gemm_arguments():
     ]
     for args in bad:
         assert fq.fq_int4_gemm(*args, 0) == INVAL
+
+
+@pytest.mark.parametrize("M,N,mode,p2_empty,auto,accepts", [
+    (256, 256, "fp4", True, 5, {1, 3, 5}),       # left-only E2M1: the streaming kernel
+    (256, 256, "fp4", False, 3, {1, 3}),         # two-sided E2M1: the whole-workgroup kernel
+    (256, 256, "int4", False, 4, {1, 3, 4}),     # two-sided per-token int4: the pipelined kernel
+    (256, 256, "int8", False, 3, {1, 3}),
+    (128, 256, "fp4", True, 1, {1}),             # 256-class kernels need M = N = 256
+    (128, 128, "fp4", True, 2, {1, 2}),
+])
+def test_256_class_kernels_by_mode_and_transforms(M, N, mode, p2_empty, auto, accepts):
+    """Which variants accept a plan (fq_executor_set_kernel returns success) and which one the
+    automatic choice takes: the streaming kernel (5) only for 256 x 256 slices with an empty
+    P2 and E2M1 codes."""
+    p = problem(3, M, N, mode=mode, p2_empty=p2_empty)
+    st, ws, ex = fq.fq_get_workspace_size(p["x"], p["p1"], p["p2"], 1.0, 0.0, p["out"], p["sc"])
+    assert st == OK
+    try:
+        assert fq.fq_executor_kernel(ex) == auto
+        for k in range(1, 6):
+            got = fq.fq_executor_set_kernel(ex, k)
+            assert (got == OK) == (k in accepts), (k, got)
+        assert fq.fq_executor_set_kernel(ex, 0) == OK and fq.fq_executor_kernel(ex) == auto
+    finally:
+        fq.fq_executor_destroy(ex)
