@@ -399,3 +399,14 @@ def test_streaming_left_only_kernel_writes_every_slice(K):
             assert rep["ok"], rep["errors"]
     finally:
         ex.destroy()
+
+
+@pytest.mark.parametrize("dt,dmax", [("f16", 6.0), ("bf16", 0.0)])
+def test_streaming_left_only_kernel_other_dtype_and_rules(dt, dmax):
+    """The streaming 256 x 256 left-only kernel on K = 257 slices (some workgroups take two)
+    in fp16 with the V2 rule by division (dstTypeMax 6) and in bf16 with the V1 rule, every
+    slice compared with the oracle."""
+    K = 257
+    x, p1, _ = _inputs(256, 256, dt, K, seed=11, dist="laplace", frac=0.01, scale=30.0, two_sided=False)
+    rep = check(x, p1, None, dt, "fp4", 1.0, dmax, kernel=fq.KERNEL_MFMA_WIDE_L, label=f"streaming {dt} dmax={dmax}")
+    assert rep["ok"], rep["errors"]
