@@ -327,3 +327,34 @@ def test_cancellation_reaches_two_codes_in_fp32_and_is_flagged(dt):
     assert codes == {0, 1}
     assert r["lvl"][0, 0] == 1 and (r["lo"][0, 0], r["hi"][0, 0]) == (0, 1)
     assert (r["lo"][0, 1:] == r["hi"][0, 1:]).all()
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_order_that_loses_three_fp32_steps_is_flagged(dt):
+    """T[0, 0] = 1 + (half a dtype step) + six terms of 2^-24 (half an fp32 step at 1): the
+    exact sum lies 3 fp32 steps above the dtype midpoint 1 + ulp/2, so the correctly rounded T
+    is the dtype value above.  Summed from 1 upwards every 2^-24 is a tie that rounds back to
+    even, and the fp32 sum is the midpoint itself, which rounds half to even to 1.0: one order
+    gives the other T, and with it the other int4 code.  Brute force over every order
+    confirms both; the oracle's range must contain both.  The fp32 error bound gamma_8 times
+    the terms' magnitude is about 4.2 fp32 steps here and the error is 3 steps, so a bound
+    of half the size (2.1 steps) would miss that order."""
+    half_dt = 2.0 ** -(FRAC[dt] + 1)
+    lo_t, hi_t, mid = 1.0, 1.0 + 2 * half_dt, 1.0 + half_dt
+    p = 1.4921875 if dt == "bf16" else 1.4990234375  # p lo_t < 1.5 < p hi_t
+    terms = [lo_t, half_dt] + [2.0 ** -24] * 6
+    sums = _fp32_sums_every_order(terms)
+    assert min(sums) == mid and max(sums) == mid + 3 * 2.0 ** -23
+    assert sorted({float(to_dt(s, dt)) for s in sums}) == [lo_t, hi_t]
+    x = np.zeros((1, 2, 8))
+    x[0, 0, :] = terms
+    x[0, 1, 0] = 7.0                        # y[1, 0] = 7: scale 1
+    p2 = np.eye(8)
+    p2[1:, 0] = 1.0                         # T[0, 0] = sum of row 0
+    p1 = np.diag([p, 1.0])
+    xb, p1b, p2b = rt(x, dt), rt(p1, dt), rt(p2, dt)
+    assert np.array_equal(val(xb, dt), x) and np.array_equal(val(p1b, dt), p1)
+    r = oracle.run(xb, p1b, p2b, dt, "int32", clip_ratio=1.0)
+    assert r["scale"][0] == 1.0
+    assert p * lo_t < 1.5 < p * hi_t
+    assert r["lvl"][0, 0] == 2 and (r["lo"][0, 0], r["hi"][0, 0]) == (1, 2)
