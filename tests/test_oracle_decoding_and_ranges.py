@@ -358,3 +358,39 @@ def test_order_that_loses_three_fp32_steps_is_flagged(dt):
     assert r["scale"][0] == 1.0
     assert p * lo_t < 1.5 < p * hi_t
     assert r["lvl"][0, 0] == 2 and (r["lo"][0, 0], r["hi"][0, 0]) == (1, 2)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_long_sum_that_ties_down_at_every_step_is_flagged(dt):
+    """y[0, 0] = sum over 256 rows of T[m, 0] (P1's first row all ones, P2 = I), per group:
+    the terms 1.25, -2^-19 and -2^-22 form m' = 1.25 - 18 fp32 steps (even), and 253 terms of
+    half an fp32 step follow.  The group's maximum y[0, 1] = 3 is far from a power of two, so
+    its e8m0 scale (0.5) is certain and y[0, 0] / 0.5 sits near the E2M1 decision point 2.5.
+    The exact sum is 1.25 + 108.5 steps (code of 3.0); summed from m' upwards every half step
+    is a tie that rounds back to even and the fp32 sum stays m' (code of 2.0).  Both points
+    lie outside the 1e-6 tie window, so only the fp32 error bound of GEMM2 can reach the
+    lower code: gamma_256 times the terms' magnitude is 160 steps here, half of it (80) would
+    not reach below the decision point."""
+    step = 2.0 ** -23
+    head = [1.25, -(2.0 ** -19), -(2.0 ** -22)]
+    tail = [2.0 ** -24] * 253
+    acc = np.float32(0.0)
+    for t in head + tail:  # one order: m' first, then the ties
+        acc = np.float32(acc + np.float32(t))
+    assert float(acc) == 1.25 - 18 * step
+    exact = sum(head) + sum(tail)
+    assert exact == 1.25 + 108.5 * step
+    assert abs(float(acc) - 1.25) > 1e-6 * 1.25 and abs(exact - 1.25) > 1e-6 * 1.25  # outside the tie window
+    M, N = 256, 32
+    x = np.zeros((1, M, N))
+    x[0, :, 0] = head + tail
+    x[0, 1, 1] = 3.0                        # y[0, 1] = 3: group 0's maximum, e8m0 code 126
+    p1 = np.zeros((M, M))
+    p1[0, :] = 1.0
+    xb, p1b, p2b = rt(x, dt), rt(p1, dt), rt(np.eye(N), dt)
+    assert np.array_equal(val(xb, dt), x)
+    r = oracle.run(xb, p1b, p2b, dt, "fp4", dst_type_max=0.0)
+    assert r["e8m0"][0, 0] == 126
+    code = lambda v: [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0].index(v)
+    assert r["lvl"][0, 0] == code(3.0) and (r["lo"][0, 0], r["hi"][0, 0]) == (code(2.0), code(3.0))
+    assert r["ns_tie"][0, 0] == 0  # not flagged by the tie window
