@@ -231,7 +231,9 @@ def test_far_from_every_boundary_gives_one_code(dt, mode):
         assert r["scale"][0] == 1.0 and abs(r["scale_hi"][0] / r["scale_lo"][0] - 1) < 1e-5
     else:
         assert (r["e8m0"][0, :8] == 126).all() and (r["g_lo"] == r["g_hi"]).all()
-        assert (r["alt_lo"] == r["alt_hi"]).all() or True  # the alternative code is the code itself
+        # no alternative scale: the alternative pass is the primary one
+        assert (r["g_alt"] == r["e8m0"][:, :r["g_alt"].shape[1]]).all()
+        assert (r["alt_lvl"] == r["lvl"]).all() and (r["alt_lo"] == r["lo"]).all() and (r["alt_hi"] == r["hi"]).all()
 
 
 def _fp32_sums_every_order(terms):
@@ -394,3 +396,30 @@ def test_long_sum_that_ties_down_at_every_step_is_flagged(dt):
     code = lambda v: [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0].index(v)
     assert r["lvl"][0, 0] == code(3.0) and (r["lo"][0, 0], r["hi"][0, 0]) == (code(2.0), code(3.0))
     assert r["ns_tie"][0, 0] == 0  # not flagged by the tie window
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_group_max_next_to_a_power_of_two_reaches_both_e8m0_codes(dt):
+    """y[0, 0] = 2^1 + 2^0 + ... + 2^-21 = 4 - 2^-21 (P1's first row all ones over x's
+    column of powers of two: every term and every partial sum exact), the maximum of its
+    group, lies within reach of 4 (V1: e8m0 code 126 below 4, 127 at 4); y[0, 1] = 1.  The
+    oracle's code is 126, the reachable range 126 .. 127 with 127 as the alternative, and the
+    codes under both scales are those of y / 2^(code - 127): the maximum saturates to 6 under
+    126 and rounds to 4 under 127; y[0, 1] gives 2 and 1."""
+    M, N = 32, 32
+    x = np.zeros((1, M, N))
+    x[0, :23, 0] = [2.0 ** (1 - m) for m in range(23)]
+    x[0, 0, 1] = 1.0
+    p1 = np.zeros((M, M))
+    p1[0, :] = 1.0
+    xb, p1b, p2b = rt(x, dt), rt(p1, dt), rt(np.eye(N), dt)
+    assert np.array_equal(val(xb, dt), x)
+    assert sum(x[0, :, 0]) == 4.0 - 2.0 ** -21
+    r = oracle.run(xb, p1b, p2b, dt, "fp4", dst_type_max=0.0, want_y=True)
+    assert r["y"][0, 0, 0] == np.float32(4.0 - 2.0 ** -21) and r["y"][0, 0, 1] == 1.0
+    assert r["e8m0"][0, 0] == 126
+    assert (r["g_lo"][0, 0], r["g_hi"][0, 0], r["g_alt"][0, 0]) == (126, 127, 127)
+    code = lambda v: [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0].index(v)
+    assert r["lvl"][0, 0] == code(6.0) and r["alt_lvl"][0, 0] == code(4.0)
+    assert r["lvl"][0, 1] == code(2.0) and r["alt_lvl"][0, 1] == code(1.0)
+    assert (r["lo"][0, :2] == r["hi"][0, :2]).all() and (r["alt_lo"][0, :2] == r["alt_hi"][0, :2]).all()
