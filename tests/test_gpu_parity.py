@@ -410,3 +410,36 @@ def test_streaming_left_only_kernel_other_dtype_and_rules(dt, dmax):
     x, p1, _ = _inputs(256, 256, dt, K, seed=11, dist="laplace", frac=0.01, scale=30.0, two_sided=False)
     rep = check(x, p1, None, dt, "fp4", 1.0, dmax, kernel=fq.KERNEL_MFMA_WIDE_L, label=f"streaming {dt} dmax={dmax}")
     assert rep["ok"], rep["errors"]
+
+
+@pytest.mark.parametrize("mode,two_sided,dmax,kernel", [("int4", True, 0.0, fq.KERNEL_MFMA_WIDE_T),
+                                                       ("fp4", True, 8.0, fq.KERNEL_MFMA_WIDE),
+                                                       ("fp4", False, 8.0, fq.KERNEL_MFMA_WIDE_L)])
+def test_256_class_kernels_past_four_gigabytes_of_x(mode, two_sided, dmax, kernel):
+    """K = 40000 slices of 256 x 256 (x spans 5.2 GB: slice offsets pass 2^31 elements and
+    2^32 bytes from slice 32768 on), x drawn on the device from a seeded normal distribution;
+    the slices on both sides of those boundaries and the last ones are compared with the
+    oracle (their x copied back)."""
+    K, M, N, dt = 40000, 256, 256, "bf16"
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(7)
+    xd = torch.randn((K, M, N), generator=gen, device=DEV, dtype=torch.float32).to(torch.bfloat16)
+    p1 = synth.gen_orthogonal(M, dt, 7, 2)
+    p2 = synth.gen_orthogonal(N, dt, 7, 3) if two_sided else None
+    p1d, p2d = to_dev(p1, dt), (to_dev(p2, dt) if two_sided else None)
+    out, sc = fq.empty_outputs(K, M, N, mode, DEV)
+    ex = fq.Executor(xd, p1d, p2d, out, sc, mode, 0.95 if mode == "int4" else 1.0, dmax, kernel=kernel)
+    assert ex.kernel == kernel
+    say(f"[gpu] K={K} 256x256 {mode} two_sided={two_sided} kernel {kernel}")
+    try:
+        ex.run()
+        torch.cuda.synchronize()
+    finally:
+        ex.destroy()
+    slices = [0, 1, 32767, 32768, 32769, 39743, 39744, 39998, 39999]
+    xs = xd[slices].view(torch.int16).cpu().numpy().view(np.uint16)
+    del xd
+    packed, scale = fetch(out, sc, mode, K)
+    orc = oracle.run(xs, p1, p2, dt, mode, 0.95 if mode == "int4" else 1.0, dmax, nthreads=8)
+    rep = compare(orc, packed[slices], scale[slices])
+    assert rep["ok"], rep["errors"]
