@@ -412,15 +412,17 @@ def test_streaming_left_only_kernel_other_dtype_and_rules(dt, dmax):
     assert rep["ok"], rep["errors"]
 
 
-@pytest.mark.parametrize("mode,two_sided,dmax,kernel", [("int4", True, 0.0, fq.KERNEL_MFMA_WIDE_T),
-                                                       ("fp4", True, 8.0, fq.KERNEL_MFMA_WIDE),
-                                                       ("fp4", False, 8.0, fq.KERNEL_MFMA_WIDE_L)])
-def test_256_class_kernels_past_four_gigabytes_of_x(mode, two_sided, dmax, kernel):
-    """K = 40000 slices of 256 x 256 (x spans 5.2 GB: slice offsets pass 2^31 elements and
-    2^32 bytes from slice 32768 on), x drawn on the device from a seeded normal distribution;
-    the slices on both sides of those boundaries and the last ones are compared with the
-    oracle (their x copied back)."""
-    K, M, N, dt = 40000, 256, 256, "bf16"
+@pytest.mark.parametrize("M,N,K,mode,two_sided,dmax,kernel", [
+    (256, 256, 40000, "int4", True, 0.0, fq.KERNEL_MFMA_WIDE_T),
+    (256, 256, 40000, "fp4", True, 8.0, fq.KERNEL_MFMA_WIDE),
+    (256, 256, 40000, "fp4", False, 8.0, fq.KERNEL_MFMA_WIDE_L),
+    (128, 128, 262144, "int4", True, 0.0, fq.KERNEL_MFMA_SMALL)])
+def test_kernels_past_four_gigabytes_of_x(M, N, K, mode, two_sided, dmax, kernel):
+    """x spanning more than 4 GB (5.2 GB for 40000 slices of 256 x 256, 8.6 GB for 262144 of
+    128 x 128: slice offsets pass 2^31 elements and 2^32 bytes), drawn on the device from a
+    seeded normal distribution; the slices on both sides of those offsets and the last ones
+    are compared with the oracle (their x copied back)."""
+    dt = "bf16"
     gen = torch.Generator(device=DEV)
     gen.manual_seed(7)
     xd = torch.randn((K, M, N), generator=gen, device=DEV, dtype=torch.float32).to(torch.bfloat16)
@@ -436,7 +438,8 @@ def test_256_class_kernels_past_four_gigabytes_of_x(mode, two_sided, dmax, kerne
         torch.cuda.synchronize()
     finally:
         ex.destroy()
-    slices = [0, 1, 32767, 32768, 32769, 39743, 39744, 39998, 39999]
+    b31 = (1 << 31) // (M * N)  # the first slice at 2^31 elements (2^32 bytes)
+    slices = sorted({0, 1, b31 - 1, b31, b31 + 1, K - 257, K - 256, K - 2, K - 1})
     xs = xd[slices].view(torch.int16).cpu().numpy().view(np.uint16)
     del xd
     packed, scale = fetch(out, sc, mode, K)
