@@ -446,3 +446,9 @@ def test_kernels_past_four_gigabytes_of_x(M, N, K, mode, two_sided, dmax, kernel
     orc = oracle.run(xs, p1, p2, dt, mode, 0.95 if mode == "int4" else 1.0, dmax, nthreads=8)
     rep = compare(orc, packed[slices], scale[slices])
     assert rep["ok"], rep["errors"]
+    # the dequantized values of the same outputs (2 bytes an element: past 4 GB as well)
+    vals = fq.dequantize(out, sc, mode, M, N, torch.bfloat16)
+    torch.cuda.synchronize()
+    got = vals[slices].view(torch.int16).cpu().numpy().view(np.uint16)
+    want = oracle.dequant(packed[slices], scale[slices], M, N, dt, mode)
+    assert np.array_equal(got, want)
