@@ -15,6 +15,13 @@
 //     MFMAs) -- the full intermediate T never exists;
 //   * y (256 x 64 per wave, fp32) stays in registers; per token, max|y| is reduced across
 //     the 4 waves through LDS; per group, a 32-group is 8 neighbouring lanes of one row.
+// PAD: a slice of M x N elements with a side above 128 (M, N <= 256, N a multiple of 8; of
+// 32 per group, so that 32-groups stay inside rows) runs in the two-sided kernel at
+// 256 x 256: P1 and P2 are staged with zero rows and columns past their own sizes (an empty
+// P2 as the identity: T = RNE(x * 1) = x exactly), x's rows and columns past the slice's
+// read zeros through the bounded loads, so the padded y is the real one bordered by zeros
+// (max|y| and every group maximum unchanged), and only the real rows and columns of the
+// codes and e8m0 bytes are stored, at the slice's own row pitch.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -39,7 +46,8 @@ constexpr int kStoreNT = 2;
 
 // CLAMP (per token): the int4 or INT8 clamp is compiled in.  SV (per group): the e8m0 rule.  Q (per
 // token): 0 for int4 codes, else the 8-bit mode (kPerTokenInt8 / E4M3 / E5M2), one byte a code.
-template <int DT, bool PG, bool CLAMP, int SV, int Q>
+// PAD: pb.M x pb.N slices padded to 256 x 256 (see above).
+template <int DT, bool PG, bool CLAMP, int SV, int Q, bool PAD>
 __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb, Buffers b) {
   __shared__ u32x4_t frag1[kIT * kNChunk * 64];   // 128 KB: P1 A fragments
   // 2 x 16 KB: x chunks in GEMM1 A-fragment order.  The 16-byte slot q = 4ks + g of chunk
@@ -58,7 +66,23 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb,
 
   // ---- P1 -> LDS fragments: P1[i, m] -> frag1[(it*8 + ch)*64 + 16*gg + i%16] element t,
   // m = 32ch + (t < 4 ? 4gg + t : 16 + 4gg + t - 4) ----
-  {
+  // the slice's own sizes (256 when not padded)
+  const int Mr = PAD ? static_cast<int>(pb.M) : kW, Nr = PAD ? static_cast<int>(pb.N) : kW;
+  if constexpr (PAD) {
+    // element by element, zero past P1's own Mr x Mr
+    uint16_t* f1 = reinterpret_cast<uint16_t*>(frag1);
+    for (int ch16 = tid; ch16 < kW * kW / 8; ch16 += kWideThreads) {
+      const int i = ch16 >> 5, m0 = (ch16 & 31) * 8;
+      const int it = i >> 4, rr = i & 15;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int m = m0 + e, ch = m >> 5, wv = m & 31;
+        const int gg = wv < 16 ? (wv >> 2) : ((wv - 16) >> 2);
+        const int t = wv < 16 ? (wv & 3) : 4 + ((wv - 16) & 3);
+        f1[((it * kNChunk + ch) * 64 + 16 * gg + rr) * 8 + t] = (i < Mr && m < Mr) ? b.p1[i * Mr + m] : uint16_t(0);
+      }
+    }
+  } else {
     uint16_t* f1 = reinterpret_cast<uint16_t*>(frag1);
     for (int base = 0; base < kW * kW / 8; base += kWideThreads * 4) {
       u32x4_t r[4];
@@ -83,16 +107,35 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb,
   // ---- this wave's P2 strip as GEMM1 B fragments: p2f[ks][nt] element t =
   // P2[32ks + 8g + t, 64w + 4c + nt] ----
   u32x4_t p2f[kW / 32][kNT];
+  if constexpr (PAD) {
+    // zero past P2's own Nr x Nr; an empty P2 is the identity
+    const uint16_t one = DT == kBF16 ? uint16_t(0x3F80) : uint16_t(0x3C00);
+    auto p2v = [&](int j, int n) -> uint32_t {
+      if (j >= Nr || n >= Nr) return 0u;
+      return pb.two_sided ? uint32_t(b.p2[j * Nr + n]) : (j == n ? uint32_t(one) : 0u);
+    };
 #pragma unroll
-  for (int ks = 0; ks < kW / 32; ++ks)
+    for (int ks = 0; ks < kW / 32; ++ks)
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) {
-      const uint16_t* col = b.p2 + (32 * ks + 8 * g) * kW + 64 * w + 4 * c + nt;
-      uint32_t v[4];
+      for (int nt = 0; nt < kNT; ++nt) {
+        const int j0 = 32 * ks + 8 * g, n = 64 * w + 4 * c + nt;
+        uint32_t v[4];
 #pragma unroll
-      for (int p = 0; p < 4; ++p) v[p] = uint32_t(col[(2 * p) * kW]) | (uint32_t(col[(2 * p + 1) * kW]) << 16);
-      p2f[ks][nt] = u32x4_t{v[0], v[1], v[2], v[3]};
-    }
+        for (int p = 0; p < 4; ++p) v[p] = p2v(j0 + 2 * p, n) | (p2v(j0 + 2 * p + 1, n) << 16);
+        p2f[ks][nt] = u32x4_t{v[0], v[1], v[2], v[3]};
+      }
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < kW / 32; ++ks)
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) {
+        const uint16_t* col = b.p2 + (32 * ks + 8 * g) * kW + 64 * w + 4 * c + nt;
+        uint32_t v[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) v[p] = uint32_t(col[(2 * p) * kW]) | (uint32_t(col[(2 * p + 1) * kW]) << 16);
+        p2f[ks][nt] = u32x4_t{v[0], v[1], v[2], v[3]};
+      }
+  }
 
   // Chunk j of the workgroup: slice blockIdx.x + (j / 8) * gridDim.x, x rows 32 * (j % 8) ..
   // Load h of wave w covers chunk rows 8h + 4(w/2) .. +3, slots 16(w%2) .. +15: lane l takes
@@ -104,6 +147,23 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb,
   auto load_chunk = [&](int64_t j, u32x4_t* r) {
     const int64_t slice = blockIdx.x + (j >> 3) * stride;
     const bool in = slice < pb.K;
+    if constexpr (PAD) {
+      // a resource over the whole slice; the lane's row (32 (j % 8) + 8h + 4 (w/2) + l%4) and
+      // 16-byte piece (columns 8 (16 (w%2) + l/4) ..) in the offset, sent past the range
+      // (zeros, no memory access) for rows and columns past the slice's own
+      const int bytes = Mr * Nr * 2;
+      const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(b.x + (in ? slice : 0) * (int64_t(Mr) * Nr)),
+                                                          static_cast<int16_t>(0), in ? bytes : 0, kBufferWord3);
+      const int row0 = kChunk * static_cast<int>(j & 7) + 4 * (w >> 1) + (lane & 3);
+      const int col = 8 * (16 * (w & 1) + (lane >> 2));
+#pragma unroll
+      for (int h = 0; h < XR; ++h) {
+        const int row = row0 + 8 * h;
+        const int off = (row < Mr && col < Nr) ? (row * Nr + col) * 2 : bytes;
+        r[h] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
+      }
+      return;
+    }
     const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(b.x + (in ? slice : 0) * (kW * kW) + (j & 7) * (kChunk * kW)),
         static_cast<int16_t>(0), in ? kChunk * kW * 2 : 0, kBufferWord3);
@@ -240,11 +300,32 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb,
   auto epilogue = [&]() {
     agpr_fence<16>(y);
     constexpr int kCodeB = Q ? kW * kW : kW * kW / 2;  // code bytes of a slice
-    const auto rs_codes = __builtin_amdgcn_make_buffer_rsrc(b.codes + s * kCodeB, static_cast<int16_t>(0), kCodeB,
+    const int code_bytes = PAD ? (Q ? Mr * Nr : Mr * Nr / 2) : kCodeB;
+    const auto rs_codes = __builtin_amdgcn_make_buffer_rsrc(b.codes + s * code_bytes, static_cast<int16_t>(0), code_bytes,
                                                             kBufferWord3);
-    // the lane's 4 codes of a row are columns 64 w + 4 c .. +3
-    int code_off = Q ? 4 * g * kW + 64 * w + 4 * c : 4 * g * (kW / 2) + 32 * w + 2 * c;
-    asm volatile("" : "+v"(code_off));
+    // the lane's 4 codes of a row are columns 64 w + 4 c .. +3 (PAD: the column bytes alone;
+    // the row goes into the offset below)
+    int code_off = PAD ? (Q ? 64 * w + 4 * c : 32 * w + 2 * c)
+                       : (Q ? 4 * g * kW + 64 * w + 4 * c : 4 * g * (kW / 2) + 32 * w + 2 * c);
+    int prow = 4 * g;  // the lane's row in a tile, less r0
+    if constexpr (PAD)
+      asm volatile("" : "+v"(code_off), "+v"(prow));
+    else
+      asm volatile("" : "+v"(code_off));
+    // store offsets of the lane's codes of row r0 + 4g (r0 = 16 it + i): vector and scalar
+    // part; PAD: the whole offset in the vector part, past the range (no store) for rows and
+    // columns past the slice's own
+    auto cvo = [&](int r0) -> int {
+      if constexpr (PAD)
+        return (r0 + prow < Mr && 64 * w + 4 * c < Nr) ? (r0 + prow) * (Q ? Nr : Nr / 2) + code_off : code_bytes;
+      else
+        return code_off;
+    };
+    auto cso = [&](int r0) -> int { return PAD ? 0 : r0 * (Q ? kW : kW / 2); };
+    // PAD: cached stores (a row of a narrower slice leaves runs shorter than a cache line,
+    // which non-temporal stores write to HBM as partial lines: 1.4x the code bytes measured
+    // at 224 x 128)
+    constexpr int kSt = PAD ? 0 : kStoreNT;
     if constexpr (!PG) {
       // [FQV2] 第3步 pertoken: max|y| over the slice (4 waves), scale, codes.  The partial
       // maxima pass through xs[1], which held the slice's last chunk (every wave finished
@@ -281,7 +362,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb,
           for (int i = 0; i < 4; ++i) {
             const int r0 = 16 * it + i;  // row - 4g
             const uint32_t v = code8x4<Q, CLAMP>(y[it][0][i], y[it][1][i], y[it][2][i], y[it][3][i], inv);
-            __builtin_amdgcn_raw_buffer_store_b32(v, rs_codes, code_off, r0 * kW, kStoreNT);
+            __builtin_amdgcn_raw_buffer_store_b32(v, rs_codes, cvo(r0), cso(r0), kSt);
             if (i == 3) __builtin_amdgcn_sched_barrier(0);
           }
       } else {
@@ -293,17 +374,31 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb,
           const uint32_t b0 = pair_byte(int4_biased<CLAMP>(y[it][0][i], inv), int4_biased<CLAMP>(y[it][1][i], inv));
           const uint32_t b1 = pair_byte(int4_biased<CLAMP>(y[it][2][i], inv), int4_biased<CLAMP>(y[it][3][i], inv));
           __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(unbias(__builtin_amdgcn_perm(b1, b0, 0x0C0C0400u))),
-                                                rs_codes, code_off, r0 * (kW / 2), kStoreNT);
+                                                rs_codes, cvo(r0), cso(r0), kSt);
           if (i == 3) __builtin_amdgcn_sched_barrier(0);
         }
       }
     } else {
       // [FQV2] 第3步 pergroup / 第4步: a 32-group is 8 neighbouring lanes of one row
-      const auto rs_e8 = __builtin_amdgcn_make_buffer_rsrc(
-          static_cast<uint8_t*>(b.scale) + s * e8m0_bytes_per_slice(kW * kW), static_cast<int16_t>(0),
-          static_cast<int>(e8m0_bytes_per_slice(kW * kW)), kBufferWord3);
-      int e8_off = 4 * g * (kW / 32) + 2 * w + (c >> 3);
+      const int e8_bytes = static_cast<int>(e8m0_bytes_per_slice(int64_t(Mr) * Nr));
+      const auto rs_e8 = __builtin_amdgcn_make_buffer_rsrc(static_cast<uint8_t*>(b.scale) + s * e8_bytes,
+                                                           static_cast<int16_t>(0), e8_bytes, kBufferWord3);
+      int e8_off = PAD ? 2 * w + (c >> 3) : 4 * g * (kW / 32) + 2 * w + (c >> 3);
       asm volatile("" : "+v"(e8_off));
+      // the group's e8m0 byte of row r0 + 4g (PAD: whole offset, past the range for rows
+      // and groups past the slice's own)
+      auto evo = [&](int r0) -> int {
+        if constexpr (PAD)
+          return (r0 + prow < Mr && 64 * w + 32 * (c >> 3) < Nr) ? (r0 + prow) * (Nr / 32) + e8_off : e8_bytes;
+        else
+          return e8_off;
+      };
+      auto eso = [&](int r0) -> int { return PAD ? 0 : r0 * (kW / 32); };
+      if constexpr (PAD) {
+        // an odd count of groups leaves the slice's last e8m0 byte as padding: zero
+        const int groups = Mr * Nr / 32;
+        __builtin_amdgcn_raw_buffer_store_b8(uint8_t(0), rs_e8, (tid == 0 && (groups & 1)) ? groups : e8_bytes, 0, 0);
+      }
 #pragma unroll
       for (int it = 0; it < kIT; ++it)
 #pragma unroll
@@ -316,9 +411,9 @@ __global__ __launch_bounds__(kWideThreads, 1) void mfma_wide2_kernel(Problem pb,
           const float sc = e8m0_to_float(code);
           uint32_t packed = fp4x2<0>(0u, y[it][0][i], y[it][1][i], sc);
           packed = fp4x2<1>(packed, y[it][2][i], y[it][3][i], sc);
-          __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(packed), rs_codes, code_off, r0 * (kW / 2), 0);
+          __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(packed), rs_codes, cvo(r0), cso(r0), 0);
           // the 8 lanes of a group hold the same code and all store it (no branch)
-          __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(code), rs_e8, e8_off, r0 * (kW / 32), 0);
+          __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(code), rs_e8, evo(r0), eso(r0), 0);
         }
     }
   };
@@ -550,7 +645,7 @@ hipError_t launch_w1(const Problem& pb, const Buffers& b, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int DT, bool PG, bool CLAMP, int SV, int Q = 0>
+template <int DT, bool PG, bool CLAMP, int SV, int Q, bool PAD>
 hipError_t launch_w2(const Problem& pb, const Buffers& b, hipStream_t s) {
   static int cus = 0;
   if (cus == 0) {
@@ -560,30 +655,30 @@ hipError_t launch_w2(const Problem& pb, const Buffers& b, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   const int grid = static_cast<int>(pb.K < cus ? pb.K : cus);
-  mfma_wide2_kernel<DT, PG, CLAMP, SV, Q><<<grid, kWideThreads, 0, s>>>(pb, b);
+  mfma_wide2_kernel<DT, PG, CLAMP, SV, Q, PAD><<<grid, kWideThreads, 0, s>>>(pb, b);
   return hipGetLastError();
 }
 
-template <int DT>
+template <int DT, bool PAD>
 hipError_t dispatch_w2(const Problem& pb, const Buffers& b, hipStream_t s) {
   if (pb.mode == kPerGroupFp4) {
     switch (e8m0_variant(pb)) {
-      case kE8V1: return launch_w2<DT, true, false, kE8V1>(pb, b, s);
-      case kE8V2Pow2: return launch_w2<DT, true, false, kE8V2Pow2>(pb, b, s);
-      default: return launch_w2<DT, true, false, kE8V2Div>(pb, b, s);
+      case kE8V1: return launch_w2<DT, true, false, kE8V1, 0, PAD>(pb, b, s);
+      case kE8V2Pow2: return launch_w2<DT, true, false, kE8V2Pow2, 0, PAD>(pb, b, s);
+      default: return launch_w2<DT, true, false, kE8V2Div, 0, PAD>(pb, b, s);
     }
   }
   switch (pb.mode) {
     case kPerTokenInt8:
       // The INT8 clamp can only bite when (127/clipRatio) * (1 + 4 ulp) reaches 127.5.
-      if (pb.d >= 127.4999f) return launch_w2<DT, false, true, kE8V1, kPerTokenInt8>(pb, b, s);
-      return launch_w2<DT, false, false, kE8V1, kPerTokenInt8>(pb, b, s);
-    case kPerTokenE4M3: return launch_w2<DT, false, false, kE8V1, kPerTokenE4M3>(pb, b, s);
-    case kPerTokenE5M2: return launch_w2<DT, false, false, kE8V1, kPerTokenE5M2>(pb, b, s);
+      if (pb.d >= 127.4999f) return launch_w2<DT, false, true, kE8V1, kPerTokenInt8, PAD>(pb, b, s);
+      return launch_w2<DT, false, false, kE8V1, kPerTokenInt8, PAD>(pb, b, s);
+    case kPerTokenE4M3: return launch_w2<DT, false, false, kE8V1, kPerTokenE4M3, PAD>(pb, b, s);
+    case kPerTokenE5M2: return launch_w2<DT, false, false, kE8V1, kPerTokenE5M2, PAD>(pb, b, s);
     default: break;
   }
-  if (pb.d >= 7.4999f) return launch_w2<DT, false, true, kE8V1>(pb, b, s);
-  return launch_w2<DT, false, false, kE8V1>(pb, b, s);
+  if (pb.d >= 7.4999f) return launch_w2<DT, false, true, kE8V1, 0, PAD>(pb, b, s);
+  return launch_w2<DT, false, false, kE8V1, 0, PAD>(pb, b, s);
 }
 
 template <int DT>
@@ -597,15 +692,27 @@ hipError_t dispatch_w1(const Problem& pb, const Buffers& b, hipStream_t s) {
 
 }  // namespace
 
+namespace {
+// M x N slices that run padded to 256 x 256: a side above 128 (smaller ones fit the
+// one-wave-per-slice kernel), N a multiple of 8 (16-byte x pieces inside rows), per group a
+// multiple of 32 (32-groups inside rows, as in the padded layout).
+bool wide_padded_shape(const Problem& pb) {
+  return (pb.M > 128 || pb.N > 128) && pb.M <= kW && pb.N <= kW && !(pb.M == kW && pb.N == kW) && pb.N % 8 == 0 &&
+         (pb.mode != kPerGroupFp4 || pb.N % 32 == 0);
+}
+}  // namespace
+
 bool mfma_wide_supports(const Problem& pb) {
   // two-sided: every mode; left-only: per group (the only mode an empty P2 is valid for)
-  return pb.M == kW && pb.N == kW && (pb.two_sided || pb.mode == kPerGroupFp4);
+  return (pb.M == kW && pb.N == kW && (pb.two_sided || pb.mode == kPerGroupFp4)) || wide_padded_shape(pb);
 }
 
 hipError_t launch_mfma_wide(const Problem& pb, const Buffers& b, hipStream_t s) {
   if (!mfma_wide_supports(pb)) return hipErrorNotSupported;
+  if (wide_padded_shape(pb))  // both sides, an empty P2 as the identity
+    return pb.dtype == kBF16 ? dispatch_w2<kBF16, true>(pb, b, s) : dispatch_w2<kF16, true>(pb, b, s);
   if (!pb.two_sided) return pb.dtype == kBF16 ? dispatch_w1<kBF16>(pb, b, s) : dispatch_w1<kF16>(pb, b, s);
-  return pb.dtype == kBF16 ? dispatch_w2<kBF16>(pb, b, s) : dispatch_w2<kF16>(pb, b, s);
+  return pb.dtype == kBF16 ? dispatch_w2<kBF16, false>(pb, b, s) : dispatch_w2<kF16, false>(pb, b, s);
 }
 
 }  // namespace fq

@@ -247,7 +247,9 @@ fq_status fq_executor_set_repeatable(fq_executor* executor, int32_t repeat);
  * kernel (any shape), 2 = the small-slice MFMA kernel (one wave per slice; M and N up to
  * 128, run at the next of 16, 32, 64, 128 with zero padding where they are not one of
  * them: per token N a multiple of 8, per group N one of 32, 64, 128), 3 = the
- * whole-workgroup MFMA kernel for 256 x 256 slices, 4 = its pipelined form for 256 x 256
+ * whole-workgroup MFMA kernel for 256 x 256 slices, which also takes the slices with a side
+ * above 128 (M, N up to 256; N a multiple of 8, per group of 32), zero-padded to 256 x 256
+ * (an empty P2 as the identity), 4 = its pipelined form for 256 x 256
  * slices with both transforms and per-token int4 codes (INT32 / INT4 out; the automatic
  * choice there), 5 = the streaming MFMA kernel for 256 x 256 slices with an empty P2 and
  * FLOAT4_E2M1 out (x through an LDS ring filled by DMA, P1 in registers; the automatic

@@ -3,8 +3,8 @@
 Modes: "int32" = per-token int4 packed 8 per int32 word [K, M, N/8]; "int4" = per-token
 int4 packed 2 per byte [K, M, N]; "fp4" = per-group-32 E2M1 [K, M*N] with e8m0 scales
 [K, ceilDiv(M*N, 64), 2]; "int8" / "e4m3" / "e5m2" = per-token 8-bit codes [K, M, N].
-The last five run the 64 x 64 and the two-sided 256 x 256 activation workloads with 8-bit
-codes.  Transform matrices are Haar-random orthogonal matrices rounded
+The next five run the 64 x 64 and the two-sided 256 x 256 activation workloads with 8-bit
+codes; the last has a side above 128.  Transform matrices are Haar-random orthogonal matrices rounded
 to the activation dtype; ``two_sided=False`` passes an empty [0, 0] right transform.
 """
 from __future__ import annotations
@@ -57,4 +57,8 @@ WORKLOADS = {
                      "gauss", 0.01, 20.0, "int8", 1.0, 0.0),
     "c4e4m3": Workload("K32768_M256_N256_bf16_out1pct_x20_fp8e4m3_clip1.0", 32768, 256, 256, "bf16",
                        "gauss", 0.01, 20.0, "e4m3", 1.0, 0.0),
+    # a side above 128: hidden 28672 as 224 x 128 (the MLP width of a 70B-class model), which
+    # runs padded to 256 x 256
+    "p224": Workload("K16384_M224_N128_bf16_out1pct_x20_int32_clip0.9", 16384, 224, 128, "bf16", "gauss",
+                     0.01, 20.0, "int32", 0.9, 0.0),
 }

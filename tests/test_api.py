@@ -83,18 +83,22 @@ def test_pipelined_kernel_plans_a_slice_counter(mode, p2_empty, ws):
 
 @pytest.mark.parametrize("M,N,mode,kernel", [(64, 64, "int32", 2), (64, 128, "int4", 2), (128, 64, "int32", 2),
                                             (64, 128, "int8", 2), (128, 128, "int32", 2), (128, 128, "fp4", 2),
-                                            (64, 128, "fp4", 2), (86, 128, "int4", 2), (128, 256, "fp4", 1),
-                                            (112, 128, "int4", 2), (128, 128, "e4m3", 2), (128, 136, "int32", 1),
+                                            (64, 128, "fp4", 2), (86, 128, "int4", 2), (128, 256, "fp4", 3),
+                                            (112, 128, "int4", 2), (128, 128, "e4m3", 2), (128, 136, "int32", 3),
                                             (17, 24, "int32", 2), (86, 64, "int4", 2), (33, 40, "int8", 2),
                                             (3, 8, "int32", 2), (40, 120, "e5m2", 2), (17, 34, "int4", 1),
-                                            (33, 30, "int4", 1), (129, 64, "int32", 1), (17, 32, "fp4", 2),
-                                            (86, 128, "fp4", 2), (17, 48, "fp4", 1), (129, 32, "fp4", 1)])
+                                            (33, 30, "int4", 1), (129, 64, "int32", 3), (17, 32, "fp4", 2),
+                                            (86, 128, "fp4", 2), (17, 48, "fp4", 1), (129, 32, "fp4", 3),
+                                            (224, 128, "int4", 3), (256, 200, "e5m2", 3), (3, 256, "int8", 3),
+                                            (200, 130, "int4", 1), (224, 48, "fp4", 1), (130, 34, "int4", 1),
+                                            (256, 96, "fp4", 3)])
 def test_automatic_kernel_by_shape(M, N, mode, kernel):
     """The one-wave-per-slice MFMA kernel takes per-token slices up to 128 x 128 (one wave
     per SIMD above 4096 elements, two passes over GEMM2 above 8192), padded to its sizes when
     N is a multiple of 8, and per-group ones up to 128 x 128 (one wave per SIMD above 8192),
-    M padded when N is 32, 64 or 128; other shapes below 256 x 256 take the generic
-    kernel."""
+    M padded when N is 32, 64 or 128.  Slices with a side above 128 run the two-sided 256 x 256
+    kernel padded, when N is a multiple of 8 (per group: of 32).  Other shapes take the
+    generic kernel."""
     st, ws, ex = fq.fq_get_workspace_size(*[problem(3, M, N, mode=mode)[k] for k in ("x", "p1", "p2")], 1.0, 0.0,
                                           problem(3, M, N, mode=mode)["out"], problem(3, M, N, mode=mode)["sc"])
     assert st == OK
@@ -560,13 +564,16 @@ def test_int4_gemm_arguments():
     (256, 256, "fp4", False, 3, {1, 3}),         # two-sided E2M1: the whole-workgroup kernel
     (256, 256, "int4", False, 4, {1, 3, 4}),     # two-sided per-token int4: the pipelined kernel
     (256, 256, "int8", False, 3, {1, 3}),
-    (128, 256, "fp4", True, 1, {1}),             # 256-class kernels need M = N = 256
+    (128, 256, "fp4", True, 3, {1, 3}),          # a side above 128: padded in the whole-workgroup kernel
+    (224, 128, "int4", False, 3, {1, 3}),        # (the pipelined and streaming kernels need 256 x 256)
+    (200, 48, "fp4", False, 1, {1}),             # per group padding needs N a multiple of 32
     (128, 128, "fp4", True, 2, {1, 2}),
 ])
 def test_256_class_kernels_by_mode_and_transforms(M, N, mode, p2_empty, auto, accepts):
     """Which variants accept a plan (fq_executor_set_kernel returns success) and which one the
     automatic choice takes: the streaming kernel (5) only for 256 x 256 slices with an empty
-    P2 and E2M1 codes."""
+    P2 and E2M1 codes, the pipelined one (4) only for 256 x 256 two-sided per-token int4,
+    the whole-workgroup kernel (3) also for padded slices with a side above 128."""
     p = problem(3, M, N, mode=mode, p2_empty=p2_empty)
     st, ws, ex = fq.fq_get_workspace_size(p["x"], p["p1"], p["p2"], 1.0, 0.0, p["out"], p["sc"])
     assert st == OK

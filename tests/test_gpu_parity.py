@@ -51,6 +51,7 @@ EDGE_PER_TOKEN = [  # (M, N, mode)
     (128, 64, "int32"),  # with (64, 128): one wave per SIMD on the small MFMA kernel
     (86, 64, "int4"), (56, 64, "int32"), (40, 120, "int32"), (9, 8, "int4"),  # padded on it
     (112, 128, "int4"), (86, 128, "int32"), (100, 96, "int4"),  # two passes over GEMM2 on it
+    (224, 128, "int32"), (129, 136, "int4"), (256, 200, "int4"),  # padded on the 256 x 256 kernel
 ]
 
 
@@ -72,6 +73,7 @@ EDGE_PER_GROUP = [  # (M, N, two_sided, dmax)
     (256, 256, False, 8.0), (1, 256, False, 0.0), (256, 2, False, 7.0),
     (128, 128, True, 0.0), (128, 128, False, 8.0),  # one wave per SIMD on the small MFMA kernel
     (86, 128, True, 0.0), (17, 32, False, 8.0), (33, 64, True, 12.0),  # M padded on it
+    (224, 128, True, 0.0), (129, 160, True, 6.0), (256, 96, False, 8.0), (160, 256, False, 0.0),  # padded, 256 x 256
 ]
 
 
@@ -210,6 +212,48 @@ def test_padded_per_group_on_the_small_kernel(M, N, two_sided, dmax, K):
     assert (bo[:G] == 0xA5).all() and (bo[G + nb_out:] == 0xA5).all()
     assert (bs[:G] == 0x5A).all() and (bs[G + nb_sc:] == 0x5A).all()
     # (the pad byte itself: compared with the oracle's zero above through check())
+
+
+@pytest.mark.parametrize("M,N,mode,two_sided,dmax,dt,K", [
+    (224, 128, "int32", True, 0.0, "bf16", 300), (256, 200, "int4", True, 0.0, "f16", 263),
+    (3, 256, "int32", True, 0.0, "bf16", 517), (129, 136, "int8", True, 0.0, "bf16", 77),
+    (200, 248, "e4m3", True, 0.0, "f16", 40), (136, 256, "e5m2", True, 0.0, "bf16", 33),
+    (224, 128, "fp4", True, 0.0, "bf16", 300), (129, 160, "fp4", True, 6.0, "f16", 77),
+    (256, 96, "fp4", False, 8.0, "bf16", 257), (160, 256, "fp4", False, 10.0, "f16", 100),
+])
+def test_padded_shapes_on_the_wide_kernel(M, N, mode, two_sided, dmax, dt, K):
+    """Slices with a side above 128 run the two-sided 256 x 256 MFMA kernel padded (an empty
+    P2 as the identity): every slice against the oracle, at K past the grid (workgroups with
+    one and two slices), and nothing written outside the outputs (4 KB guard bands).  129 x 160
+    per group has an odd count of groups, so each slice ends with the zero pad byte."""
+    clip = 1.0 if mode == "fp4" else 0.9
+    say(f"[gpu] padded wide {M}x{N} {mode} two_sided={two_sided} dmax={dmax} {dt} K={K}")
+    x, p1, p2 = _inputs(M, N, dt, K, seed=M * 1000 + N + 13, dist="laplace" if mode == "fp4" else "gauss",
+                        two_sided=two_sided)
+    xd, p1d = to_dev(x, dt), to_dev(p1, dt)
+    p2d = to_dev(p2, dt) if p2 is not None else None
+    ks = supported_kernels(xd, p1d, p2d, mode, clip, dmax)
+    assert fq.KERNEL_MFMA_WIDE in ks and fq.KERNEL_MFMA_SMALL not in ks
+    rep = check(x, p1, p2, dt, mode, clip, dmax, kernel=fq.KERNEL_MFMA_WIDE, label="padded wide")
+    assert rep["ok"], rep["errors"]
+    G = 4096
+    ref_out, ref_sc = fq.empty_outputs(K, M, N, mode, DEV)
+    nb_out = ref_out.numel() * ref_out.element_size()
+    nb_sc = ref_sc.numel() * ref_sc.element_size()
+    big_o = torch.full((G + nb_out + G,), 0xA5, dtype=torch.uint8, device=DEV)
+    big_s = torch.full((G + nb_sc + G,), 0x5A, dtype=torch.uint8, device=DEV)
+    out = big_o[G:G + nb_out].view(ref_out.dtype).reshape(ref_out.shape)
+    sc = big_s[G:G + nb_sc].view(ref_sc.dtype).reshape(ref_sc.shape)
+    fq.quantize(xd, p1d, p2d, out, sc, mode, clip, dmax, kernel=fq.KERNEL_MFMA_WIDE)
+    torch.cuda.synchronize()
+    bo, bs = big_o.cpu().numpy(), big_s.cpu().numpy()
+    assert (bo[:G] == 0xA5).all() and (bo[G + nb_out:] == 0xA5).all()
+    assert (bs[:G] == 0x5A).all() and (bs[G + nb_sc:] == 0x5A).all()
+    # every output byte was written (the guard value survives nowhere inside the outputs
+    # unless the codes themselves hold it: compare with the run into fresh buffers)
+    o2, s2 = run_lib(xd, p1d, p2d, mode, clip, dmax, fq.KERNEL_MFMA_WIDE)
+    assert np.array_equal(bo[G:G + nb_out], o2.contiguous().view(torch.uint8).reshape(-1).cpu().numpy())
+    assert np.array_equal(bs[G:G + nb_sc], s2.contiguous().view(torch.uint8).reshape(-1).cpu().numpy())
 
 
 def test_zero_input_gives_zero_scale_and_codes():
