@@ -285,6 +285,12 @@ class Executor:
             raise RuntimeError("executor already released")
         s = stream if stream is not None else torch.cuda.current_stream(self._keep[0].device)
         wsp = self.workspace.data_ptr() if self.workspace is not None else 0
+        if self.workspace is not None:
+            # The workspace was allocated on the planning thread's current stream; the
+            # kernels may run on another one.  Tell the caching allocator, so that a
+            # workspace freed right after this call (quantize() drops its executor) is not
+            # handed to work on the allocating stream while these kernels still use it.
+            self.workspace.record_stream(s)
         st = fq_run(wsp, self.workspace_size, self.handle, s.cuda_stream)
         if not self.repeatable:
             self.handle = None

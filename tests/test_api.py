@@ -585,3 +585,43 @@ def test_256_class_kernels_by_mode_and_transforms(M, N, mode, p2_empty, auto, ac
         assert fq.fq_executor_set_kernel(ex, 0) == OK and fq.fq_executor_kernel(ex) == auto
     finally:
         fq.fq_executor_destroy(ex)
+
+
+def test_run_on_another_stream_records_the_workspace_on_it(monkeypatch):
+    """The binding allocates a planned call's workspace (here the slice counter of the
+    256 x 256 per-token kernel) on the planning thread's current stream.  Run on another
+    stream, it must mark the workspace as in use there before the kernels are enqueued, or
+    the caching allocator could hand it to the allocating stream while they still run
+    (quantize() drops its executor, and so the workspace, as soon as it returns)."""
+    import torch
+    K, M, N = 4, 256, 256
+    x = torch.zeros((K, M, N), dtype=torch.bfloat16)
+    p1 = torch.zeros((M, M), dtype=torch.bfloat16)
+    p2 = torch.zeros((N, N), dtype=torch.bfloat16)
+    out, sc = fq.empty_outputs(K, M, N, "int4", device="cpu")
+    ex = fq.Executor(x, p1, p2, out, sc, "int4", 0.95)
+    assert ex.workspace_size > 0 and ex.workspace is not None
+    events = []
+
+    class Workspace:
+        def data_ptr(self):
+            return 0x20000
+
+        def record_stream(self, s):
+            events.append(("record_stream", s))
+
+    class Stream:
+        cuda_stream = 0x1234
+
+    def fake_run(wsp, size, handle, stream):
+        events.append(("fq_run", wsp, size, stream))
+        return fq.FQ_SUCCESS
+
+    side = Stream()
+    ex.workspace = Workspace()
+    monkeypatch.setattr(fq, "fq_run", fake_run)
+    try:
+        ex.run(stream=side)
+    finally:
+        ex.destroy()
+    assert events == [("record_stream", side), ("fq_run", 0x20000, ex.workspace_size, 0x1234)]
