@@ -266,6 +266,11 @@ class Executor:
         self.handle = ex
         self.workspace_size = ws
         self.workspace = torch.empty((max(ws, 1),), dtype=torch.uint8, device=x.device) if ws else None
+        # streams (handles) the caching allocator knows the workspace is used on: the
+        # allocating one, then every other stream a run was enqueued on
+        self._ws_streams = set()
+        if self.workspace is not None and x.device.type == "cuda":
+            self._ws_streams.add(torch.cuda.current_stream(x.device).cuda_stream)
         if repeatable:
             fq_executor_set_repeatable(ex, True)
         self.repeatable = repeatable
@@ -285,12 +290,14 @@ class Executor:
             raise RuntimeError("executor already released")
         s = stream if stream is not None else torch.cuda.current_stream(self._keep[0].device)
         wsp = self.workspace.data_ptr() if self.workspace is not None else 0
-        if self.workspace is not None:
+        if self.workspace is not None and s.cuda_stream not in self._ws_streams:
             # The workspace was allocated on the planning thread's current stream; the
-            # kernels may run on another one.  Tell the caching allocator, so that a
-            # workspace freed right after this call (quantize() drops its executor) is not
-            # handed to work on the allocating stream while these kernels still use it.
+            # kernels may run on another one.  Tell the caching allocator (once per stream:
+            # it keeps the set until the block is freed), so that a workspace freed right
+            # after this call (quantize() drops its executor) is not handed to work on the
+            # allocating stream while these kernels still use it.
             self.workspace.record_stream(s)
+            self._ws_streams.add(s.cuda_stream)
         st = fq_run(wsp, self.workspace_size, self.handle, s.cuda_stream)
         if not self.repeatable:
             self.handle = None

@@ -622,6 +622,8 @@ def test_run_on_another_stream_records_the_workspace_on_it(monkeypatch):
     monkeypatch.setattr(fq, "fq_run", fake_run)
     try:
         ex.run(stream=side)
+        ex.run(stream=side)  # the allocator keeps the stream: no second record
     finally:
         ex.destroy()
-    assert events == [("record_stream", side), ("fq_run", 0x20000, ex.workspace_size, 0x1234)]
+    run = ("fq_run", 0x20000, ex.workspace_size, 0x1234)
+    assert events == [("record_stream", side), run, run]
