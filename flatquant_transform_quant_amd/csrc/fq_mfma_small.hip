@@ -34,6 +34,8 @@
 // current slice's GEMM2 and epilogue run.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "fq_mfma_common.h"
 #include "fq_mfma_pstage.h"
 
@@ -467,7 +469,10 @@ __global__ __launch_bounds__((64 * small_waves<M, N, PG>()),
 template <int DT, int M, int N, bool PG, bool CLAMP, int SV, int Q = 0, bool PAD = false>
 hipError_t launch_one(const Problem& pb, const Buffers& b, hipStream_t s) {
   constexpr int kWaves = small_waves<M, N, PG>(), kThreads = 64 * kWaves;
-  static int grid_cap = 0;  // workgroups that fit the device at once (per instantiation)
+  // workgroups that fit the device at once (per instantiation); first calls from several
+  // threads may race here, and each stores the same value
+  static std::atomic<int> grid_cap_cache{0};
+  int grid_cap = grid_cap_cache.load(std::memory_order_relaxed);
   if (grid_cap == 0) {
     int dev = 0, cus = 0, per_cu = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -477,6 +482,7 @@ hipError_t launch_one(const Problem& pb, const Buffers& b, hipStream_t s) {
                                                        kThreads, 0);
     if (e != hipSuccess) return e;
     grid_cap = cus * (per_cu > 0 ? per_cu : 1);
+    grid_cap_cache.store(grid_cap, std::memory_order_relaxed);
   }
   const int64_t need = (pb.K + kWaves - 1) / kWaves;
   const int grid = static_cast<int>(need < grid_cap ? need : grid_cap);

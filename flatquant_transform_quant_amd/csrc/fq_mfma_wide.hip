@@ -24,6 +24,8 @@
 // codes and e8m0 bytes are stored, at the slice's own row pitch.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include <type_traits>
 
 #include "fq_mfma_common.h"
@@ -633,12 +635,14 @@ __global__ __launch_bounds__(kLeftThreads, 1) void mfma_wide1_kernel(Problem pb,
 
 template <int DT, int SV>
 hipError_t launch_w1(const Problem& pb, const Buffers& b, hipStream_t s) {
-  static int cus = 0;
+  static std::atomic<int> cus_cache{0};  // first calls from several threads may race: each stores the same value
+  int cus = cus_cache.load(std::memory_order_relaxed);
   if (cus == 0) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
+    cus_cache.store(cus, std::memory_order_relaxed);
   }
   const int grid = static_cast<int>(pb.K < cus ? pb.K : cus);
   mfma_wide1_kernel<DT, SV><<<grid, kLeftThreads, 0, s>>>(pb, b);
@@ -647,12 +651,14 @@ hipError_t launch_w1(const Problem& pb, const Buffers& b, hipStream_t s) {
 
 template <int DT, bool PG, bool CLAMP, int SV, int Q, bool PAD>
 hipError_t launch_w2(const Problem& pb, const Buffers& b, hipStream_t s) {
-  static int cus = 0;
+  static std::atomic<int> cus_cache{0};  // first calls from several threads may race: each stores the same value
+  int cus = cus_cache.load(std::memory_order_relaxed);
   if (cus == 0) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
+    cus_cache.store(cus, std::memory_order_relaxed);
   }
   const int grid = static_cast<int>(pb.K < cus ? pb.K : cus);
   mfma_wide2_kernel<DT, PG, CLAMP, SV, Q, PAD><<<grid, kWideThreads, 0, s>>>(pb, b);

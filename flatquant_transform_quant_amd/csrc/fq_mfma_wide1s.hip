@@ -36,6 +36,8 @@
 // issued after it (the DMA loads of the chunks ahead, and an epilogue's stores).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include <type_traits>
 
 #include "fq_mfma_common.h"
@@ -308,12 +310,14 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_wide1s_kernel(Problem pb, Bu
 
 template <int DT, int SV>
 hipError_t launch_w1s(const Problem& pb, const Buffers& b, hipStream_t s) {
-  static int cus = 0;
+  static std::atomic<int> cus_cache{0};  // first calls from several threads may race: each stores the same value
+  int cus = cus_cache.load(std::memory_order_relaxed);
   if (cus == 0) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
+    cus_cache.store(cus, std::memory_order_relaxed);
   }
   const int grid = static_cast<int>(pb.K < cus ? pb.K : cus);
   mfma_wide1s_kernel<DT, SV><<<grid, kThreads, 0, s>>>(pb, b);

@@ -37,6 +37,8 @@
 // the launch ended with the slowest (every workgroup takes the same cycle count).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include <type_traits>
 
 #include "fq_mfma_common.h"
@@ -696,12 +698,14 @@ bool mfma_wide2t_supports(const Problem& pb) {
 hipError_t launch_mfma_wide2t(const Problem& pb, const Buffers& b, hipStream_t s) {
   if (!mfma_wide2t_supports(pb)) return hipErrorNotSupported;
   if (!b.ctr) return hipErrorInvalidValue;
-  static int cus = 0;
+  static std::atomic<int> cus_cache{0};  // first calls from several threads may race: each stores the same value
+  int cus = cus_cache.load(std::memory_order_relaxed);
   if (cus == 0) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
+    cus_cache.store(cus, std::memory_order_relaxed);
   }
   const int grid = static_cast<int>(pb.K < cus ? pb.K : cus);
   // the slice counter starts from zero (a kernel, not a memset: the launch may be captured)
